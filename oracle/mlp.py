@@ -1,0 +1,232 @@
+"""The quantized MLP block, written out as its plain definition.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+What is computed, step by step, and the passage each step follows:
+
+  pack      Weights are stored in fewer bytes: FP8 E4M3 with one fp32 scale per
+            output channel, NVFP4 (E2M1 with one E4M3 scale per 16 inputs and
+            one fp32 per-tensor scale), or BF16 for a layer kept at higher
+            precision.  ("OCRia 推理栈：单卡 B200 提速近 10 倍", section
+            "Reducing the data moved: workload-aware quantization": FP8 halves
+            the bytes per weight; precision is mixed per layer across BF16,
+            FP8 and NVFP4; sensitive layers stay at higher precision.)
+  x-quant   Every row (token) of x is quantized to E4M3 with its own fp32
+            scale amax/448 (per-token FP8 activations).
+  gate/up   G = x W_g^T and U = x W_u^T over all M rows at once: a verify pass
+            covers every request's 1 + draft tokens, and the weights are read
+            again on every step (section "Generate more tokens per target
+            pass: speculative decoding").
+  SiLU.up   h = SiLU(G) * U, then h is quantized per token to E4M3 right away
+            (German page "Wie es funktioniert": SiLU activation and
+            quantization fused so the intermediate never goes to HBM; same in
+            the French "Comment cela fonctionne", Spanish "Cómo funciona" and
+            Japanese "仕組み").
+  down      Y = h W_d^T with the down weights in the precision chosen for that
+            layer (FP8, BF16 or NVFP4); y = bf16(Y).
+
+Readings where the pages are silent (all listed with the design notes):
+  * scale = fl32(amax / 448); zero amax -> scale 0 and all codes +0.
+  * every quantization decision (a code) is taken on the binary32 quotient
+    value/scale, i.e. on what an fp32 kernel holds; in particular h is
+    rounded to binary32 before its amax, scale and codes are formed.
+  * scales apply after the integer-code sums (exact algebra for per-row and
+    per-column scales); NVFP4 block scales apply inside the sum.
+  * in the BF16-down mode h enters the down projection as bf16(h) with no
+    FP8 requantization.
+Accumulation is fp64; with E4M3/E2M1 operands every product and every partial
+sum of the code-domain matmuls is exact in fp64, so the summation order of
+the matmul library does not matter.
+"""
+
+import numpy as np
+
+from .formats import (E2M1, E4M3, bf16_to_f64, dec_e4m3, enc_e2m1, enc_e4m3,
+                      rne_bf16)
+
+PREC_FP8 = 0            # gate/up FP8, down FP8
+PREC_FP8_DOWN_BF16 = 1  # gate/up FP8, down BF16 (layer kept at higher precision)
+PREC_FP4 = 2            # gate/up/down NVFP4
+
+NVFP4_BLOCK = 16
+
+
+def _f32(a):
+    return np.asarray(a, dtype=np.float64).astype(np.float32)
+
+
+# ----------------------------------------------------------------------------
+# per-row E4M3 quantization (weights per output channel, x and h per token)
+# ----------------------------------------------------------------------------
+
+
+def quantize_rows_e4m3(a):
+    """Per-row absmax E4M3 quantization.
+
+    a: 2-D array.  The values are first taken as binary32 (a no-op for fp32
+    weights and bf16 activations; the fp32 rounding of h for the
+    intermediate).  Returns (codes uint8 [R, C], scales float32 [R]) with
+    scale = fl32(amax / 448) and codes = E4M3(fl32(value / scale)).
+    """
+    a32 = _f32(a)
+    amax = np.max(np.abs(a32), axis=1) if a32.shape[1] else np.zeros(a32.shape[0], np.float32)
+    scale = _f32(amax.astype(np.float64) / 448.0)
+    codes = np.zeros(a32.shape, dtype=np.uint8)
+    nz = scale > 0
+    if np.any(nz):
+        quot = _f32(a32[nz].astype(np.float64) / scale[nz, None].astype(np.float64))
+        codes[nz] = enc_e4m3(quot)
+    return codes, scale
+
+
+# ----------------------------------------------------------------------------
+# weight packing (quantization) -- "Reducing the data moved"
+# ----------------------------------------------------------------------------
+
+
+def pack_fp8(w):
+    """FP8 E4M3 weights, one fp32 scale per output channel (row of [out, in])."""
+    return quantize_rows_e4m3(w)
+
+
+def pack_bf16(w):
+    """BF16 weights (round to nearest even), bit patterns [out, in]."""
+    return rne_bf16(np.asarray(w, dtype=np.float32).astype(np.float64))
+
+
+def pack_nvfp4(w):
+    """NVFP4 weights: E2M1 codes, one E4M3 scale per 16 consecutive inputs of
+    each output row, one fp32 per-tensor scale.
+
+      S          = fl32(amax(|W|) / (448 * 6))
+      sb[n, j]   = E4M3(fl32(amax_j(|W[n, 16j:16j+16]|) / (6 S)))
+      q[n, k]    = E2M1(fl32(W[n, k] / (dec(sb[n, k/16]) * S)))
+    with codes 0 wherever S or the block scale is 0.
+    Returns (codes uint8 [N, K] with one E2M1 code per byte, block scales
+    uint8 [N, K/16], S float32).
+    """
+    w32 = np.asarray(w, dtype=np.float32)
+    n, k = w32.shape
+    assert k % NVFP4_BLOCK == 0
+    amax = np.float32(np.max(np.abs(w32))) if w32.size else np.float32(0)
+    S = np.float32(np.float64(amax) / (448.0 * 6.0))
+    codes = np.zeros((n, k), dtype=np.uint8)
+    sb = np.zeros((n, k // NVFP4_BLOCK), dtype=np.uint8)
+    if S > 0:
+        blocks = w32.reshape(n, k // NVFP4_BLOCK, NVFP4_BLOCK).astype(np.float64)
+        amax_b = np.max(np.abs(blocks), axis=2)
+        r = _f32(amax_b / (6.0 * np.float64(S)))
+        sb = enc_e4m3(r)
+        d = dec_e4m3(sb) * np.float64(S)                # exact product
+        ok = d > 0
+        quot = np.zeros_like(blocks)
+        quot[ok] = blocks[ok] / d[ok][:, None]
+        q = enc_e2m1(_f32(quot))
+        q[~ok] = 0
+        codes = q.reshape(n, k)
+    return codes, sb, S
+
+
+def pack_block(w_gate, w_up, w_down, prec_mode):
+    """Quantize the three projections of one block for `prec_mode`."""
+    if prec_mode in (PREC_FP8, PREC_FP8_DOWN_BF16):
+        g = pack_fp8(w_gate)
+        u = pack_fp8(w_up)
+        d = pack_fp8(w_down) if prec_mode == PREC_FP8 else pack_bf16(w_down)
+    elif prec_mode == PREC_FP4:
+        g, u, d = pack_nvfp4(w_gate), pack_nvfp4(w_up), pack_nvfp4(w_down)
+    else:
+        raise ValueError("unknown prec_mode %r" % (prec_mode,))
+    return {"prec_mode": prec_mode, "gate": g, "up": u, "down": d}
+
+
+# ----------------------------------------------------------------------------
+# dequantized operands (exact fp64 values of the stored weights)
+# ----------------------------------------------------------------------------
+
+
+def fp8_weight_values(packed_fp8):
+    """Code values of an FP8 weight (the scale is applied after the sum)."""
+    codes, _ = packed_fp8
+    return dec_e4m3(codes)
+
+
+def nvfp4_weight_values(packed_fp4):
+    """E2M1 value times its E4M3 block scale (exact); S applies after the sum."""
+    codes, sb, _ = packed_fp4
+    blk = np.repeat(dec_e4m3(sb), NVFP4_BLOCK, axis=1)
+    return E2M1[codes & 0xF] * blk
+
+
+# ----------------------------------------------------------------------------
+# SiLU
+# ----------------------------------------------------------------------------
+
+
+def silu(g):
+    """SiLU(g) = g * sigmoid(g) = g / (1 + e^-g); for g < 0 the equivalent
+    g e^g / (1 + e^g) avoids overflow of e^-g."""
+    g = np.asarray(g, dtype=np.float64)
+    out = np.empty_like(g)
+    pos = g >= 0
+    out[pos] = g[pos] / (1.0 + np.exp(-g[pos]))
+    e = np.exp(g[~pos])
+    out[~pos] = g[~pos] * e / (1.0 + e)
+    return out
+
+
+# ----------------------------------------------------------------------------
+# the block
+# ----------------------------------------------------------------------------
+
+
+def _projection(a_vals, a_scale, w_packed, kind):
+    """sum_k a[t,k] w[n,k] in fp64, then the row (token) and column scales."""
+    if kind == "fp8":
+        acc = a_vals @ fp8_weight_values(w_packed).T
+        return acc * a_scale.astype(np.float64)[:, None] * w_packed[1].astype(np.float64)[None, :]
+    if kind == "fp4":
+        acc = a_vals @ nvfp4_weight_values(w_packed).T
+        return acc * a_scale.astype(np.float64)[:, None] * np.float64(w_packed[2])
+    raise ValueError(kind)
+
+
+def forward(x_bits, packed):
+    """One MLP block over all M rows.
+
+    x_bits: uint16 [M, H] bfloat16 bit patterns.
+    packed: result of pack_block.
+    Returns a dict with
+      xq (uint8 [M,H]), sx (float32 [M]),
+      hq (uint8 [M,I]) and sh (float32 [M])   -- FP8 / FP4 modes,
+      hb (uint16 [M,I])                        -- BF16-down mode,
+      h  (float64 [M,I]), Y (float64 [M,H]), y (uint16 [M,H]).
+    """
+    prec = packed["prec_mode"]
+    x = bf16_to_f64(x_bits)
+    xq, sx = quantize_rows_e4m3(x)
+    X = dec_e4m3(xq)
+
+    kind_gu = "fp4" if prec == PREC_FP4 else "fp8"
+    G = _projection(X, sx, packed["gate"], kind_gu)
+    U = _projection(X, sx, packed["up"], kind_gu)
+    h = silu(G) * U
+
+    out = {"xq": xq, "sx": sx, "h": h}
+    if prec == PREC_FP8_DOWN_BF16:
+        hb = rne_bf16(_f32(h).astype(np.float64))
+        Y = bf16_to_f64(hb) @ bf16_to_f64(packed["down"]).T
+        out["hb"] = hb
+    else:
+        hq, sh = quantize_rows_e4m3(h)
+        Y = _projection(dec_e4m3(hq), sh, packed["down"], "fp4" if prec == PREC_FP4 else "fp8")
+        out["hq"] = hq
+        out["sh"] = sh
+    out["Y"] = Y
+    out["y"] = rne_bf16(Y)
+    return out
+
+
+def block_reference(x_bits, w_gate, w_up, w_down, prec_mode):
+    """Pack and run in one call."""
+    return forward(x_bits, pack_block(w_gate, w_up, w_down, prec_mode))

@@ -1,0 +1,269 @@
+"""Pins for the oracle's block forward and weight packing (CPU only).
+
+The block has no worked example in the pages, so the oracle is pinned by
+(1) lossless special cases: inputs and weights chosen on the quantization
+grids (x rows = E4M3 values * 2^k with a +-448 in each row, weight rows likewise,
+NVFP4 weights = E2M1 * E4M3 block scale * 2^-12) make every quantization step
+exact, so G, U and the down projection must equal the textbook SiLU-gated MLP
+computed here with numpy matmuls, torch's SiLU and torch's FP8 / bf16 casts;
+(2) invariants of the definition (scale rule, zero rows, power-of-two row
+scaling, row independence); (3) the error bound of round-to-nearest.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import formats as F
+from oracle import mlp as O
+from quantized_memory_bound_amd import inputs as I
+
+
+# ------------------------------------------------------------------ helpers
+
+def _grid_rows(rng, n, k, exps):
+    """n x k values E4M3 * 2^e_row, each row holding one +-448 (so the row's
+    scale is exactly 2^e_row and its codes are the chosen codes)."""
+    codes = rng.integers(0, 0x7F, size=(n, k)).astype(np.uint8)      # 0..126, no NaN
+    codes |= (rng.integers(0, 2, size=(n, k)) * 0x80).astype(np.uint8)
+    pos = rng.integers(0, k, size=n)
+    codes[np.arange(n), pos] = np.where(rng.integers(0, 2, n) > 0, 0x7E, 0xFE)
+    vals = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    e = rng.choice(exps, size=n)
+    return codes, e, vals * np.exp2(e)[:, None]
+
+
+def _bf16_bits_exact(v):
+    t = torch.from_numpy(np.asarray(v, np.float32)).to(torch.bfloat16)
+    assert np.array_equal(t.to(torch.float64).numpy(), np.asarray(v, np.float64))
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def _torch_e4m3_codes(v):
+    return torch.from_numpy(np.asarray(v, np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def _torch_e4m3_values(codes):
+    return torch.from_numpy(np.asarray(codes, np.uint8)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def _silu_torch(g):
+    return torch.nn.functional.silu(torch.from_numpy(g)).numpy()
+
+
+def _lossless_setup(seed, M=5, H=64, Iw=48):
+    rng = np.random.default_rng(seed)
+    xc, xe, x = _grid_rows(rng, M, H, np.arange(-6, 1))
+    gc, ge, wg = _grid_rows(rng, Iw, H, np.arange(-16, -10))
+    uc, ue, wu = _grid_rows(rng, Iw, H, np.arange(-16, -10))
+    x_bits = _bf16_bits_exact(x)
+    return rng, dict(x=x, x_bits=x_bits, xc=xc, xe=xe, wg=wg.astype(np.float32), gc=gc, ge=ge,
+                     wu=wu.astype(np.float32), uc=uc, ue=ue)
+
+
+# ------------------------------------------------------------------ lossless special cases
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_lossless_fp8_block_equals_textbook_mlp(seed):
+    rng, d = _lossless_setup(seed)
+    H = d["x"].shape[1]
+    dc, de, wd = _grid_rows(rng, H, d["wg"].shape[0], np.arange(-16, -10))
+    packed = O.pack_block(d["wg"], d["wu"], wd.astype(np.float32), O.PREC_FP8)
+    # packing recovers the chosen codes and the power-of-two scales exactly
+    assert np.array_equal(packed["gate"][0], d["gc"]) and np.array_equal(packed["gate"][1], np.exp2(d["ge"]))
+    assert np.array_equal(packed["up"][0], d["uc"]) and np.array_equal(packed["up"][1], np.exp2(d["ue"]))
+    assert np.array_equal(packed["down"][0], dc) and np.array_equal(packed["down"][1], np.exp2(de))
+
+    out = O.forward(d["x_bits"], packed)
+    assert np.array_equal(out["xq"], d["xc"]) and np.array_equal(out["sx"], np.exp2(d["xe"]))
+    # gate/up: textbook x W^T (every step exact on these grids)
+    G = d["x"] @ d["wg"].astype(np.float64).T
+    U = d["x"] @ d["wu"].astype(np.float64).T
+    h = _silu_torch(G) * U
+    np.testing.assert_allclose(out["h"], h, rtol=1e-13, atol=0)
+    # requant: scale = fl32(amax/448) and codes by torch's own E4M3 cast
+    h32 = out["h"].astype(np.float32)
+    sh = (np.max(np.abs(h32), axis=1) / np.float32(448)).astype(np.float32)
+    assert np.array_equal(out["sh"], sh)
+    assert np.array_equal(out["hq"], _torch_e4m3_codes(h32 / sh[:, None]))
+    # down: textbook (dequantized h) W_d^T, W_d exact on its grid
+    Y = (_torch_e4m3_values(out["hq"]) * sh[:, None].astype(np.float64)) @ wd.T
+    np.testing.assert_allclose(out["Y"], Y, rtol=1e-13, atol=1e-300)
+    yb = torch.from_numpy(Y).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.mean(out["y"] != yb) <= 1e-3      # torch rounds fp64 -> bf16 via fp32 (rare double rounding)
+
+
+@pytest.mark.parametrize("seed", [3, 4])
+def test_lossless_bf16_down_equals_textbook(seed):
+    rng, d = _lossless_setup(seed)
+    H, Iw = d["x"].shape[1], d["wg"].shape[0]
+    wd = torch.from_numpy(rng.standard_normal((H, Iw)).astype(np.float32) * 0.05).to(torch.bfloat16)
+    wd = wd.to(torch.float32).numpy()                       # exactly bf16-valued
+    out = O.block_reference(d["x_bits"], d["wg"], d["wu"], wd, O.PREC_FP8_DOWN_BF16)
+    G = d["x"] @ d["wg"].astype(np.float64).T
+    U = d["x"] @ d["wu"].astype(np.float64).T
+    h = _silu_torch(G) * U
+    np.testing.assert_allclose(out["h"], h, rtol=1e-13)
+    hb = torch.from_numpy(out["h"].astype(np.float32)).to(torch.bfloat16)
+    assert np.array_equal(out["hb"], hb.view(torch.int16).numpy().view(np.uint16))
+    Y = hb.to(torch.float64).numpy() @ wd.astype(np.float64).T
+    np.testing.assert_allclose(out["Y"], Y, rtol=1e-13, atol=1e-300)
+
+
+def _fp4_grid_weight(rng, n, k, S_exp=-12):
+    """W = e2m1 * dec(sb) * 2^S_exp with one +-6 per 16-block and one block
+    scale 448, so S = 2^S_exp and every code is recovered exactly."""
+    nb = k // 16
+    sb = rng.integers(0x30, 0x7F, size=(n, nb)).astype(np.uint8)      # normal E4M3 scales
+    sb[0, 0] = 0x7E
+    q = rng.integers(0, 16, size=(n, k)).astype(np.uint8)
+    slot = rng.integers(0, 16, size=(n, nb))
+    rows, blks = np.meshgrid(np.arange(n), np.arange(nb), indexing="ij")
+    q[rows, blks * 16 + slot] = np.where(rng.integers(0, 2, (n, nb)) > 0, 0x7, 0xF)
+    vals = F.E2M1[q] * np.repeat(_torch_e4m3_values(sb), 16, axis=1) * 2.0 ** S_exp
+    return q, sb, vals
+
+
+@pytest.mark.parametrize("seed", [5, 6])
+def test_lossless_nvfp4_block(seed):
+    rng, d = _lossless_setup(seed, H=64, Iw=32)
+    H, Iw = 64, 32
+    qg, sbg, wg = _fp4_grid_weight(rng, Iw, H)
+    qu, sbu, wu = _fp4_grid_weight(rng, Iw, H)
+    qd, sbd, wd = _fp4_grid_weight(rng, H, Iw)
+    for q, sb, w in ((qg, sbg, wg), (qu, sbu, wu), (qd, sbd, wd)):
+        codes, sbo, S = O.pack_nvfp4(w.astype(np.float32))
+        assert S == np.float32(2.0 ** -12)
+        assert np.array_equal(sbo, sb)
+        # +-0 codes may differ only in sign of zero; compare values
+        assert np.array_equal(F.E2M1[codes], F.E2M1[q])
+    out = O.block_reference(d["x_bits"], wg.astype(np.float32), wu.astype(np.float32),
+                            wd.astype(np.float32), O.PREC_FP4)
+    G = d["x"] @ wg.T
+    U = d["x"] @ wu.T
+    np.testing.assert_allclose(out["h"], _silu_torch(G) * U, rtol=1e-13)
+    sh = out["sh"].astype(np.float64)
+    Y = (_torch_e4m3_values(out["hq"]) * sh[:, None]) @ wd.T
+    np.testing.assert_allclose(out["Y"], Y, rtol=1e-13, atol=1e-300)
+
+
+# ------------------------------------------------------------------ invariants on workload inputs
+
+@pytest.fixture(scope="module")
+def tiny():
+    d = I.workload_inputs("tiny_fp8")
+    return d
+
+
+@pytest.mark.parametrize("prec", [O.PREC_FP8, O.PREC_FP8_DOWN_BF16, O.PREC_FP4])
+def test_scale_rule_max_code_448(tiny, prec):
+    packed = O.pack_block(tiny["w_gate"], tiny["w_up"], tiny["w_down"], prec)
+    out = O.forward(tiny["x_bits"], packed)
+    for codes in [out["xq"]] + ([out["hq"]] if "hq" in out else []):
+        mx = np.max(np.abs(F.dec_e4m3(codes)), axis=1)
+        assert np.all(mx == 448.0)
+    if prec != O.PREC_FP4:
+        for codes, s in (packed["gate"], packed["up"]):
+            assert np.all(np.max(np.abs(F.dec_e4m3(codes)), axis=1) == 448.0)
+    else:
+        for codes, sb, S in (packed["gate"], packed["up"], packed["down"]):
+            assert np.all(np.abs(F.dec_e2m1(codes)) <= 6.0)
+            assert np.max(F.dec_e4m3(sb)) == 448.0
+
+
+def test_nvfp4_tensor_scale_and_nearest(tiny):
+    w = tiny["w_gate"]
+    codes, sb, S = O.pack_nvfp4(w)
+    amax = np.float64(np.max(np.abs(w)))
+    assert abs(np.float64(S) * 2688.0 - amax) <= amax * 2.0 ** -23
+    # every element is the nearest E2M1 grid point at its block's scale
+    d = np.repeat(F.dec_e4m3(sb), 16, axis=1) * np.float64(S)
+    deq = F.dec_e2m1(codes) * d
+    grid = F.E2M1[:8][None, None, :] * d[:, :, None]
+    err_best = np.min(np.abs(np.abs(w.astype(np.float64))[:, :, None] - grid), axis=2)
+    assert np.all(np.abs(deq - w) <= err_best * (1 + 1e-6) + 1e-30)
+
+
+def test_fp8_weight_nearest(tiny):
+    w = tiny["w_up"]
+    codes, s = O.pack_fp8(w)
+    deq = F.dec_e4m3(codes) * s[:, None].astype(np.float64)
+    # error never exceeds half the E4M3 spacing at the value (relative 2^-4, or 2^-10 * s absolute)
+    err = np.abs(deq - w)
+    bound = np.maximum(np.abs(w) * 2.0 ** -4, 2.0 ** -10 * s[:, None]) * (1 + 1e-6)
+    assert np.all(err <= bound)
+
+
+def test_zero_row_and_power_of_two_row_scaling(tiny):
+    x = tiny["x_bits"].copy()
+    x[1] = 0
+    xf = F.bf16_to_f64(x)
+    xf[2] = xf[2] * 2.0 ** 5                     # exact in bf16
+    x2 = _bf16_bits_exact(xf)
+    for prec in (O.PREC_FP8, O.PREC_FP8_DOWN_BF16, O.PREC_FP4):
+        packed = O.pack_block(tiny["w_gate"], tiny["w_up"], tiny["w_down"], prec)
+        a = O.forward(tiny["x_bits"], packed)
+        b = O.forward(x2, packed)
+        assert b["sx"][1] == 0 and np.all(b["xq"][1] == 0)
+        assert np.all(F.bf16_to_f64(b["y"][1]) == 0)
+        assert np.array_equal(b["xq"][2], a["xq"][2]) and b["sx"][2] == a["sx"][2] * 32
+        assert np.array_equal(b["y"][0], a["y"][0]) and np.array_equal(b["y"][3], a["y"][3])
+
+
+def test_row_independence():
+    d = I.make_inputs(256, 512, 52, x_outliers=True, w_std=0.02, seed=7)
+    for prec in (O.PREC_FP8, O.PREC_FP8_DOWN_BF16, O.PREC_FP4):
+        packed = O.pack_block(d["w_gate"], d["w_up"], d["w_down"], prec)
+        full = O.forward(d["x_bits"], packed)
+        part = O.forward(d["x_bits"][:13], packed)
+        for key in ("xq", "sx", "y") + (("hb",) if prec == O.PREC_FP8_DOWN_BF16 else ("hq", "sh")):
+            assert np.array_equal(full[key][:13], part[key]), (prec, key)
+
+
+def test_up_projection_is_linear_gate_is_not(tiny):
+    # doubling W_up doubles h exactly (same codes, scales x2), hence same hq and
+    # sh x2 and y x2; doubling W_gate does not (SiLU is applied to the gate only).
+    p1 = O.pack_block(tiny["w_gate"], tiny["w_up"], tiny["w_down"], O.PREC_FP8)
+    p2 = O.pack_block(tiny["w_gate"], tiny["w_up"] * 2, tiny["w_down"], O.PREC_FP8)
+    p3 = O.pack_block(tiny["w_gate"] * 2, tiny["w_up"], tiny["w_down"], O.PREC_FP8)
+    a, b, c = (O.forward(tiny["x_bits"], p) for p in (p1, p2, p3))
+    assert np.array_equal(a["hq"], b["hq"]) and np.array_equal(b["sh"], a["sh"] * 2)
+    assert np.array_equal(F.bf16_to_f64(b["y"]), 2 * F.bf16_to_f64(a["y"]))
+    assert not np.array_equal(F.bf16_to_f64(c["y"]), 2 * F.bf16_to_f64(a["y"]))
+
+
+def test_silu_identities():
+    g = np.array([0.0, 1.0, -1.0, 3.5, -3.5, 40.0, -40.0, 800.0, -800.0])
+    s = O.silu(g)
+    assert s[0] == 0.0
+    assert abs(s[1] - 1.0 / (1.0 + np.exp(-1.0))) < 1e-16
+    np.testing.assert_allclose(s[1::2] - s[2::2], g[1::2], rtol=1e-15)   # silu(g) - silu(-g) = g
+    assert s[7] == 800.0 and abs(s[8]) < 1e-300
+    assert np.all(np.isfinite(s))
+
+
+def test_quantized_block_close_to_unquantized_mlp(tiny):
+    x = F.bf16_to_f64(tiny["x_bits"])
+    wg, wu, wd = (tiny[k].astype(np.float64) for k in ("w_gate", "w_up", "w_down"))
+    y_ref = (_silu_torch(x @ wg.T) * (x @ wu.T)) @ wd.T
+    for prec, hi in ((O.PREC_FP8, 0.08), (O.PREC_FP8_DOWN_BF16, 0.06), (O.PREC_FP4, 0.3)):
+        y = F.bf16_to_f64(O.block_reference(tiny["x_bits"], tiny["w_gate"], tiny["w_up"], tiny["w_down"], prec)["y"])
+        rel = np.linalg.norm(y - y_ref) / np.linalg.norm(y_ref)
+        assert 1e-3 < rel < hi, (prec, rel)
+
+
+def test_code_sums_exact_vs_rationals():
+    # brute force: the fp64 code-domain sum equals the exact rational sum on a small case
+    from fractions import Fraction
+    rng = np.random.default_rng(9)
+    a = rng.integers(0, 255, (3, 40)).astype(np.uint8)
+    b = rng.integers(0, 255, (4, 40)).astype(np.uint8)
+    a[a == 0x7F] = 0x7E
+    b[b == 0x7F] = 0x7E
+    a[a == 0xFF] = 0xFE
+    b[b == 0xFF] = 0xFE
+    got = F.dec_e4m3(a) @ F.dec_e4m3(b).T
+    for i in range(3):
+        for j in range(4):
+            exact = sum(Fraction(float(F.E4M3[a[i, k]])) * Fraction(float(F.E4M3[b[j, k]])) for k in range(40))
+            assert Fraction(float(got[i, j])) == exact

@@ -1,0 +1,145 @@
+/*
+ * ocq.h -- C ABI of the quantized speculative-verify MLP block for AMD
+ * MI355X (gfx950).
+ *
+ * What one call computes (the post "OCRia 推理栈：单卡 B200 提速近 10 倍"):
+ *   x [M, hidden] bf16                            (M = requests x (1 + drafts),
+ *                                                   section "Generate more tokens
+ *                                                   per target pass")
+ *   xq, sx = per-token E4M3 quantization of x     (sx = amax/448)
+ *   G = (xq Wg^T) sx sw_g ;  U = (xq Wu^T) sx sw_u (weights FP8 or NVFP4, section
+ *                                                   "Reducing the data moved:
+ *                                                   workload-aware quantization")
+ *   h = SiLU(G) * U, quantized per token to E4M3  (German page "Wie es
+ *                                                   funktioniert": SiLU fused with
+ *                                                   the quantization, kept in
+ *                                                   registers)
+ *   y = bf16( h Wd^T )                            (down projection in the
+ *                                                   precision chosen for the
+ *                                                   layer: FP8, BF16 or NVFP4)
+ * Formats: E4M3 = OCP FP8 E4M3FN (max 448); E2M1 = OCP MX FP4; NVFP4 = E2M1
+ * elements with one E4M3 scale per 16 inputs and one fp32 per-tensor scale.
+ * Rounding: nearest, ties to even, saturating.  Scales: fl32(amax / 448) for
+ * E4M3 rows, fl32(amax / 2688) per NVFP4 tensor, fl32(block amax / (6 S)) per
+ * NVFP4 block before its own E4M3 rounding.  A zero row gets scale 0 and codes 0.
+ *
+ * Conventions for every entry point
+ *   - Pointers named *_dev are device pointers (hipMalloc / torch CUDA
+ *     tensors); *_host are host pointers.  The caller owns all memory and
+ *     the stream; the library allocates nothing and frees nothing.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *   - A negative ocq_status is returned on failure, before anything is
+ *     launched; ocq_last_error() then gives a message (thread-local, valid
+ *     until the next call on the same thread).  Argument checks are
+ *     synchronous; faults inside a kernel surface at the caller's next
+ *     synchronization, as with any stream API.
+ *   - Shapes: hidden and inter must be multiples of 128, 128 <= each <= 65536;
+ *     1 <= M <= 8192.  Device pointers must be 16-byte aligned.
+ */
+#ifndef OCQ_H
+#define OCQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  OCQ_OK = 0,
+  OCQ_ERR_INVALID_ARG = -1,      /* null / misaligned pointer, bad M, bad enum   */
+  OCQ_ERR_UNSUPPORTED = -2,      /* shape outside the supported set              */
+  OCQ_ERR_DEVICE = -3,           /* HIP runtime error (no device, launch failure) */
+  OCQ_ERR_BUFFER_TOO_SMALL = -4, /* packed blob or workspace smaller than needed  */
+  OCQ_ERR_BAD_BLOB = -5          /* blob header does not match the call          */
+} ocq_status;
+
+typedef enum {
+  OCQ_PREC_FP8 = 0,           /* gate/up FP8 E4M3, down FP8 E4M3                */
+  OCQ_PREC_FP8_DOWN_BF16 = 1, /* gate/up FP8 E4M3, down BF16 (sensitive layer)  */
+  OCQ_PREC_FP4 = 2            /* gate/up/down NVFP4                              */
+} ocq_prec_mode;
+
+/* Library version (major * 10000 + minor * 100 + patch). */
+int ocq_version(void);
+
+/* Bytes of the packed weight blob for one block; 0 if the shape or mode is
+ * invalid.  The blob holds a 256-byte header followed by the quantized
+ * gate/up and down weights in the kernels' fragment order and their scales. */
+size_t ocq_packed_bytes(int hidden, int inter, int prec_mode);
+
+/* Quantize and pack one block's weights into a HOST buffer (no GPU used).
+ * w_gate_host, w_up_host: fp32 [inter, hidden] row-major ([out, in]).
+ * w_down_host: fp32 [hidden, inter] row-major.  Weights must be finite.
+ * FP8: one fp32 scale per output row, codes E4M3(fl32(w / scale)).
+ * BF16 (down in OCQ_PREC_FP8_DOWN_BF16): round to nearest even.
+ * NVFP4: per-tensor S, per-16-input E4M3 block scale, E2M1 codes.
+ * packed_host must hold ocq_packed_bytes() bytes.  Thread-safe. */
+ocq_status ocq_pack_weights_host(const float* w_gate_host, const float* w_up_host,
+                                 const float* w_down_host, int hidden, int inter,
+                                 int prec_mode, void* packed_host, size_t packed_bytes);
+
+/* Same, then copy the blob to device memory with hipMemcpyAsync on `stream`
+ * and wait for that copy (the staging buffer is freed before returning). */
+ocq_status ocq_pack_weights(const float* w_gate_host, const float* w_up_host,
+                            const float* w_down_host, int hidden, int inter, int prec_mode,
+                            void* packed_dev, size_t packed_bytes, void* stream);
+
+/* Inverse of the packing layout, for inspection and tests: from a HOST copy
+ * of a blob, write one projection in plain row-major form.
+ *   which = 0 gate, 1 up, 2 down.
+ *   codes_out: uint8 [rows, cols] (E4M3 or E2M1 code per byte) or uint16
+ *              bf16 bits [rows, cols] for a BF16 projection.
+ *   scales_out: FP8 -> float [rows]; NVFP4 -> uint8 E4M3 [rows, cols/16];
+ *               BF16 -> unused (may be NULL).
+ *   tensor_scale_out: NVFP4 -> S; others -> 0 (may be NULL). */
+ocq_status ocq_unpack_weights_host(const void* packed_host, size_t packed_bytes, int which,
+                                   void* codes_out, void* scales_out, float* tensor_scale_out);
+
+/* Device workspace bytes needed by ocq_mlp_forward for this call shape. */
+size_t ocq_workspace_bytes(int M, int hidden, int inter, int prec_mode);
+
+/* Optional plain-layout copies of the intermediates, for parity checks.
+ * Each pointer is a device pointer or NULL.
+ *   x_codes [M, hidden] uint8, x_scales [M] float,
+ *   h_out:  FP8/NVFP4 modes -> E4M3 codes [M, inter] uint8;
+ *           BF16-down mode  -> bf16 bits [M, inter] uint16,
+ *   h_scales [M] float (FP8/NVFP4 modes; untouched in BF16-down mode). */
+typedef struct {
+  void* x_codes;
+  void* x_scales;
+  void* h_out;
+  void* h_scales;
+} ocq_taps;
+
+/* One MLP block over M rows, enqueued on `stream` (asynchronous).
+ * packed_dev: blob from ocq_pack_weights for (hidden, inter, prec_mode),
+ *             packed_bytes >= ocq_packed_bytes(...).
+ * x_bf16_dev: bf16 [M, hidden] row-major, finite values.
+ * y_bf16_dev: bf16 [M, hidden] row-major, written by the call.
+ * workspace_dev: >= ocq_workspace_bytes(M, hidden, inter, prec_mode) bytes;
+ *             contents need not be initialized; calls that share a
+ *             workspace must be ordered on one stream.
+ * taps: NULL or optional intermediate copies (see ocq_taps).
+ * The blob header is not read back to the host (that would synchronize);
+ * a blob packed for other dimensions or another mode gives wrong results
+ * but all reads stay inside packed_bytes.  Use ocq_check_blob to verify. */
+ocq_status ocq_mlp_forward(const void* packed_dev, size_t packed_bytes, const void* x_bf16_dev,
+                           int M, int hidden, int inter, int prec_mode, void* y_bf16_dev,
+                           void* workspace_dev, size_t workspace_bytes, const ocq_taps* taps,
+                           void* stream);
+
+/* Synchronously read a device blob's header and check it against
+ * (hidden, inter, prec_mode): OCQ_OK or OCQ_ERR_BAD_BLOB. */
+ocq_status ocq_check_blob(const void* packed_dev, size_t packed_bytes, int hidden, int inter,
+                          int prec_mode, void* stream);
+
+/* Message for the last failure on this thread ("" if none). */
+const char* ocq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OCQ_H */

@@ -1,0 +1,160 @@
+// C-ABI entry points of the ocq library: argument checks, planning, launches.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "ocq_internal.h"
+
+namespace ocq {
+
+static thread_local std::string g_err;
+
+ocq_status set_error(ocq_status st, const char* msg) {
+  g_err = msg ? msg : "";
+  return st;
+}
+
+static ocq_status set_hip_error(hipError_t e, const char* where) {
+  char buf[256];
+  std::snprintf(buf, sizeof(buf), "%s: %s (%d)", where, hipGetErrorString(e), (int)e);
+  return set_error(OCQ_ERR_DEVICE, buf);
+}
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+static ocq_status check_shape(int hidden, int inter, int prec_mode) {
+  if (prec_mode < 0 || prec_mode > 2) return set_error(OCQ_ERR_INVALID_ARG, "prec_mode must be 0, 1 or 2");
+  if (!shape_ok(hidden, inter))
+    return set_error(OCQ_ERR_UNSUPPORTED, "hidden and inter must be multiples of 128 in [128, 65536]");
+  return OCQ_OK;
+}
+
+}  // namespace ocq
+
+using namespace ocq;
+
+extern "C" {
+
+int ocq_version(void) { return 10000; }
+
+const char* ocq_last_error(void) { return g_err.c_str(); }
+
+size_t ocq_packed_bytes(int hidden, int inter, int prec_mode) {
+  if (prec_mode < 0 || prec_mode > 2 || !shape_ok(hidden, inter)) return 0;
+  return blob_layout(hidden, inter, prec_mode).total;
+}
+
+ocq_status ocq_pack_weights_host(const float* w_gate_host, const float* w_up_host, const float* w_down_host,
+                                 int hidden, int inter, int prec_mode, void* packed_host, size_t packed_bytes) {
+  g_err.clear();
+  ocq_status st = check_shape(hidden, inter, prec_mode);
+  if (st != OCQ_OK) return st;
+  if (!w_gate_host || !w_up_host || !w_down_host || !packed_host)
+    return set_error(OCQ_ERR_INVALID_ARG, "null weight or output pointer");
+  return pack_host(w_gate_host, w_up_host, w_down_host, hidden, inter, prec_mode, (uint8_t*)packed_host,
+                   packed_bytes);
+}
+
+ocq_status ocq_pack_weights(const float* w_gate_host, const float* w_up_host, const float* w_down_host, int hidden,
+                            int inter, int prec_mode, void* packed_dev, size_t packed_bytes, void* stream) {
+  g_err.clear();
+  ocq_status st = check_shape(hidden, inter, prec_mode);
+  if (st != OCQ_OK) return st;
+  if (!w_gate_host || !w_up_host || !w_down_host || !packed_dev)
+    return set_error(OCQ_ERR_INVALID_ARG, "null weight or output pointer");
+  if (!aligned16(packed_dev)) return set_error(OCQ_ERR_INVALID_ARG, "packed_dev must be 16-byte aligned");
+  const size_t need = blob_layout(hidden, inter, prec_mode).total;
+  if (packed_bytes < need) return set_error(OCQ_ERR_BUFFER_TOO_SMALL, "packed_bytes < ocq_packed_bytes()");
+  std::vector<uint8_t> host(need);
+  st = pack_host(w_gate_host, w_up_host, w_down_host, hidden, inter, prec_mode, host.data(), need);
+  if (st != OCQ_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(packed_dev, host.data(), need, hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return set_hip_error(e, "hipMemcpyAsync(blob)");
+  e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return set_hip_error(e, "hipStreamSynchronize(blob copy)");
+  return OCQ_OK;
+}
+
+ocq_status ocq_unpack_weights_host(const void* packed_host, size_t packed_bytes, int which, void* codes_out,
+                                   void* scales_out, float* tensor_scale_out) {
+  g_err.clear();
+  if (!packed_host) return set_error(OCQ_ERR_INVALID_ARG, "null blob pointer");
+  return unpack_host((const uint8_t*)packed_host, packed_bytes, which, codes_out, scales_out, tensor_scale_out);
+}
+
+size_t ocq_workspace_bytes(int M, int hidden, int inter, int prec_mode) {
+  if (prec_mode < 0 || prec_mode > 2 || !shape_ok(hidden, inter) || M < 1 || M > 8192) return 0;
+  return make_plan(M, hidden, inter, prec_mode).total;
+}
+
+ocq_status ocq_check_blob(const void* packed_dev, size_t packed_bytes, int hidden, int inter, int prec_mode,
+                          void* stream) {
+  g_err.clear();
+  ocq_status st = check_shape(hidden, inter, prec_mode);
+  if (st != OCQ_OK) return st;
+  if (!packed_dev) return set_error(OCQ_ERR_INVALID_ARG, "null blob pointer");
+  if (packed_bytes < sizeof(BlobHeader)) return set_error(OCQ_ERR_BUFFER_TOO_SMALL, "blob smaller than its header");
+  BlobHeader hd;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(&hd, packed_dev, sizeof(hd), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return set_hip_error(e, "reading blob header");
+  if (std::memcmp(hd.magic, kBlobMagic, 8) != 0 || hd.version != kBlobVersion)
+    return set_error(OCQ_ERR_BAD_BLOB, "bad blob magic or version");
+  if (hd.hidden != hidden || hd.inter != inter || hd.prec_mode != prec_mode)
+    return set_error(OCQ_ERR_BAD_BLOB, "blob was packed for other dimensions or another prec_mode");
+  if (hd.total_bytes != blob_layout(hidden, inter, prec_mode).total || packed_bytes < hd.total_bytes)
+    return set_error(OCQ_ERR_BAD_BLOB, "blob size does not match its layout");
+  return OCQ_OK;
+}
+
+ocq_status ocq_mlp_forward(const void* packed_dev, size_t packed_bytes, const void* x_bf16_dev, int M, int hidden,
+                           int inter, int prec_mode, void* y_bf16_dev, void* workspace_dev, size_t workspace_bytes,
+                           const ocq_taps* taps, void* stream) {
+  g_err.clear();
+  ocq_status st = check_shape(hidden, inter, prec_mode);
+  if (st != OCQ_OK) return st;
+  if (M < 1 || M > 8192) return set_error(OCQ_ERR_INVALID_ARG, "M must be in [1, 8192]");
+  if (!packed_dev || !x_bf16_dev || !y_bf16_dev || !workspace_dev)
+    return set_error(OCQ_ERR_INVALID_ARG, "null device pointer");
+  if (!aligned16(packed_dev) || !aligned16(x_bf16_dev) || !aligned16(y_bf16_dev) || !aligned16(workspace_dev))
+    return set_error(OCQ_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  if (packed_bytes < blob_layout(hidden, inter, prec_mode).total)
+    return set_error(OCQ_ERR_BUFFER_TOO_SMALL, "packed_bytes < ocq_packed_bytes()");
+  const Plan p = make_plan(M, hidden, inter, prec_mode);
+  if (workspace_bytes < p.total) return set_error(OCQ_ERR_BUFFER_TOO_SMALL, "workspace_bytes < ocq_workspace_bytes()");
+  if (taps) {
+    const void* tp[4] = {taps->x_codes, taps->x_scales, taps->h_out, taps->h_scales};
+    for (const void* t : tp)
+      if (t && !aligned16(t)) return set_error(OCQ_ERR_INVALID_ARG, "tap pointers must be 16-byte aligned");
+  }
+  FwdArgs a{(const uint8_t*)packed_dev, (const uint16_t*)x_bf16_dev, (uint16_t*)y_bf16_dev, (uint8_t*)workspace_dev,
+            stream};
+  int rc = launch_forward(p, a);
+  if (rc != 0) return set_hip_error((hipError_t)rc, "kernel launch");
+  if (taps) {
+    hipStream_t s = (hipStream_t)stream;
+    uint8_t* ws = (uint8_t*)workspace_dev;
+    hipError_t e = hipSuccess;
+    if (taps->x_codes && e == hipSuccess)
+      e = hipMemcpyAsync(taps->x_codes, ws + p.off_xq, (size_t)M * hidden, hipMemcpyDeviceToDevice, s);
+    if (taps->x_scales && e == hipSuccess)
+      e = hipMemcpyAsync(taps->x_scales, ws + p.off_sx, (size_t)M * 4, hipMemcpyDeviceToDevice, s);
+    if (taps->h_out && e == hipSuccess) {
+      if (prec_mode == kFP8DownBF16)
+        e = hipMemcpyAsync(taps->h_out, ws + p.off_hb, (size_t)M * inter * 2, hipMemcpyDeviceToDevice, s);
+      else
+        e = hipMemcpyAsync(taps->h_out, ws + p.off_hq, (size_t)M * inter, hipMemcpyDeviceToDevice, s);
+    }
+    if (taps->h_scales && prec_mode != kFP8DownBF16 && e == hipSuccess)
+      e = hipMemcpyAsync(taps->h_scales, ws + p.off_sh, (size_t)M * 4, hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return set_hip_error(e, "tap copies");
+  }
+  return OCQ_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,36 @@
+// Internal declarations of the ocq library (not part of the C ABI).
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/ocq.h"
+#include "ocq_layout.h"
+
+namespace ocq {
+
+// thread-local error message; returns `st` for convenience
+ocq_status set_error(ocq_status st, const char* msg);
+
+// host packer (pack.cpp)
+ocq_status pack_host(const float* wg, const float* wu, const float* wd, int hidden, int inter, int prec,
+                     uint8_t* out, size_t out_bytes);
+ocq_status unpack_host(const uint8_t* blob, size_t bytes, int which, void* codes_out, void* scales_out,
+                       float* tensor_scale_out);
+uint8_t host_enc_e4m3(float v);
+float host_dec_e4m3(uint8_t c);
+uint8_t host_enc_e2m1(float v);
+uint16_t host_bf16_rne(float v);
+
+// device pointers of one forward call
+struct FwdArgs {
+  const uint8_t* blob;
+  const uint16_t* x;
+  uint16_t* y;
+  uint8_t* ws;
+  void* stream;
+};
+
+// enqueue the kernels of one forward call (kernels.hip); returns 0 or a hipError_t value
+int launch_forward(const Plan& p, const FwdArgs& a);
+
+}  // namespace ocq

@@ -1,0 +1,175 @@
+// Packed-weight blob layout and workspace layout shared by the host packer,
+// the C-ABI entry points and the HIP kernels.
+//
+// Fragment order.  The matrix cores take, per 16x16xK product, one operand
+// fragment per lane.  Every weight projection is cut into "tiles" of 16
+// output rows and "chunks" of 128 input columns.  Lane l = 16 g + r (g = 0..3,
+// r = 0..15) of a wave holds row r of the tile and the 32 consecutive inputs
+// k = 128 c + 32 g + j, j = 0..31, of chunk c.  Activations are read with the
+// same per-lane k-ranges straight from their row-major buffers, so the two
+// operands agree on which k each lane/byte carries and the hardware sums the
+// same products as the plain definition.
+//
+//   FP8 chunk  (2048 B): [half h = 0,1][lane][16 B]   byte j of lane l at
+//                        h = j / 16, offset (h * 64 + l) * 16 + j % 16.
+//   BF16 chunk (4096 B): [sub i = 0..3][lane][16 B]   bf16 element j at
+//                        i = j / 8, offset (i * 64 + l) * 16 + 2 * (j % 8).
+//   FP4 chunk  (1024 B): [lane][16 B]                 E2M1 code j in byte j/2,
+//                        low nibble for even j.
+//   FP4 block scales: per tile, groups of 8 chunks, [lane][8 chunks x 2 B]
+//                        (1024 B per group); byte 2 (c % 8) + b is the E4M3
+//                        scale of inputs 128 c + 32 g + 16 b .. +16.
+//
+// Gate/up tiles interleave the two projections: tile t holds gate rows
+// 8t..8t+7 (tile rows 0..7) and up rows 8t..8t+7 (tile rows 8..15), so one
+// output fragment carries both values of the SiLU(gate) * up product.
+// Down tiles hold 16 consecutive output rows of W_down.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ocq {
+
+constexpr uint32_t kBlobVersion = 1;
+constexpr char kBlobMagic[8] = {'O', 'C', 'Q', 'B', 'L', 'O', 'B', '1'};
+constexpr int kChunk = 128;           // inputs per chunk
+constexpr int kTileRows = 16;         // output rows per tile
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t v, size_t a = kAlign) { return (v + a - 1) / a * a; }
+
+enum Prec { kFP8 = 0, kFP8DownBF16 = 1, kFP4 = 2 };
+enum WeightKind { kWFP8 = 0, kWBF16 = 1, kWFP4 = 2 };
+
+struct BlobHeader {
+  char magic[8];
+  uint32_t version;
+  int32_t hidden, inter, prec_mode;
+  // byte offsets from the blob start
+  uint64_t off_gu_codes, off_gu_scales, off_gu_bscales;
+  uint64_t off_dn_codes, off_dn_scales, off_dn_bscales;
+  uint64_t total_bytes;
+  float s_gate, s_up, s_down;  // NVFP4 per-tensor scales (0 otherwise)
+  uint8_t pad[256 - 8 - 4 - 12 - 7 * 8 - 12];
+};
+static_assert(sizeof(BlobHeader) == 256, "header is 256 bytes");
+
+// bytes of a projection's codes / scale sections with `rows` outputs, `cols` inputs
+inline size_t codes_bytes(WeightKind k, size_t rows, size_t cols) {
+  switch (k) {
+    case kWFP8: return rows * cols;
+    case kWBF16: return rows * cols * 2;
+    case kWFP4: return rows * cols / 2;
+  }
+  return 0;
+}
+inline size_t chunk_groups(size_t cols) { return (cols / kChunk + 7) / 8; }
+inline size_t bscale_bytes(WeightKind k, size_t rows, size_t cols) {
+  return k == kWFP4 ? (rows / kTileRows) * chunk_groups(cols) * 1024 : 0;
+}
+
+struct BlobLayout {
+  WeightKind gu, dn;
+  uint64_t off_gu_codes, off_gu_scales, off_gu_bscales;
+  uint64_t off_dn_codes, off_dn_scales, off_dn_bscales;
+  uint64_t total;
+};
+
+inline bool shape_ok(int hidden, int inter) {
+  return hidden >= 128 && inter >= 128 && hidden <= 65536 && inter <= 65536 &&
+         hidden % kChunk == 0 && inter % kChunk == 0;
+}
+
+inline BlobLayout blob_layout(int hidden, int inter, int prec) {
+  BlobLayout L{};
+  L.gu = prec == kFP4 ? kWFP4 : kWFP8;
+  L.dn = prec == kFP4 ? kWFP4 : (prec == kFP8DownBF16 ? kWBF16 : kWFP8);
+  size_t H = hidden, I = inter;
+  size_t o = align_up(sizeof(BlobHeader));
+  L.off_gu_codes = o;   o = align_up(o + codes_bytes(L.gu, 2 * I, H));
+  L.off_gu_scales = o;  o = align_up(o + (L.gu == kWFP8 ? 2 * I * sizeof(float) : 0));
+  L.off_gu_bscales = o; o = align_up(o + bscale_bytes(L.gu, 2 * I, H));
+  L.off_dn_codes = o;   o = align_up(o + codes_bytes(L.dn, H, I));
+  L.off_dn_scales = o;  o = align_up(o + (L.dn == kWFP8 ? H * sizeof(float) : 0));
+  L.off_dn_bscales = o; o = align_up(o + bscale_bytes(L.dn, H, I));
+  L.total = o;
+  return L;
+}
+
+// ---------------------------------------------------------------------------
+// Execution plan and workspace
+// ---------------------------------------------------------------------------
+
+// m-tiles (16 rows each) per workgroup pass; instantiated template values
+constexpr int kMTChoices[] = {1, 2, 4, 7, 13};
+constexpr int kMTMax = 13;
+
+struct Plan {
+  int M, hidden, inter, prec;
+  int MT;          // m-tiles per m-block
+  int n_mblocks;   // m-blocks
+  int Mpad;        // rows of every activation buffer (n_mblocks * 16 * MT)
+  // gate/up kernel
+  int T1;          // interleaved tiles per workgroup
+  int ngroups1;    // (inter / 8) / T1
+  // down kernel
+  int T2;          // down tiles per workgroup
+  int ngroups2;    // (hidden / 16) / T2
+  int nsplit2;     // split-K factor
+  int chunks_per_split2;
+  // workspace offsets
+  size_t off_xq, off_sx, off_amax, off_h32, off_hq, off_hb, off_sh, off_part, off_cnt, total;
+};
+
+inline int pick_mt(int M) {
+  int need = (M + 15) / 16;
+  for (int c : kMTChoices)
+    if (c >= need) return c;
+  return kMTMax;
+}
+
+inline Plan make_plan(int M, int hidden, int inter, int prec) {
+  Plan p{};
+  p.M = M; p.hidden = hidden; p.inter = inter; p.prec = prec;
+  p.MT = pick_mt(M);
+  int rows_per_block = 16 * p.MT;
+  p.n_mblocks = (M + rows_per_block - 1) / rows_per_block;
+  p.Mpad = p.n_mblocks * rows_per_block;
+  // gate/up: tiles of 8 gate + 8 up columns
+  int nt1 = inter / 8;
+  p.T1 = 1;
+  for (int t : {3, 2}) {
+    if (nt1 % t == 0 && p.MT * t <= 39 && nt1 / t >= 192) { p.T1 = t; break; }
+  }
+  p.ngroups1 = nt1 / p.T1;
+  // down: tiles of 16 output columns, split-K over inter
+  int nt2 = hidden / 16;
+  int c2 = inter / kChunk;
+  p.T2 = 1;
+  for (int t : {8, 4, 3, 2}) {
+    if (nt2 % t == 0 && p.MT * t <= 39 && nt2 / t >= 16) { p.T2 = t; break; }
+  }
+  p.ngroups2 = nt2 / p.T2;
+  int target = 256 / p.n_mblocks;  // workgroups wanted per m-block
+  int ns = target / p.ngroups2;
+  if (ns < 1) ns = 1;
+  if (ns > c2 / 4) ns = c2 / 4 > 0 ? c2 / 4 : 1;   // keep >= 4 chunks (one per wave) per split
+  p.chunks_per_split2 = (c2 + ns - 1) / ns;
+  p.nsplit2 = (c2 + p.chunks_per_split2 - 1) / p.chunks_per_split2;
+  // workspace
+  size_t Mp = p.Mpad, H = hidden, I = inter;
+  size_t o = 0;
+  p.off_xq = o;   o = align_up(o + Mp * H);
+  p.off_sx = o;   o = align_up(o + Mp * 4);
+  p.off_amax = o; o = align_up(o + Mp * 4);
+  p.off_h32 = o;  o = align_up(o + (prec == kFP8DownBF16 ? 0 : Mp * I * 4));
+  p.off_hq = o;   o = align_up(o + (prec == kFP8DownBF16 ? 0 : Mp * I));
+  p.off_hb = o;   o = align_up(o + (prec == kFP8DownBF16 ? Mp * I * 2 : 0));
+  p.off_sh = o;   o = align_up(o + Mp * 4);
+  p.off_part = o; o = align_up(o + (p.nsplit2 > 1 ? (size_t)p.nsplit2 * Mp * H * 4 : 0));
+  p.off_cnt = o;  o = align_up(o + (size_t)p.n_mblocks * p.ngroups2 * 4);
+  p.total = o;
+  return p;
+}
+
+}  // namespace ocq

@@ -1,0 +1,195 @@
+"""Python binding of the ocq C ABI (include/ocq.h): argument marshalling only.
+
+Every step of the block runs in the HIP library libocq.so built in-tree next
+to this file (``python -m quantized_memory_bound_amd.build``).  There is no
+fallback: if the library is missing, every call raises.  PyTorch is used only
+for device memory and streams.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libocq.so")
+
+PREC_FP8 = 0
+PREC_FP8_DOWN_BF16 = 1
+PREC_FP4 = 2
+
+OK = 0
+ERR_INVALID_ARG = -1
+ERR_UNSUPPORTED = -2
+ERR_DEVICE = -3
+ERR_BUFFER_TOO_SMALL = -4
+ERR_BAD_BLOB = -5
+
+EXPORTS = ("ocq_version", "ocq_packed_bytes", "ocq_pack_weights_host", "ocq_pack_weights",
+           "ocq_unpack_weights_host", "ocq_workspace_bytes", "ocq_mlp_forward", "ocq_check_blob",
+           "ocq_last_error")
+
+
+class OcqError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__("ocq status %d: %s" % (status, message))
+        self.status = status
+
+
+class Taps(ctypes.Structure):
+    _fields_ = [("x_codes", ctypes.c_void_p), ("x_scales", ctypes.c_void_p),
+                ("h_out", ctypes.c_void_p), ("h_scales", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libocq.so (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libocq.so is not built (%s); run python -m quantized_memory_bound_amd.build" % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    vp, sz, i, f = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_float
+    L.ocq_version.argtypes, L.ocq_version.restype = [], i
+    L.ocq_last_error.argtypes, L.ocq_last_error.restype = [], ctypes.c_char_p
+    L.ocq_packed_bytes.argtypes, L.ocq_packed_bytes.restype = [i, i, i], sz
+    L.ocq_pack_weights_host.argtypes = [vp, vp, vp, i, i, i, vp, sz]
+    L.ocq_pack_weights_host.restype = i
+    L.ocq_pack_weights.argtypes = [vp, vp, vp, i, i, i, vp, sz, vp]
+    L.ocq_pack_weights.restype = i
+    L.ocq_unpack_weights_host.argtypes = [vp, sz, i, vp, vp, ctypes.POINTER(f)]
+    L.ocq_unpack_weights_host.restype = i
+    L.ocq_workspace_bytes.argtypes, L.ocq_workspace_bytes.restype = [i, i, i, i], sz
+    L.ocq_mlp_forward.argtypes = [vp, sz, vp, i, i, i, i, vp, vp, sz, ctypes.POINTER(Taps), vp]
+    L.ocq_mlp_forward.restype = i
+    L.ocq_check_blob.argtypes, L.ocq_check_blob.restype = [vp, sz, i, i, i, vp], i
+    _lib = L
+    return L
+
+
+def _check(status):
+    if status != OK:
+        raise OcqError(status, lib().ocq_last_error().decode())
+    return status
+
+
+def last_error():
+    return lib().ocq_last_error().decode()
+
+
+def version():
+    return lib().ocq_version()
+
+
+def packed_bytes(hidden, inter, prec_mode):
+    return lib().ocq_packed_bytes(hidden, inter, prec_mode)
+
+
+def workspace_bytes(M, hidden, inter, prec_mode):
+    return lib().ocq_workspace_bytes(M, hidden, inter, prec_mode)
+
+
+def _f32c(a):
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def pack_weights_host(w_gate, w_up, w_down, prec_mode):
+    """Quantize + pack on the host; returns the blob as a uint8 numpy array."""
+    wg, wu, wd = _f32c(w_gate), _f32c(w_up), _f32c(w_down)
+    inter, hidden = wg.shape
+    n = packed_bytes(hidden, inter, prec_mode)
+    if n == 0:
+        raise OcqError(ERR_UNSUPPORTED, "invalid shape or prec_mode")
+    out = np.empty(n, dtype=np.uint8)
+    _check(lib().ocq_pack_weights_host(wg.ctypes.data, wu.ctypes.data, wd.ctypes.data, hidden, inter,
+                                       prec_mode, out.ctypes.data, n))
+    return out
+
+
+def unpack_weights_host(blob, which, hidden, inter, prec_mode):
+    """Plain-layout codes / scales of one projection from a host blob."""
+    blob = np.ascontiguousarray(blob, dtype=np.uint8)
+    rows, cols = (inter, hidden) if which < 2 else (hidden, inter)
+    bf16 = prec_mode == PREC_FP8_DOWN_BF16 and which == 2
+    codes = np.zeros((rows, cols), dtype=np.uint16 if bf16 else np.uint8)
+    if prec_mode == PREC_FP4:
+        scales = np.zeros((rows, cols // 16), dtype=np.uint8)
+    elif bf16:
+        scales = None
+    else:
+        scales = np.zeros(rows, dtype=np.float32)
+    ts = ctypes.c_float(0.0)
+    _check(lib().ocq_unpack_weights_host(blob.ctypes.data, blob.nbytes, which, codes.ctypes.data,
+                                         None if scales is None else scales.ctypes.data, ctypes.byref(ts)))
+    return codes, scales, ts.value
+
+
+def _stream_handle(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def pack_weights(w_gate, w_up, w_down, prec_mode, device="cuda", stream=None):
+    """Quantize + pack and upload; returns a uint8 torch tensor on `device`."""
+    import torch
+    wg, wu, wd = _f32c(w_gate), _f32c(w_up), _f32c(w_down)
+    inter, hidden = wg.shape
+    n = packed_bytes(hidden, inter, prec_mode)
+    if n == 0:
+        raise OcqError(ERR_UNSUPPORTED, "invalid shape or prec_mode")
+    blob = torch.empty(n, dtype=torch.uint8, device=device)
+    _check(lib().ocq_pack_weights(wg.ctypes.data, wu.ctypes.data, wd.ctypes.data, hidden, inter, prec_mode,
+                                  blob.data_ptr(), n, _stream_handle(stream)))
+    return blob
+
+
+def check_blob(blob, hidden, inter, prec_mode, stream=None):
+    _check(lib().ocq_check_blob(blob.data_ptr(), blob.numel(), hidden, inter, prec_mode, _stream_handle(stream)))
+
+
+def mlp_forward(blob, x, hidden, inter, prec_mode, y=None, workspace=None, taps=None, stream=None):
+    """y = block(x) for x a bf16 [M, hidden] CUDA tensor; returns y (bf16 [M, hidden]).
+
+    taps: optional dict with any of x_codes, x_scales, h_out, h_scales tensors.
+    """
+    import torch
+    M = x.shape[0]
+    if y is None:
+        y = torch.empty((M, hidden), dtype=torch.bfloat16, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(max(1, workspace_bytes(M, hidden, inter, prec_mode)), dtype=torch.uint8,
+                                device=x.device)
+    t = None
+    if taps:
+        t = Taps(*(taps[k].data_ptr() if taps.get(k) is not None else None
+                   for k in ("x_codes", "x_scales", "h_out", "h_scales")))
+    _check(lib().ocq_mlp_forward(blob.data_ptr(), blob.numel(), x.data_ptr(), M, hidden, inter, prec_mode,
+                                 y.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                 ctypes.byref(t) if t is not None else None, _stream_handle(stream)))
+    return y
+
+
+class QuantizedMLP:
+    """One packed block on the GPU with its workspace, for repeated calls."""
+
+    def __init__(self, w_gate, w_up, w_down, prec_mode, device="cuda"):
+        self.inter, self.hidden = np.asarray(w_gate).shape
+        self.prec_mode = prec_mode
+        self.device = device
+        self.blob = pack_weights(w_gate, w_up, w_down, prec_mode, device)
+        self._ws = {}
+
+    def workspace(self, M):
+        import torch
+        if M not in self._ws:
+            self._ws[M] = torch.empty(workspace_bytes(M, self.hidden, self.inter, self.prec_mode),
+                                      dtype=torch.uint8, device=self.device)
+        return self._ws[M]
+
+    def __call__(self, x, y=None, taps=None, stream=None):
+        return mlp_forward(self.blob, x, self.hidden, self.inter, self.prec_mode, y=y,
+                           workspace=self.workspace(x.shape[0]), taps=taps, stream=stream)

@@ -1,0 +1,143 @@
+"""Host-side checks of the C-ABI library (no GPU needed).
+
+* the library loads and exports every entry point include/ocq.h declares;
+* the host packer's codes and scales equal the oracle's bit for bit (read
+  back through ocq_unpack_weights_host, the inverse of the fragment layout);
+* argument validation returns the documented status before touching a GPU.
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import mlp as O
+from quantized_memory_bound_amd import inputs as I
+from quantized_memory_bound_amd import ocq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_library_exports_every_declared_symbol():
+    with open(os.path.join(ROOT, "include", "ocq.h")) as f:
+        hdr = f.read()
+    declared = set(re.findall(r"\b(ocq_[a-z_]+)\s*\(", hdr))
+    assert declared == set(ocq.EXPORTS), declared ^ set(ocq.EXPORTS)
+    L = ocq.lib()
+    for name in declared:
+        assert hasattr(L, name), name
+    assert ocq.version() >= 10000
+
+
+def _packer_vs_oracle(hidden, inter, prec, seed=0, w_std=0.02):
+    d = I.make_inputs(hidden, inter, 1, w_std=w_std, seed=seed)
+    blob = ocq.pack_weights_host(d["w_gate"], d["w_up"], d["w_down"], prec)
+    ref = O.pack_block(d["w_gate"], d["w_up"], d["w_down"], prec)
+    for which, key in enumerate(("gate", "up", "down")):
+        codes, scales, ts = ocq.unpack_weights_host(blob, which, hidden, inter, prec)
+        r = ref[key]
+        if prec == O.PREC_FP4:
+            assert np.array_equal(codes, r[0]), key
+            assert np.array_equal(scales, r[1]), key
+            assert np.float32(ts) == r[2], key
+        elif prec == O.PREC_FP8_DOWN_BF16 and key == "down":
+            assert np.array_equal(codes, r), key
+        else:
+            assert np.array_equal(codes, r[0]), key
+            assert np.array_equal(scales, r[1]), key
+
+
+@pytest.mark.parametrize("prec", [0, 1, 2])
+@pytest.mark.parametrize("hidden,inter", [(256, 512), (384, 640), (128, 1152)])
+def test_packer_matches_oracle_small(hidden, inter, prec):
+    _packer_vs_oracle(hidden, inter, prec, seed=hidden + inter)
+
+
+@pytest.mark.parametrize("name", ["decode_fp8", "mixed_bf16_down", "nvfp4"])
+def test_packer_matches_oracle_workload_shapes(name):
+    cfg = I.WORKLOADS[name]
+    _packer_vs_oracle(cfg["hidden"], cfg["inter"], cfg["prec_mode"], seed=0, w_std=cfg["w_std"])
+
+
+def test_packer_zero_and_outlier_rows():
+    hidden, inter = 256, 512
+    d = I.make_inputs(hidden, inter, 1, seed=3)
+    d["w_gate"][5] = 0.0                       # zero row -> scale 0, codes 0
+    d["w_up"][7, 3] = 1e4                      # outlier
+    d["w_down"][:, :16] = 0.0                  # zero NVFP4 blocks
+    for prec in (0, 1, 2):
+        blob = ocq.pack_weights_host(d["w_gate"], d["w_up"], d["w_down"], prec)
+        ref = O.pack_block(d["w_gate"], d["w_up"], d["w_down"], prec)
+        for which, key in enumerate(("gate", "up", "down")):
+            codes, scales, ts = ocq.unpack_weights_host(blob, which, hidden, inter, prec)
+            r = ref[key]
+            rc = r if (prec == 1 and key == "down") else r[0]
+            assert np.array_equal(codes, rc), (prec, key)
+
+
+def test_packed_and_workspace_sizes():
+    assert ocq.packed_bytes(2048, 6144, 0) >= 3 * 2048 * 6144
+    assert ocq.packed_bytes(4096, 12288, 2) >= 3 * 4096 * 12288 // 2
+    assert ocq.packed_bytes(100, 6144, 0) == 0
+    assert ocq.packed_bytes(2048, 6144, 3) == 0
+    assert ocq.workspace_bytes(208, 2048, 6144, 0) > 0
+    assert ocq.workspace_bytes(0, 2048, 6144, 0) == 0
+    assert ocq.workspace_bytes(8193, 2048, 6144, 0) == 0
+
+
+def _fwd(**kw):
+    a = dict(blob=0x10000, nblob=1 << 30, x=0x20000, M=16, hidden=2048, inter=6144, prec=0, y=0x30000,
+             ws=0x40000, nws=1 << 30, taps=None, stream=None)
+    a.update(kw)
+    return ocq.lib().ocq_mlp_forward(a["blob"], a["nblob"], a["x"], a["M"], a["hidden"], a["inter"], a["prec"],
+                                     a["y"], a["ws"], a["nws"], a["taps"], a["stream"])
+
+
+def test_forward_argument_errors():
+    assert _fwd(hidden=2000) == ocq.ERR_UNSUPPORTED
+    assert _fwd(inter=100) == ocq.ERR_UNSUPPORTED
+    assert _fwd(prec=7) == ocq.ERR_INVALID_ARG
+    assert _fwd(M=0) == ocq.ERR_INVALID_ARG
+    assert _fwd(M=9000) == ocq.ERR_INVALID_ARG
+    assert _fwd(x=None) == ocq.ERR_INVALID_ARG
+    assert _fwd(y=0x30008) == ocq.ERR_INVALID_ARG          # misaligned
+    assert _fwd(nblob=1000) == ocq.ERR_BUFFER_TOO_SMALL
+    assert _fwd(nws=1000) == ocq.ERR_BUFFER_TOO_SMALL
+    assert "workspace" in ocq.last_error()
+    taps = ocq.Taps(0x50004, None, None, None)
+    assert _fwd(taps=ctypes.pointer(taps)) == ocq.ERR_INVALID_ARG
+
+
+def test_pack_argument_errors():
+    L = ocq.lib()
+    w = np.zeros((512, 256), np.float32)
+    out = np.zeros(10, np.uint8)
+    assert L.ocq_pack_weights_host(w.ctypes.data, w.ctypes.data, w.ctypes.data, 256, 512, 0, out.ctypes.data, 10) \
+        == ocq.ERR_BUFFER_TOO_SMALL
+    assert L.ocq_pack_weights_host(None, w.ctypes.data, w.ctypes.data, 256, 512, 0, out.ctypes.data, 10) \
+        == ocq.ERR_INVALID_ARG
+    assert L.ocq_pack_weights_host(w.ctypes.data, w.ctypes.data, w.ctypes.data, 250, 512, 0, out.ctypes.data, 10) \
+        == ocq.ERR_UNSUPPORTED
+
+
+def test_unpack_rejects_bad_blob():
+    d = I.make_inputs(256, 512, 1, seed=1)
+    blob = ocq.pack_weights_host(d["w_gate"], d["w_up"], d["w_down"], 0)
+    bad = blob.copy()
+    bad[0] ^= 0xFF
+    with pytest.raises(ocq.OcqError) as e:
+        ocq.unpack_weights_host(bad, 0, 256, 512, 0)
+    assert e.value.status == ocq.ERR_BAD_BLOB
+    with pytest.raises(ocq.OcqError) as e:
+        ocq.unpack_weights_host(blob[:1000], 0, 256, 512, 0)
+    assert e.value.status == ocq.ERR_BUFFER_TOO_SMALL
+
+
+def test_forward_without_device_reports_device_error():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    st = _fwd()
+    assert st == ocq.ERR_DEVICE, (st, ocq.last_error())

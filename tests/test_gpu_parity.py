@@ -1,0 +1,180 @@
+"""GPU parity: the HIP path (through the C ABI) against the oracle.
+
+Same seeded inputs on both sides.  Small shapes span several tiles and a
+ragged tail in every dimension the kernels tile (16-row m-tiles, 128-input
+chunks, 8-column gate/up tiles, 16-column down tiles, split-K); the workload
+shapes run in the launch configuration the benchmark times, with the oracle
+evaluated on all rows or, for the two largest, on sampled rows (the block is
+row-independent, so the oracle on a subset of rows is exact for those rows).
+"""
+
+import numpy as np
+import pytest
+
+from oracle import mlp as O
+from quantized_memory_bound_amd import inputs as I
+from quantized_memory_bound_amd import ocq
+from parity import bf16_near_zero, bf16_rank, check_codes, check_y, e4m3_rank
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ocq.lib()
+
+
+def _to_dev_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to("cuda").view(torch.bfloat16)
+
+
+def run_gpu(d, prec, blob=None, x_bits=None):
+    """One forward call with every tap set; returns numpy copies."""
+    x_bits = d["x_bits"] if x_bits is None else x_bits
+    M, H = x_bits.shape
+    Iw = d["w_gate"].shape[0]
+    if blob is None:
+        blob = ocq.pack_weights(d["w_gate"], d["w_up"], d["w_down"], prec)
+    x = _to_dev_bf16(x_bits)
+    taps = {
+        "x_codes": torch.empty((M, H), dtype=torch.uint8, device="cuda"),
+        "x_scales": torch.empty(M, dtype=torch.float32, device="cuda"),
+        "h_out": torch.empty((M, Iw), dtype=torch.int16 if prec == O.PREC_FP8_DOWN_BF16 else torch.uint8,
+                             device="cuda"),
+        "h_scales": torch.empty(M, dtype=torch.float32, device="cuda"),
+    }
+    y = ocq.mlp_forward(blob, x, H, Iw, prec, taps=taps)
+    torch.cuda.synchronize()
+    out = {"y": y.view(torch.int16).cpu().numpy().view(np.uint16),
+           "xq": taps["x_codes"].cpu().numpy(), "sx": taps["x_scales"].cpu().numpy()}
+    if prec == O.PREC_FP8_DOWN_BF16:
+        out["hb"] = taps["h_out"].cpu().numpy().view(np.uint16)
+    else:
+        out["hq"] = taps["h_out"].cpu().numpy()
+        out["sh"] = taps["h_scales"].cpu().numpy()
+    return out, blob
+
+
+def compare(g, r, prec, rows=None, what=""):
+    sel = (lambda a: a[rows]) if rows is not None else (lambda a: a)
+    assert np.array_equal(sel(g["xq"]), r["xq"]), what + ": x codes differ"
+    assert np.array_equal(sel(g["sx"]), r["sx"]), what + ": x scales differ"
+    if prec == O.PREC_FP8_DOWN_BF16:
+        check_codes(sel(g["hb"]), r["hb"], bf16_rank, what + " hb", bf16_near_zero(sel(g["hb"]), r["hb"]))
+    else:
+        check_codes(sel(g["hq"]), r["hq"], e4m3_rank, what + " hq")
+        np.testing.assert_allclose(sel(g["sh"]), r["sh"], rtol=1e-4, err_msg=what + " sh")
+    return check_y(sel(g["y"]), r["y"], what + " y")
+
+
+SMALL = [(256, 512, 1), (256, 512, 4), (384, 640, 17), (512, 1024, 37), (256, 768, 100), (128, 384, 208),
+         (256, 512, 300), (640, 384, 65)]
+
+
+@pytest.mark.parametrize("prec", [0, 1, 2])
+@pytest.mark.parametrize("hidden,inter,M", SMALL)
+def test_small_shapes(hidden, inter, M, prec):
+    print("case hidden=%d inter=%d M=%d prec=%d" % (hidden, inter, M, prec), flush=True)
+    d = I.make_inputs(hidden, inter, M, x_outliers=True, w_std=0.02, seed=hidden * 7 + inter + M)
+    g, _ = run_gpu(d, prec)
+    r = O.block_reference(d["x_bits"], d["w_gate"], d["w_up"], d["w_down"], prec)
+    compare(g, r, prec, what="%dx%d M=%d prec=%d" % (hidden, inter, M, prec))
+
+
+_PACK_CACHE = {}
+
+
+def _workload(name):
+    if name not in _PACK_CACHE:
+        d = I.workload_inputs(name)
+        cfg = I.WORKLOADS[name]
+        _PACK_CACHE[name] = (d, O.pack_block(d["w_gate"], d["w_up"], d["w_down"], cfg["prec_mode"]),
+                             ocq.pack_weights(d["w_gate"], d["w_up"], d["w_down"], cfg["prec_mode"]))
+    return _PACK_CACHE[name]
+
+
+@pytest.mark.parametrize("name", ["tiny_fp8", "decode_fp8", "spec_verify_fp8"])
+def test_workload_fp8_full(name):
+    print("case workload", name, flush=True)
+    d, packed, blob = _workload(name)
+    g, _ = run_gpu(d, packed["prec_mode"], blob=blob)
+    r = O.forward(d["x_bits"], packed)
+    rel, mx = compare(g, r, packed["prec_mode"], what=name)
+    print("%s: y normwise %.2e, max %.2e" % (name, rel, mx))
+
+
+def _sample_rows(M, n=48):
+    rows = np.unique(np.concatenate([np.linspace(0, M - 1, n).astype(int), np.arange(max(0, M - 5), M)]))
+    return rows
+
+
+def test_workload_mixed_bf16_down_sampled():
+    print("case workload mixed_bf16_down", flush=True)
+    d, packed, blob = _workload("mixed_bf16_down")
+    g, _ = run_gpu(d, packed["prec_mode"], blob=blob)
+    rows = _sample_rows(d["x_bits"].shape[0])
+    r = O.forward(d["x_bits"][rows], packed)
+    compare(g, r, packed["prec_mode"], rows=rows, what="mixed_bf16_down")
+
+
+@pytest.mark.parametrize("M", I.NVFP4_M_SWEEP)
+def test_workload_nvfp4_sweep(M):
+    print("case workload nvfp4 M=%d" % M, flush=True)
+    d, packed, blob = _workload("nvfp4")
+    xb = d["x_bits"][:M]
+    g, _ = run_gpu(d, 2, blob=blob, x_bits=xb)
+    rows = _sample_rows(M) if M > 64 else None
+    r = O.forward(xb[rows] if rows is not None else xb, packed)
+    compare(g, r, 2, rows=rows, what="nvfp4 M=%d" % M)
+
+
+@pytest.mark.parametrize("prec", [0, 1, 2])
+def test_deterministic_and_zero_rows(prec):
+    print("case determinism prec=%d" % prec, flush=True)
+    d = I.make_inputs(512, 1024, 40, x_outliers=True, seed=11)
+    d["x_bits"][3] = 0
+    d["x_bits"][39] = 0x8000                  # -0.0 row
+    g1, blob = run_gpu(d, prec)
+    g2, _ = run_gpu(d, prec, blob=blob)
+    assert np.array_equal(g1["y"], g2["y"])
+    for row in (3, 39):
+        assert g1["sx"][row] == 0 and np.all(g1["xq"][row] & 0x7F == 0)
+        assert np.all(g1["y"][row] & 0x7FFF == 0)
+    r = O.block_reference(d["x_bits"], d["w_gate"], d["w_up"], d["w_down"], prec)
+    compare(g1, r, prec, what="zero rows prec=%d" % prec)
+
+
+def test_lossless_grid_inputs_tight():
+    # x and weights on the E4M3 grid with power-of-two scales: quantization of x
+    # and the weights is exact, so the only differences left are fp32 vs fp64
+    # accumulation order and the fp32 SiLU
+    print("case lossless grid", flush=True)
+    rng = np.random.default_rng(21)
+    M, H, Iw = 20, 256, 384
+
+    def grid(n, k, lo, hi):
+        c = rng.integers(0, 0x7F, size=(n, k)).astype(np.uint8) | (rng.integers(0, 2, (n, k)) * 0x80).astype(np.uint8)
+        c[np.arange(n), rng.integers(0, k, n)] = 0x7E
+        v = torch.from_numpy(c).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+        return v * np.exp2(rng.integers(lo, hi, n))[:, None]
+
+    x = grid(M, H, -9, -5)
+    d = {"x_bits": torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16),
+         "w_gate": grid(Iw, H, -16, -12).astype(np.float32), "w_up": grid(Iw, H, -16, -12).astype(np.float32),
+         "w_down": grid(H, Iw, -12, -8).astype(np.float32)}
+    g, _ = run_gpu(d, 0)
+    r = O.block_reference(d["x_bits"], d["w_gate"], d["w_up"], d["w_down"], 0)
+    rel, mx = compare(g, r, 0, what="lossless")
+    assert rel < 1e-3
+
+
+def test_check_blob():
+    d = I.make_inputs(256, 512, 4, seed=2)
+    blob = ocq.pack_weights(d["w_gate"], d["w_up"], d["w_down"], 0)
+    ocq.check_blob(blob, 256, 512, 0)
+    with pytest.raises(ocq.OcqError) as e:
+        ocq.check_blob(blob, 256, 512, 1)
+    assert e.value.status == ocq.ERR_BAD_BLOB

@@ -1,0 +1,293 @@
+#!/usr/bin/env python3
+"""Benchmark of the quantized spec-verify MLP block on one MI355X.
+
+A step is one pass of the whole block (x-quant, gate/up + SiLU(gate)*up +
+per-token requant, down projection) over one batch of M rows.  Default
+workload: hidden 2048, inter 6144, M = 208 rows (16 requests x (1 + 12 draft
+tokens)), FP8 E4M3 weights in all three projections, synthetic seeded
+inputs (x ~ N(0,1) in bf16, weights ~ N(0, 0.02) quantized per output row).
+
+Timing: R copies of the packed weights are rotated so that R x blob >= 512 MB,
+twice the MI355X's 256 MB last-level (Infinity) cache, as consecutive layers
+of a model would see.  Inputs are resident in HBM before the timed region.
+The stream is pre-filled behind a GPU spin so the K timed steps run back to
+back on the GPU (the host-side cost of a call, ~20 us in Python, would
+otherwise pace the ~10 us steps).  HIP events bracket the K steps; the
+library's stage-event hook brackets the gate/up kernel of every step.
+
+Output: one JSON line (see the field list at the end of main()).
+"""
+
+import argparse
+import ctypes
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0   # dense fp16 / bf16
+MFMA_FP8_PEAK_TFLOPS = 5000.0   # dense fp8
+MALL_BYTES = 256 << 20
+
+
+def alg_bytes(M, H, I, prec):
+    """Compulsory traffic of one block: weight codes + weight scales + x (bf16,
+    read once) + y (bf16, written once)."""
+    if prec == 0:
+        w = 2 * I * H + 2 * I * 4 + H * I + H * 4
+    elif prec == 1:
+        w = 2 * I * H + 2 * I * 4 + 2 * H * I
+    else:
+        w = I * H + 2 * I * H // 16 + 8 + H * I // 2 + H * I // 16 + 4
+    return w + 2 * M * H * 2
+
+
+def gateup_alg(M, H, I, prec):
+    """Gate/up kernel: weight codes + scales + x codes and scales read once
+    (h stays on chip in the method, so its spill is not counted) and flops."""
+    if prec in (0, 1):
+        w = 2 * I * H + 2 * I * 4
+    else:
+        w = I * H + 2 * I * H // 16 + 8
+    return w + M * H + M * 4, 2.0 * M * H * 2 * I
+
+
+class HipEvents:
+    """Minimal hipEvent_t access through libamdhip64 (for the library hook)."""
+
+    def __init__(self):
+        self.h = ctypes.CDLL("libamdhip64.so")
+        self.h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        e = ctypes.c_void_p()
+        if self.h.hipEventCreate(ctypes.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return e.value
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        if self.h.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, e):
+        self.h.hipEventDestroy(e)
+
+
+def kernel_source_digest():
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "quantized_memory_bound_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload, digest):
+    """HBM traffic of the gate/up kernel from a committed rocprofv3 --pmc
+    summary, if it was taken on the current kernel sources."""
+    p = os.path.join(ROOT, "profiles", "gateup_%s_pmc_traffic.txt" % workload)
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        for line in f:
+            if line.startswith("TRAFFIC_JSON "):
+                d = json.loads(line[len("TRAFFIC_JSON "):])
+                if d.get("source_digest") == digest:
+                    return d.get("bytes_per_dispatch")
+    return None
+
+
+def cpu_baseline(inp, prec, M, seconds):
+    """The oracle (plain fp64 numpy) timed on this host's cores on the same
+    block: all M rows, pre-packed weights, repeated until `seconds` pass."""
+    from threadpoolctl import threadpool_info
+    from oracle import mlp as O
+    packed = O.pack_block(inp["w_gate"], inp["w_up"], inp["w_down"], prec)
+    O.forward(inp["x_bits"], packed)                       # warm caches
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        O.forward(inp["x_bits"], packed)
+        reps += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = (time.perf_counter() - t0) / reps
+    threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    return dt, reps, threads
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--workload", default="spec_verify_fp8")
+    ap.add_argument("--M", type=int, default=None, help="leading rows of the workload (NVFP4 sweep)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stage-events", action="store_true", help="skip the gate/up kernel timing pass")
+    ap.add_argument("--mode", choices=["graph", "eager"], default="graph",
+                    help="graph: replay a captured HIP graph of R steps; eager: one call per step")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="also run a plain 256 MiB copy kernel (counter calibration for rocprofv3 --pmc)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build measures one GPU; the block is row-independent and shards as data "
+              "parallel over requests with no exchange (see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from quantized_memory_bound_amd import inputs as I
+    from quantized_memory_bound_amd import ocq
+
+    cfg = I.WORKLOADS[args.workload]
+    H, Iw, prec = cfg["hidden"], cfg["inter"], cfg["prec_mode"]
+    inp = I.workload_inputs(args.workload, M=args.M)
+    M = inp["x_bits"].shape[0]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    blob0 = ocq.pack_weights(inp["w_gate"], inp["w_up"], inp["w_down"], prec)
+    R = max(2, -(-2 * MALL_BYTES // blob0.numel()))
+    blobs = [blob0] + [blob0.clone() for _ in range(R - 1)]
+    x = torch.from_numpy(inp["x_bits"].view(np.int16)).to(dev).view(torch.bfloat16)
+    y = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(ocq.workspace_bytes(M, H, Iw, prec), dtype=torch.uint8, device=dev)
+    if args.copy_calib:
+        src = torch.ones(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.add(src, 0, out=dst)
+    torch.cuda.synchronize()
+
+    def step(i):
+        ocq.mlp_forward(blobs[i % R], x, H, Iw, prec, y=y, workspace=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = HipEvents()
+
+    # --- timed region: K steps, HIP events on the stream the kernels run on
+    if args.mode == "graph":
+        # one captured graph holds R consecutive steps (one per weight copy)
+        cs = torch.cuda.Stream()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=cs):
+            for i in range(R):
+                step(i)
+        for _ in range(2):
+            graph.replay()
+        torch.cuda.synchronize()
+        n_rep = -(-K // R)
+        K = n_rep * R
+        t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t_start.record()
+        for _ in range(n_rep):
+            graph.replay()
+        t_end.record()
+        torch.cuda.synchronize()
+    else:
+        t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        # keep the GPU busy while the host enqueues the steps (~25 us each)
+        torch.cuda._sleep(int(2.4e9 * max(0.02, 30e-6 * K)))
+        t_start.record()
+        for i in range(K):
+            step(i)
+        t_end.record()
+        torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / K
+
+    # --- gate/up kernel duration: the library's stage events around the
+    # gate/up launch of each step, steps enqueued behind a GPU spin
+    gu_ms = None
+    if not args.no_stage_events:
+        Kr = min(256, args.steps)
+        ga = [ev.create() for _ in range(Kr)]
+        gb = [ev.create() for _ in range(Kr)]
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(2.4e9 * 0.02))
+        for i in range(Kr):
+            ocq.set_stage_events([None, ga[i], gb[i], None, None])
+            step(i)
+        ocq.set_stage_events(None)
+        torch.cuda.synchronize()
+        gu = [ev.elapsed_ms(a, b) for a, b in zip(ga, gb)]
+        gu_ms = sum(gu) / len(gu)
+        for e in ga + gb:
+            ev.destroy(e)
+
+    ab = alg_bytes(M, H, Iw, prec)
+    gbps = ab / (ms_step * 1e-3) / 1e9
+    tok_s = M / (ms_step * 1e-3)
+
+    roof = None
+    if gu_ms:
+        gbytes, gflops = gateup_alg(M, H, Iw, prec)
+        t_hbm = gbytes / (HBM_PEAK_GBPS * 1e9)
+        t_mfma = gflops / (MFMA_F16_PEAK_TFLOPS * 1e12)
+        traffic = read_traffic(args.workload if args.M is None else "%s_M%d" % (args.workload, M),
+                               kernel_source_digest())
+        if t_mfma > t_hbm:
+            ach = gflops / (gu_ms * 1e-3) / 1e12
+            roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(ach / MFMA_F16_PEAK_TFLOPS, 4), "traffic": traffic}
+        else:
+            ach = gbytes / (gu_ms * 1e-3) / 1e9
+            roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": traffic}
+        roof["kernel"] = "k_gateup (gate/up GEMM + SiLU*up + per-token amax)"
+        roof["us_per_launch"] = round(gu_ms * 1e3, 3)
+        roof["alg_bytes_per_launch"] = gbytes
+        roof["alg_flops_per_launch"] = gflops
+        roof["hbm_frac_at_this_duration"] = round(gbytes / (gu_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        dt, reps, threads = cpu_baseline(inp, prec, M, args.cpu_seconds)
+        cpu = {"value": round(ab / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+               "sample": "whole block, all %d rows, weights pre-packed, %d repetitions (%.2f s each)" % (M, reps, dt),
+               "tokens_per_s": round(M / dt, 1), "us_per_block": round(dt * 1e6, 1)}
+
+    prec_name = {0: "fp8_e4m3", 1: "fp8_e4m3 gate/up + bf16 down", 2: "nvfp4 (e2m1 + e4m3 block scales)"}[prec]
+    out = {
+        "metric": "achieved HBM GB/s (% of peak) + verified tokens/s per MLP block, M=208",
+        "value": round(gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "mode": args.mode,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e4m3" if prec == 0 else prec_name,
+        "data": "synthetic (seeded; shapes and distributions of the workload)",
+        "config": {"workload": args.workload, "hidden": H, "inter": Iw, "M": M, "prec_mode": prec_name,
+                   "weight_copies_rotated": R, "alg_bytes_per_block": ab},
+        "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "tokens_per_s": round(tok_s, 1),
+        "us_per_block": round(ms_step * 1e3, 3),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

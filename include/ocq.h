@@ -100,8 +100,9 @@ ocq_status ocq_unpack_weights_host(const void* packed_host, size_t packed_bytes,
 /* Device workspace bytes needed by ocq_mlp_forward for this call shape. */
 size_t ocq_workspace_bytes(int M, int hidden, int inter, int prec_mode);
 
-/* Optional plain-layout copies of the intermediates, for parity checks.
- * Each pointer is a device pointer or NULL.
+/* Optional plain-layout copies of the intermediates, for parity checks,
+ * written by the call's own kernels as they produce them.  Each pointer is a
+ * 16-byte-aligned device pointer or NULL.
  *   x_codes [M, hidden] uint8, x_scales [M] float,
  *   h_out:  FP8/NVFP4 modes -> E4M3 codes [M, inter] uint8;
  *           BF16-down mode  -> bf16 bits [M, inter] uint16,
@@ -134,6 +135,15 @@ ocq_status ocq_mlp_forward(const void* packed_dev, size_t packed_bytes, const vo
  * (hidden, inter, prec_mode): OCQ_OK or OCQ_ERR_BAD_BLOB. */
 ocq_status ocq_check_blob(const void* packed_dev, size_t packed_bytes, int hidden, int inter,
                           int prec_mode, void* stream);
+
+/* Per-stage timing hook (profiling).  When set, every later ocq_mlp_forward
+ * on this thread records events[i] (hipEvent_t passed as void*, owned by the
+ * caller; NULL entries are skipped) on the call's stream at stage boundary i:
+ *   0 before the x quantization, 1 before gate/up + SiLU, 2 after gate/up,
+ *   3 before the down projection, 4 after the down projection.
+ * count must be 5 to enable, 0 (or events == NULL) to disable.  The pointer
+ * array is copied; the events must stay valid while the hook is set. */
+ocq_status ocq_set_stage_events(void* const* events, int count);
 
 /* Message for the last failure on this thread ("" if none). */
 const char* ocq_last_error(void);

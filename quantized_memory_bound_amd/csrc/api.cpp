@@ -11,6 +11,8 @@
 namespace ocq {
 
 static thread_local std::string g_err;
+static thread_local void* g_stage_events[5];
+static thread_local bool g_stage_on = false;
 
 ocq_status set_error(ocq_status st, const char* msg) {
   g_err = msg ? msg : "";
@@ -41,6 +43,18 @@ extern "C" {
 int ocq_version(void) { return 10000; }
 
 const char* ocq_last_error(void) { return g_err.c_str(); }
+
+ocq_status ocq_set_stage_events(void* const* events, int count) {
+  g_err.clear();
+  if (events == nullptr || count == 0) {
+    g_stage_on = false;
+    return OCQ_OK;
+  }
+  if (count != 5) return set_error(OCQ_ERR_INVALID_ARG, "count must be 5 (or 0 to disable)");
+  for (int i = 0; i < 5; ++i) g_stage_events[i] = events[i];
+  g_stage_on = true;
+  return OCQ_OK;
+}
 
 size_t ocq_packed_bytes(int hidden, int inter, int prec_mode) {
   if (prec_mode < 0 || prec_mode > 2 || !shape_ok(hidden, inter)) return 0;
@@ -133,27 +147,10 @@ ocq_status ocq_mlp_forward(const void* packed_dev, size_t packed_bytes, const vo
       if (t && !aligned16(t)) return set_error(OCQ_ERR_INVALID_ARG, "tap pointers must be 16-byte aligned");
   }
   FwdArgs a{(const uint8_t*)packed_dev, (const uint16_t*)x_bf16_dev, (uint16_t*)y_bf16_dev, (uint8_t*)workspace_dev,
-            stream};
+            stream, g_stage_on ? g_stage_events : nullptr, ocq_taps{}};
+  if (taps) a.taps = *taps;
   int rc = launch_forward(p, a);
   if (rc != 0) return set_hip_error((hipError_t)rc, "kernel launch");
-  if (taps) {
-    hipStream_t s = (hipStream_t)stream;
-    uint8_t* ws = (uint8_t*)workspace_dev;
-    hipError_t e = hipSuccess;
-    if (taps->x_codes && e == hipSuccess)
-      e = hipMemcpyAsync(taps->x_codes, ws + p.off_xq, (size_t)M * hidden, hipMemcpyDeviceToDevice, s);
-    if (taps->x_scales && e == hipSuccess)
-      e = hipMemcpyAsync(taps->x_scales, ws + p.off_sx, (size_t)M * 4, hipMemcpyDeviceToDevice, s);
-    if (taps->h_out && e == hipSuccess) {
-      if (prec_mode == kFP8DownBF16)
-        e = hipMemcpyAsync(taps->h_out, ws + p.off_hb, (size_t)M * inter * 2, hipMemcpyDeviceToDevice, s);
-      else
-        e = hipMemcpyAsync(taps->h_out, ws + p.off_hq, (size_t)M * inter, hipMemcpyDeviceToDevice, s);
-    }
-    if (taps->h_scales && prec_mode != kFP8DownBF16 && e == hipSuccess)
-      e = hipMemcpyAsync(taps->h_scales, ws + p.off_sh, (size_t)M * 4, hipMemcpyDeviceToDevice, s);
-    if (e != hipSuccess) return set_hip_error(e, "tap copies");
-  }
   return OCQ_OK;
 }
 

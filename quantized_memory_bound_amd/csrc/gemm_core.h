@@ -1,0 +1,319 @@
+// Matrix-core main loops of the skinny GEMMs (activations [rows x K] times
+// weight tiles [16 x K]), in two decompositions:
+//
+//  K-split (few rows, M <= 64): the NW waves of a workgroup take the chunks of
+//    the input range round-robin; every wave loads its weight fragments
+//    straight from HBM into registers (non-temporal 16 B per lane, two chunks
+//    in flight) and keeps accumulators for all rows; the NW partial tiles are
+//    summed in LDS in wave order (deterministic).  With one or two chunks per
+//    wave, all of a workgroup's weight loads are in flight at once.
+//
+//  M-split (many rows): each wave owns a quarter of the m-tiles and runs over
+//    every chunk; the weight chunk is loaded once per workgroup (units spread
+//    over the waves), converted once to the matrix-core operand format and
+//    staged in a two-slot LDS ring; activations are prefetched per wave into
+//    a ring of register buffers.  One workgroup barrier per chunk; no
+//    cross-wave reduction.
+//
+// Accumulator layout (MFMA 16x16 fp32): lane l holds rows 4 (l/16) + i,
+// i = 0..3, of column l % 16 of the tile.
+#pragma once
+#include "kcommon.h"
+
+namespace ocq {
+
+// ---------------------------------------------------------------- per-chunk registers (K-split)
+
+template <int BF, int MT, int T>
+struct ChunkRegs {
+  AFrag<BF> a[MT];
+  v4i b[T][Fmt<BF>::kUnits];
+  uint32_t sb[T];
+};
+
+// Global operand pointers of one lane.
+struct LanePtrs {
+  const uint8_t* a;    // activation block (m-tile 0, chunk 0) + lane * 16 (fragment order)
+  size_t a_mt_stride;  // bytes between m-tiles (all chunks of 16 rows)
+  int a_chunk;         // bytes per (m-tile, chunk) block
+  const uint8_t* w;    // weight tile 0 of the group, + lane * 16
+  size_t w_tile;       // bytes per weight tile
+  const uint8_t* wb;   // NVFP4 block-scale groups of tile 0, + lane * 16
+  size_t wb_tile;
+};
+
+// A: fragment-ordered activations of the workgroup's first m-tile, K inputs
+template <int BF>
+__device__ __forceinline__ LanePtrs lane_ptrs(const void* A, int K, const uint8_t* W, size_t w_tile,
+                                              const uint8_t* Wb, size_t wb_tile) {
+  const int lane = threadIdx.x & 63;
+  LanePtrs p;
+  p.a = (const uint8_t*)A + lane * 16;
+  p.a_chunk = AGeom<BF>::kBlk;
+  p.a_mt_stride = (size_t)(K / kChunk) * AGeom<BF>::kBlk;
+  p.w = W + lane * 16;
+  p.w_tile = w_tile;
+  p.wb = Wb + lane * 16;
+  p.wb_tile = wb_tile;
+  return p;
+}
+
+template <int BF, int MT, int T>
+__device__ __forceinline__ void load_chunk(ChunkRegs<BF, MT, T>& r, const LanePtrs& p, int c) {
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+#pragma unroll
+    for (int u = 0; u < Fmt<BF>::kUnits; ++u)
+      r.b[t][u] = ld_nt((const v4i*)(p.w + t * p.w_tile + (size_t)c * Fmt<BF>::kGlobal + u * 1024));
+    if constexpr (BF == kB_FP4_F16)
+      r.sb[t] = *(const uint16_t*)(p.wb + t * p.wb_tile + (size_t)(c >> 3) * 1024 + 2 * (c & 7));
+  }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) load_a<BF>(r.a[mt], p.a + mt * p.a_mt_stride + (size_t)c * p.a_chunk);
+}
+
+// B operand of tile t, sub-step i, from raw registers
+template <int BF, int MT, int T>
+__device__ __forceinline__ auto b_from_regs(const ChunkRegs<BF, MT, T>& r, int t, int i) {
+  if constexpr (BF == kB_FP8) {
+    return cat(r.b[t][0], r.b[t][1]);
+  } else if constexpr (BF == kB_FP8_F16) {
+    const v4i& w = r.b[t][i >> 1];
+    return e4m3x8_to_f16((uint32_t)w[2 * (i & 1)], (uint32_t)w[2 * (i & 1) + 1]);
+  } else if constexpr (BF == kB_BF16) {
+    return __builtin_bit_cast(v8bf, r.b[t][i]);
+  } else {
+    v2h s0, s1;
+    e4m3x2_scales(r.sb[t], s0, s1);
+    return e2m1x8_to_f16((uint32_t)r.b[t][0][i], i < 2 ? s0 : s1);
+  }
+}
+
+// acc[j][t] += A[j] x B[t] over one chunk (all NMT m-tiles; padding tiles
+// hold duplicate data and are discarded by the caller)
+template <int BF, int NMT, int T, class BGet>
+__device__ __forceinline__ void compute_chunk(v4f (&acc)[NMT][T], const AFrag<BF> (&a)[NMT], int, BGet bget) {
+  if constexpr (BF == kB_FP8) {
+    v8i b[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) b[t] = bget(t, 0);
+#pragma unroll
+    for (int j = 0; j < NMT; ++j) {
+      const v8i av = cat(a[j].q[0], a[j].q[1]);
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+        acc[j][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, b[t], acc[j][t], 0, 0, 0, 0, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      decltype(bget(0, 0)) b[T];
+#pragma unroll
+      for (int t = 0; t < T; ++t) b[t] = bget(t, i);
+#pragma unroll
+      for (int j = 0; j < NMT; ++j) {
+        if constexpr (BF == kB_BF16) {
+          const v8bf av = __builtin_bit_cast(v8bf, a[j].q[i]);
+#pragma unroll
+          for (int t = 0; t < T; ++t) acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b[t], acc[j][t], 0, 0, 0);
+        } else {
+          const v4i& w = a[j].q[i >> 1];
+          const v8h av = e4m3x8_to_f16((uint32_t)w[2 * (i & 1)], (uint32_t)w[2 * (i & 1) + 1]);
+#pragma unroll
+          for (int t = 0; t < T; ++t) acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, b[t], acc[j][t], 0, 0, 0);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- software pipeline
+//
+// Runs proc(d, k) for k = 0 .. n-1 with chunk k held in register buffer
+// d = k % D, refilling buffer d with chunk k + D right after it is consumed.
+// When n is a positive multiple of D the prologue and every steady-state
+// refill are unconditional and the last group is peeled, so the compiler sees
+// the same sequence of outstanding loads on every path into the loop and
+// waits only for the buffer it is about to use (a conditional load would make
+// it wait for all outstanding loads).  Other n take the general loop.
+template <int D, class Load, class Proc>
+__device__ __forceinline__ void pipelined(int n, Load load, Proc proc) {
+  if (n >= D && n % D == 0) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) load(d, d);
+    for (int g = 0; g + D < n; g += D) {
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        proc(d, g + d);
+        load(d, g + d + D);
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < D; ++d) proc(d, n - D + d);
+  } else {
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+      if (d < n) load(d, d);
+    for (int g = 0; g < n; g += D) {
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        if (g + d < n) {
+          proc(d, g + d);
+          if (g + d + D < n) load(d, g + d + D);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- K-split main loop
+
+template <int BF, int MT, int T>
+__device__ __forceinline__ void zero_b(ChunkRegs<BF, MT, T>& r) {
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+#pragma unroll
+    for (int u = 0; u < Fmt<BF>::kUnits; ++u) r.b[t][u] = v4i{0, 0, 0, 0};
+    r.sb[t] = 0u;
+  }
+}
+
+// Every wave runs the same number of iterations (two chunks in flight); a
+// chunk index past the range is clamped to the last chunk for the loads and
+// its weight operand is zeroed, so no load depends on the wave.
+template <int BF, int MT, int T, int NW>
+__device__ __forceinline__ void ks_mainloop(const LanePtrs& p, int c0, int c1, v4f (&acc)[MT][T]) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nk = (c1 - c0 + NW - 1) / NW;
+  ChunkRegs<BF, MT, T> r[2];
+  pipelined<2>(
+      nk,
+      [&](int d, int k) {
+        const int c = c0 + wave + k * NW;
+        load_chunk(r[d], p, c < c1 ? c : c1 - 1);
+      },
+      [&](int d, int k) {
+        if (c0 + wave + k * NW >= c1) zero_b(r[d]);
+        compute_chunk<BF, MT, T>(acc, r[d].a, MT, [&](int t, int i) { return b_from_regs(r[d], t, i); });
+      });
+}
+
+// LDS partial tiles [wave][pair][i][lane]; returns after a workgroup barrier
+template <int MT, int T>
+__device__ __forceinline__ void ks_stash(const v4f (&acc)[MT][T], float* red) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[((wave * MT * T + mt * T + t) * 4 + i) * 64 + lane] = acc[mt][t][i];
+  __syncthreads();
+}
+
+template <int NW>
+__device__ __forceinline__ float ks_sum(const float* red, int PT, int p, int i, int ln) {
+  float s = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) s += red[((w * PT + p) * 4 + i) * 64 + ln];
+  return s;
+}
+
+// ---------------------------------------------------------------- M-split main loop
+
+constexpr int kMsWaves = 4;
+
+template <int BF, int MT, int T>
+struct MsGeom {
+  static constexpr int MTW = (MT + kMsWaves - 1) / kMsWaves;     // m-tiles per wave (max)
+  static constexpr int UPT = Fmt<BF>::kUnits;                    // 1 KB global units per tile-chunk
+  static constexpr int NU = T * UPT;
+  static constexpr int KU = (NU + kMsWaves - 1) / kMsWaves;       // units per wave
+  static constexpr int D = Fmt<BF>::kA16 ? 2 : 4;                // register prefetch depth (chunks)
+  static constexpr int SLOT = T * Fmt<BF>::kLds;                 // LDS bytes per ring slot
+};
+
+template <int BF, int MT, int T>
+struct MsBuf {
+  AFrag<BF> a[MsGeom<BF, MT, T>::MTW];
+  v4i bu[MsGeom<BF, MT, T>::KU];
+  uint32_t sb[MsGeom<BF, MT, T>::KU];
+};
+
+// All loads unconditional: a unit index past the tile set is clamped to the
+// last unit (duplicate load and identical LDS write) and a padding m-tile
+// (wave + 4 j >= MT) reloads the wave's first m-tile (an L1 hit); its
+// accumulators are discarded by the caller.
+template <int BF, int MT, int T>
+__device__ __forceinline__ void ms_load(MsBuf<BF, MT, T>& b, const LanePtrs& p, int c) {
+  using G = MsGeom<BF, MT, T>;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+  for (int k = 0; k < G::KU; ++k) {
+    const int u = min(wave + kMsWaves * k, G::NU - 1);
+    const int t = u / G::UPT, h = u % G::UPT;
+    b.bu[k] = ld_nt((const v4i*)(p.w + t * p.w_tile + (size_t)c * Fmt<BF>::kGlobal + h * 1024));
+    if constexpr (BF == kB_FP4_F16)
+      b.sb[k] = *(const uint16_t*)(p.wb + t * p.wb_tile + (size_t)(c >> 3) * 1024 + 2 * (c & 7));
+  }
+#pragma unroll
+  for (int j = 0; j < G::MTW; ++j) {
+    const int mt = wave + kMsWaves * j < MT ? wave + kMsWaves * j : wave;
+    load_a<BF>(b.a[j], p.a + mt * p.a_mt_stride + (size_t)c * p.a_chunk);
+  }
+}
+
+// convert this wave's weight units to operand format and write them to the slot
+// (slot layout: FP8 [t][h][lane][16 B]; others [t][i][lane][16 B])
+template <int BF, int MT, int T>
+__device__ __forceinline__ void ms_stage(const MsBuf<BF, MT, T>& b, v4i* slot) {
+  using G = MsGeom<BF, MT, T>;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+#pragma unroll
+  for (int k = 0; k < G::KU; ++k) {
+    {
+      const int u = min(wave + kMsWaves * k, G::NU - 1);
+      const int t = u / G::UPT, h = u % G::UPT;
+      if constexpr (BF == kB_FP8 || BF == kB_BF16) {
+        slot[(t * G::UPT + h) * 64 + lane] = b.bu[k];
+      } else if constexpr (BF == kB_FP8_F16) {
+        const v8h lo = e4m3x8_to_f16((uint32_t)b.bu[k][0], (uint32_t)b.bu[k][1]);
+        const v8h hi = e4m3x8_to_f16((uint32_t)b.bu[k][2], (uint32_t)b.bu[k][3]);
+        slot[(t * 4 + 2 * h) * 64 + lane] = __builtin_bit_cast(v4i, lo);
+        slot[(t * 4 + 2 * h + 1) * 64 + lane] = __builtin_bit_cast(v4i, hi);
+      } else {
+        v2h s0, s1;
+        e4m3x2_scales(b.sb[k], s0, s1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          slot[(t * 4 + i) * 64 + lane] = __builtin_bit_cast(v4i, e2m1x8_to_f16((uint32_t)b.bu[k][i], i < 2 ? s0 : s1));
+      }
+    }
+  }
+}
+
+template <int BF, int MT, int T>
+__device__ __forceinline__ void ms_mainloop(const LanePtrs& p, int c0, int c1, v4i* lds,
+                                            v4f (&acc)[MsGeom<BF, MT, T>::MTW][T]) {
+  using G = MsGeom<BF, MT, T>;
+  const int lane = threadIdx.x & 63;
+  MsBuf<BF, MT, T> buf[G::D];
+  pipelined<G::D>(
+      c1 - c0, [&](int d, int k) { ms_load(buf[d], p, c0 + k); },
+      [&](int d, int k) {
+        v4i* slot = lds + (k & 1) * (G::SLOT / 16);
+        ms_stage(buf[d], slot);
+        __syncthreads();
+        compute_chunk<BF, G::MTW, T>(acc, buf[d].a, G::MTW, [&](int t, int i) {
+          if constexpr (BF == kB_FP8) {
+            return cat(slot[(t * 2) * 64 + lane], slot[(t * 2 + 1) * 64 + lane]);
+          } else if constexpr (BF == kB_BF16) {
+            return __builtin_bit_cast(v8bf, slot[(t * 4 + i) * 64 + lane]);
+          } else {
+            return __builtin_bit_cast(v8h, slot[(t * 4 + i) * 64 + lane]);
+          }
+        });
+      });
+}
+
+}  // namespace ocq

@@ -1,0 +1,179 @@
+// Device-side building blocks shared by the ocq kernels (gfx950 / CDNA4).
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "ocq_internal.h"
+
+namespace ocq {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------- arguments
+
+// Activation operands (x, h) are stored in MFMA fragment order: blocks of 16
+// rows x 128 inputs, block (mt, c) at (mt * C + c) * BLK bytes, and inside a
+// block [unit][lane][16 B] where lane l = 16 g + r carries row r and inputs
+// 128 c + 32 g .. +32 (the same k-ranges as the weight fragments).  E4M3 codes:
+// BLK = 2048, 2 units (code j in unit j / 16); 16-bit values (fp16 / bf16):
+// BLK = 4096, 4 units (value j in unit j / 8).  One 16 B load per lane then
+// reads 1 KB of contiguous memory.
+__device__ __forceinline__ size_t frag_off8(int m, int k, int C) {   // byte offset of code (m, k)
+  const int mt = m >> 4, r = m & 15, c = k >> 7, g = (k >> 5) & 3, j = k & 31;
+  return ((size_t)(mt * C + c) * 2 + (j >> 4)) * 1024 + (16 * g + r) * 16 + (j & 15);
+}
+__device__ __forceinline__ size_t frag_off16(int m, int k, int C) {  // element offset of value (m, k)
+  const int mt = m >> 4, r = m & 15, c = k >> 7, g = (k >> 5) & 3, j = k & 31;
+  return (((size_t)(mt * C + c) * 4 + (j >> 3)) * 64 + (16 * g + r)) * 8 + (j & 7);
+}
+
+struct GateUpArgs {
+  const uint8_t* xq;        // E4M3 codes of x, fragment order, Mpad rows
+  const float* sx;          // [Mpad]
+  const uint8_t* wcodes;    // interleaved gate/up fragments
+  const float* wscales;     // FP8: [2][I] per-row scales
+  const uint8_t* wbscales;  // NVFP4: block-scale groups
+  const float* tscales;     // NVFP4: blob header s_gate, s_up
+  float* h32;               // [Mpad][p32] (FP8 / NVFP4 down modes)
+  uint16_t* hb;             // bf16(h), fragment order (BF16-down mode)
+  uint16_t* tap_hb;         // optional plain [M][I] copy of bf16(h) (BF16-down mode)
+  float* amax_part;         // [ngroups][Mpad] max |h| of each row over each workgroup's columns
+  int H, I, M, n_mb, Mpad;
+  int p32;                  // h32 row pitch (floats)
+};
+
+struct DownArgs {
+  const void* A;            // hq codes (FP8 / NVFP4) or bf16(h) (BF16), fragment order
+  const float* sh;          // [Mpad] (FP8 / NVFP4)
+  const uint8_t* wcodes;
+  const float* wscales;     // FP8: [H]
+  const uint8_t* wbscales;  // NVFP4 block-scale groups
+  const float* tscale;      // NVFP4: blob header s_down
+  float* part;              // [nsplit][Mpad][pp]
+  uint32_t* counters;       // [n_mb][ngroups]
+  uint16_t* y;              // [M][H]
+  int H, I, M, Mpad, n_mb, ngroups, cps, nsplit;
+  int pp;                   // partial row pitch (floats)
+};
+
+hipError_t launch_gateup(const Plan& p, const GateUpArgs& g, hipStream_t st);
+hipError_t launch_down(const Plan& p, const DownArgs& d, hipStream_t st);
+
+// ---------------------------------------------------------------- scalar codecs
+
+// E4M3 (OCP FN) code of an fp32 value: nearest, ties to even, saturating at 448.
+__device__ __forceinline__ uint32_t enc_e4m3(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t ua = u & 0x7FFFFFFFu;
+  const float a = __uint_as_float(ua);
+  uint32_t c;
+  if (a >= 448.0f) {
+    c = 0x7Eu;
+  } else if (a < 0.015625f) {                       // subnormal grid 2^-9 (code 8 = 2^-6)
+    c = (uint32_t)__builtin_rintf(a * 512.0f);
+  } else {
+    const uint32_t e = (ua >> 23) - 120u;           // rebias 127 -> 7
+    const uint32_t m = ua & 0x7FFFFFu;
+    const uint32_t q = (m + 0x7FFFFu + ((m >> 20) & 1u)) >> 20;
+    c = (e << 3) + q;                               // mantissa carry bumps the exponent
+  }
+  return sign | c;
+}
+
+__device__ __forceinline__ uint32_t bf16_bits(float v) {   // round to nearest even (finite v)
+  const uint32_t u = __float_as_uint(v);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Eight E4M3 codes (two dwords, byte order = element order) -> eight fp16.
+// v_cvt_scalef32_pk_f16_fp8 applies only the power-of-two part of its scale,
+// so a scale of 1.0 makes the conversion exact (every E4M3 value is an fp16).
+__device__ __forceinline__ v8h e4m3x8_to_f16(uint32_t lo, uint32_t hi) {
+  const v2h a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false);
+  const v2h b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true);
+  const v2h c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false);
+  const v2h d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true);
+  return v8h{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// Eight E2M1 codes (one dword, low nibble first) times an E4M3 block scale
+// -> eight fp16, exact: the conversion (scale 1.0) is exact, and E2M1 x E4M3
+// products have at most 6 significant bits and lie in [2^-10, 2688].
+__device__ __forceinline__ v8h e2m1x8_to_f16(uint32_t d, v2h sb) {
+  const v2h a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 0) * sb;
+  const v2h b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 1) * sb;
+  const v2h c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 2) * sb;
+  const v2h e = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 3) * sb;
+  return v8h{a[0], a[1], b[0], b[1], c[0], c[1], e[0], e[1]};
+}
+
+// two E4M3 block scales (bytes of a 16-bit value) -> broadcast fp16 pairs
+__device__ __forceinline__ void e4m3x2_scales(uint32_t two, v2h& s0, v2h& s1) {
+  const v2h sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(two, 1.0f, false);
+  s0 = v2h{sc[0], sc[0]};
+  s1 = v2h{sc[1], sc[1]};
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+
+template <class T>
+__device__ __forceinline__ T ld_nt(const T* p) { return __builtin_nontemporal_load(p); }
+
+__device__ __forceinline__ v8i cat(v4i lo, v4i hi) {
+  return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// ---------------------------------------------------------------- weight operand formats
+//
+// Weight tiles are 16 output rows; a chunk is 128 inputs.  Per format: bytes of
+// one tile-chunk in the blob, and the matrix-core instruction used.
+enum BFmt {
+  kB_FP8 = 0,       // E4M3 codes, MFMA 16x16x128 f8f6f4 (one per chunk)
+  kB_FP8_F16 = 1,   // E4M3 codes converted to fp16, MFMA 16x16x32 f16 (four per chunk)
+  kB_BF16 = 2,      // bf16, MFMA 16x16x32 bf16 (four per chunk)
+  kB_FP4_F16 = 3    // NVFP4 codes x block scale converted to fp16, MFMA 16x16x32 f16
+};
+
+template <int BF> struct Fmt;
+// kA16: the activation operand is bf16 (BF16 down projection) rather than
+// E4M3 codes (converted to fp16 in registers for the f16 formats).
+template <> struct Fmt<kB_FP8> { static constexpr int kGlobal = 2048, kUnits = 2, kLds = 2048; static constexpr bool kA16 = false; };
+template <> struct Fmt<kB_FP8_F16> { static constexpr int kGlobal = 2048, kUnits = 2, kLds = 4096; static constexpr bool kA16 = false; };
+template <> struct Fmt<kB_BF16> { static constexpr int kGlobal = 4096, kUnits = 4, kLds = 4096; static constexpr bool kA16 = true; };
+template <> struct Fmt<kB_FP4_F16> { static constexpr int kGlobal = 1024, kUnits = 1, kLds = 4096; static constexpr bool kA16 = false; };
+
+template <int BF>
+struct AGeom {
+  static constexpr int kUnits = Fmt<BF>::kA16 ? 4 : 2;   // 16 B units per lane per chunk
+  static constexpr int kBlk = kUnits * 1024;             // bytes per (m-tile, chunk) block
+};
+
+// One chunk's activation fragment of one m-tile for one lane
+template <int BF>
+struct AFrag {
+  v4i q[AGeom<BF>::kUnits];
+};
+
+// p points at this lane's 16 B of unit 0 of the (m-tile, chunk) block
+template <int BF>
+__device__ __forceinline__ void load_a(AFrag<BF>& f, const uint8_t* p) {
+#pragma unroll
+  for (int u = 0; u < AGeom<BF>::kUnits; ++u) f.q[u] = *(const v4i*)(p + u * 1024);
+}
+
+}  // namespace ocq

@@ -28,6 +28,8 @@ struct FwdArgs {
   uint16_t* y;
   uint8_t* ws;
   void* stream;
+  void* const* stage_events;  // 5 hipEvent_t or NULL
+  ocq_taps taps;              // each pointer nullable
 };
 
 // enqueue the kernels of one forward call (kernels.hip); returns 0 or a hipError_t value

@@ -6,9 +6,10 @@
 // output rows and "chunks" of 128 input columns.  Lane l = 16 g + r (g = 0..3,
 // r = 0..15) of a wave holds row r of the tile and the 32 consecutive inputs
 // k = 128 c + 32 g + j, j = 0..31, of chunk c.  Activations are read with the
-// same per-lane k-ranges straight from their row-major buffers, so the two
-// operands agree on which k each lane/byte carries and the hardware sums the
-// same products as the plain definition.
+// same per-lane k-ranges from fragment-ordered activation buffers (written so
+// by the quantization kernels), so the two operands agree on which k each
+// lane/byte carries and the hardware sums the same products as the plain
+// definition.
 //
 //   FP8 chunk  (2048 B): [half h = 0,1][lane][16 B]   byte j of lane l at
 //                        h = j / 16, offset (h * 64 + l) * 16 + j % 16.
@@ -117,7 +118,11 @@ struct Plan {
   int ngroups2;    // (hidden / 16) / T2
   int nsplit2;     // split-K factor
   int chunks_per_split2;
-  // workspace offsets
+  // row pitches (elements) of the row-major fp32 buffers, padded so that rows
+  // with power-of-two lengths do not all start in the same L2 channel
+  int p32;   // h32
+  int pp;    // split-K partials
+  // workspace offsets (xq, hq, hb are fragment-ordered operand buffers of Mpad rows)
   size_t off_xq, off_sx, off_amax, off_h32, off_hq, off_hb, off_sh, off_part, off_cnt, total;
 };
 
@@ -135,38 +140,38 @@ inline Plan make_plan(int M, int hidden, int inter, int prec) {
   int rows_per_block = 16 * p.MT;
   p.n_mblocks = (M + rows_per_block - 1) / rows_per_block;
   p.Mpad = p.n_mblocks * rows_per_block;
-  // gate/up: tiles of 8 gate + 8 up columns
+  // gate/up: tiles of 8 gate + 8 up columns; 3 tiles per workgroup when that
+  // still gives >= 192 workgroups (one per CU at the configured sizes)
   int nt1 = inter / 8;
   p.T1 = 1;
   for (int t : {3, 2}) {
-    if (nt1 % t == 0 && p.MT * t <= 39 && nt1 / t >= 192) { p.T1 = t; break; }
+    if (nt1 % t == 0 && nt1 / t >= 192) { p.T1 = t; break; }
   }
   p.ngroups1 = nt1 / p.T1;
-  // down: tiles of 16 output columns, split-K over inter
+  // down: groups of 2 output tiles (32 columns), split over inter so that
+  // m-blocks x groups x splits is about 256 workgroups, >= 4 chunks per split
   int nt2 = hidden / 16;
   int c2 = inter / kChunk;
-  p.T2 = 1;
-  for (int t : {8, 4, 3, 2}) {
-    if (nt2 % t == 0 && p.MT * t <= 39 && nt2 / t >= 16) { p.T2 = t; break; }
-  }
+  p.T2 = nt2 % 2 == 0 ? 2 : 1;
   p.ngroups2 = nt2 / p.T2;
-  int target = 256 / p.n_mblocks;  // workgroups wanted per m-block
+  int target = 256 / p.n_mblocks;
   int ns = target / p.ngroups2;
   if (ns < 1) ns = 1;
-  if (ns > c2 / 4) ns = c2 / 4 > 0 ? c2 / 4 : 1;   // keep >= 4 chunks (one per wave) per split
+  if (ns > c2 / 4) ns = c2 / 4 > 0 ? c2 / 4 : 1;
   p.chunks_per_split2 = (c2 + ns - 1) / ns;
   p.nsplit2 = (c2 + p.chunks_per_split2 - 1) / p.chunks_per_split2;
   // workspace
-  size_t Mp = p.Mpad, H = hidden, I = inter;
+  size_t Mp = p.Mpad;
   size_t o = 0;
-  p.off_xq = o;   o = align_up(o + Mp * H);
+  p.p32 = inter + 32; p.pp = hidden + 32;
+  p.off_xq = o;   o = align_up(o + Mp * hidden);
   p.off_sx = o;   o = align_up(o + Mp * 4);
-  p.off_amax = o; o = align_up(o + Mp * 4);
-  p.off_h32 = o;  o = align_up(o + (prec == kFP8DownBF16 ? 0 : Mp * I * 4));
-  p.off_hq = o;   o = align_up(o + (prec == kFP8DownBF16 ? 0 : Mp * I));
-  p.off_hb = o;   o = align_up(o + (prec == kFP8DownBF16 ? Mp * I * 2 : 0));
+  p.off_amax = o; o = align_up(o + (size_t)p.ngroups1 * Mp * 4);   // per-workgroup row maxima of |h|
+  p.off_h32 = o;  o = align_up(o + (prec == kFP8DownBF16 ? 0 : Mp * p.p32 * 4));
+  p.off_hq = o;   o = align_up(o + (prec == kFP8DownBF16 ? 0 : Mp * inter));
+  p.off_hb = o;   o = align_up(o + (prec == kFP8DownBF16 ? Mp * inter * 2 : 0));
   p.off_sh = o;   o = align_up(o + Mp * 4);
-  p.off_part = o; o = align_up(o + (p.nsplit2 > 1 ? (size_t)p.nsplit2 * Mp * H * 4 : 0));
+  p.off_part = o; o = align_up(o + (p.nsplit2 > 1 ? (size_t)p.nsplit2 * Mp * p.pp * 4 : 0));
   p.off_cnt = o;  o = align_up(o + (size_t)p.n_mblocks * p.ngroups2 * 4);
   p.total = o;
   return p;

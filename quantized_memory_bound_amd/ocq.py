@@ -26,7 +26,7 @@ ERR_BAD_BLOB = -5
 
 EXPORTS = ("ocq_version", "ocq_packed_bytes", "ocq_pack_weights_host", "ocq_pack_weights",
            "ocq_unpack_weights_host", "ocq_workspace_bytes", "ocq_mlp_forward", "ocq_check_blob",
-           "ocq_last_error")
+           "ocq_set_stage_events", "ocq_last_error")
 
 
 class OcqError(RuntimeError):
@@ -65,6 +65,7 @@ def lib():
     L.ocq_mlp_forward.argtypes = [vp, sz, vp, i, i, i, i, vp, vp, sz, ctypes.POINTER(Taps), vp]
     L.ocq_mlp_forward.restype = i
     L.ocq_check_blob.argtypes, L.ocq_check_blob.restype = [vp, sz, i, i, i, vp], i
+    L.ocq_set_stage_events.argtypes, L.ocq_set_stage_events.restype = [ctypes.POINTER(vp), i], i
     _lib = L
     return L
 
@@ -145,6 +146,15 @@ def pack_weights(w_gate, w_up, w_down, prec_mode, device="cuda", stream=None):
     _check(lib().ocq_pack_weights(wg.ctypes.data, wu.ctypes.data, wd.ctypes.data, hidden, inter, prec_mode,
                                   blob.data_ptr(), n, _stream_handle(stream)))
     return blob
+
+
+def set_stage_events(events):
+    """events: None (disable) or a list of 5 hipEvent_t handles (int or None)."""
+    if events is None:
+        _check(lib().ocq_set_stage_events(None, 0))
+        return
+    arr = (ctypes.c_void_p * 5)(*[e if e else None for e in events])
+    _check(lib().ocq_set_stage_events(arr, 5))
 
 
 def check_blob(blob, hidden, inter, prec_mode, stream=None):

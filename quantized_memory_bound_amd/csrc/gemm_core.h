@@ -178,15 +178,16 @@ __device__ __forceinline__ void zero_b(ChunkRegs<BF, MT, T>& r) {
   }
 }
 
-// Every wave runs the same number of iterations (two chunks in flight); a
-// chunk index past the range is clamped to the last chunk for the loads and
-// its weight operand is zeroed, so no load depends on the wave.
-template <int BF, int MT, int T, int NW>
+// Every wave runs the same number of iterations, rounded up to a multiple of
+// the prefetch depth D (D chunks in flight); a chunk index past the range is
+// clamped to the last chunk for the loads and its weight operand is zeroed,
+// so no load depends on the wave or the iteration.
+template <int BF, int MT, int T, int NW, int D>
 __device__ __forceinline__ void ks_mainloop(const LanePtrs& p, int c0, int c1, v4f (&acc)[MT][T]) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int nk = (c1 - c0 + NW - 1) / NW;
-  ChunkRegs<BF, MT, T> r[2];
-  pipelined<2>(
+  const int nk = ((c1 - c0 + NW - 1) / NW + D - 1) / D * D;
+  ChunkRegs<BF, MT, T> r[D];
+  pipelined<D>(
       nk,
       [&](int d, int k) {
         const int c = c0 + wave + k * NW;

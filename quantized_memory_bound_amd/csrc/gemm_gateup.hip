@@ -103,7 +103,7 @@ __global__ __launch_bounds__(64 * kKsWaves) void ks_gateup(GateUpArgs g) {
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int t = 0; t < T; ++t) acc[mt][t] = v4f{0.f, 0.f, 0.f, 0.f};
-  ks_mainloop<BF, MT, T, kKsWaves>(lp, 0, C, acc);
+  ks_mainloop<BF, MT, T, kKsWaves, 2>(lp, 0, C, acc);
   ks_stash<MT, T>(acc, red);
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;

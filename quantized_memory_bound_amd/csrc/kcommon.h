@@ -57,11 +57,8 @@ struct DownArgs {
   const float* wscales;     // FP8: [H]
   const uint8_t* wbscales;  // NVFP4 block-scale groups
   const float* tscale;      // NVFP4: blob header s_down
-  float* part;              // [nsplit][Mpad][pp]
-  uint32_t* counters;       // [n_mb][ngroups]
   uint16_t* y;              // [M][H]
-  int H, I, M, Mpad, n_mb, ngroups, cps, nsplit;
-  int pp;                   // partial row pitch (floats)
+  int H, I, M, n_mb, ngroups;
 };
 
 hipError_t launch_gateup(const Plan& p, const GateUpArgs& g, hipStream_t st);

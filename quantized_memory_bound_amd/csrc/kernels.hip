@@ -5,7 +5,7 @@
 //
 // One forward call = four kernels on the caller's stream:
 //   k_xquant   per-token E4M3 quantization of x (scale amax/448), zero rows
-//              up to whole m-blocks; also clears the split-K arrival counters.
+//              up to whole m-blocks.
 //   gate/up    G = xq Wg^T, U = xq Wu^T (exact products, fp32 accumulation),
 //              h = SiLU(G sx sw_g) * (U sx sw_u), per-workgroup row maxima of
 //              |h| (or bf16(h) for a BF16 down projection).
@@ -34,11 +34,9 @@ constexpr int kThreads = 64 * kWaves;
 // [M][H] codes and [M] scales.
 __global__ __launch_bounds__(kThreads) void k_xquant(const uint16_t* __restrict__ x, int M, int H, int Mpad,
                                                      uint8_t* __restrict__ xq, float* __restrict__ sx,
-                                                     uint8_t* __restrict__ tap_q, float* __restrict__ tap_s,
-                                                     uint32_t* __restrict__ counters, int ncnt) {
+                                                     uint8_t* __restrict__ tap_q, float* __restrict__ tap_s) {
   __shared__ float s_max[kWaves];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  for (int i = blockIdx.x * kThreads + threadIdx.x; i < ncnt; i += gridDim.x * kThreads) counters[i] = 0u;
   const int m = blockIdx.x;
   const int C = H / 128;
   if (m >= M) {                                     // padding row: zero codes, zero scale
@@ -106,6 +104,8 @@ __global__ __launch_bounds__(kThreads) void k_xquant(const uint16_t* __restrict_
 
 // amax_part[g][m] holds the |h| maximum of row m over the columns of gate/up
 // workgroup g; every block first reduces the row's ngroups partial maxima.
+// Rows M..Mpad-1 (padding, possibly beyond the gate/up m-blocks) get zero
+// codes and scale 0 without reading h.
 // Codes go to the fragment-ordered operand buffer of the down projection (4
 // consecutive inputs = 4 contiguous bytes there).  tap_q / tap_s (nullable)
 // receive the plain [M][I] codes and [M] scales.
@@ -117,6 +117,12 @@ __global__ __launch_bounds__(kThreads) void k_requant(const float* __restrict__ 
   __shared__ float s_max[kWaves];
   const int m = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (m >= M) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) sh[m] = 0.0f;
+    const int k = (blockIdx.x * kThreads + threadIdx.x) * 4;
+    if (k < I) *(uint32_t*)(hq + frag_off8(m, k, I / 128)) = 0u;
+    return;
+  }
   float a = 0.0f;
   for (int g = threadIdx.x; g < ngroups; g += kThreads) a = fmaxf(a, amax_part[(size_t)g * Mpad + m]);
   a = wave_max(a);
@@ -126,7 +132,7 @@ __global__ __launch_bounds__(kThreads) void k_requant(const float* __restrict__ 
   const float s = a / 448.0f;
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     sh[m] = s;
-    if (tap_s && m < M) tap_s[m] = s;
+    if (tap_s) tap_s[m] = s;
   }
   const int k = (blockIdx.x * kThreads + threadIdx.x) * 4;
   if (k >= I) return;
@@ -137,7 +143,7 @@ __global__ __launch_bounds__(kThreads) void k_requant(const float* __restrict__ 
     for (int j = 0; j < 4; ++j) out |= enc_e4m3(v[j] / s) << (8 * j);
   }
   *(uint32_t*)(hq + frag_off8(m, k, I / 128)) = out;
-  if (tap_q && m < M) *(uint32_t*)(tap_q + (size_t)m * I + k) = out;
+  if (tap_q) *(uint32_t*)(tap_q + (size_t)m * I + k) = out;
 }
 
 }  // namespace
@@ -159,14 +165,11 @@ int launch_forward(const Plan& p, const FwdArgs& a) {
   uint8_t* hq = ws + p.off_hq;
   uint16_t* hb = (uint16_t*)(ws + p.off_hb);
   float* sh = (float*)(ws + p.off_sh);
-  float* part = (float*)(ws + p.off_part);
-  uint32_t* cnt = (uint32_t*)(ws + p.off_cnt);
-  const int ncnt = p.n_mblocks * p.ngroups2;
 
   stage(a, 0);
   const bool bf16_down = p.prec == kFP8DownBF16;
   hipLaunchKernelGGL(k_xquant, dim3(p.Mpad), dim3(kThreads), 0, st, a.x, p.M, p.hidden, p.Mpad, xq, sx,
-                     (uint8_t*)a.taps.x_codes, (float*)a.taps.x_scales, cnt, ncnt);
+                     (uint8_t*)a.taps.x_codes, (float*)a.taps.x_scales);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return (int)e;
 
@@ -201,10 +204,8 @@ int launch_forward(const Plan& p, const FwdArgs& a) {
   d.wscales = (const float*)(a.blob + L.off_dn_scales);
   d.wbscales = a.blob + L.off_dn_bscales;
   d.tscale = (const float*)(a.blob + offsetof(BlobHeader, s_down));
-  d.part = part; d.counters = cnt; d.y = a.y;
-  d.H = p.hidden; d.I = p.inter; d.M = p.M; d.Mpad = p.Mpad; d.n_mb = p.n_mblocks;
-  d.ngroups = p.ngroups2; d.cps = p.chunks_per_split2; d.nsplit = p.nsplit2;
-  d.pp = p.pp;
+  d.y = a.y;
+  d.H = p.hidden; d.I = p.inter; d.M = p.M; d.n_mb = p.n_mb2; d.ngroups = p.ngroups2;
   e = launch_down(p, d, st);
   stage(a, 4);
   return (int)e;

@@ -29,6 +29,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <initializer_list>
+
 namespace ocq {
 
 constexpr uint32_t kBlobVersion = 1;
@@ -101,29 +103,22 @@ inline BlobLayout blob_layout(int hidden, int inter, int prec) {
 // Execution plan and workspace
 // ---------------------------------------------------------------------------
 
-// m-tiles (16 rows each) per workgroup pass; instantiated template values
+// m-tiles (16 rows each) per gate/up workgroup; instantiated template values
 constexpr int kMTChoices[] = {1, 2, 4, 7, 13};
 constexpr int kMTMax = 13;
 
 struct Plan {
   int M, hidden, inter, prec;
-  int MT;          // m-tiles per m-block
-  int n_mblocks;   // m-blocks
-  int Mpad;        // rows of every activation buffer (n_mblocks * 16 * MT)
-  // gate/up kernel
-  int T1;          // interleaved tiles per workgroup
-  int ngroups1;    // (inter / 8) / T1
-  // down kernel
-  int T2;          // down tiles per workgroup
-  int ngroups2;    // (hidden / 16) / T2
-  int nsplit2;     // split-K factor
-  int chunks_per_split2;
-  // row pitches (elements) of the row-major fp32 buffers, padded so that rows
-  // with power-of-two lengths do not all start in the same L2 channel
-  int p32;   // h32
-  int pp;    // split-K partials
+  int Mpad;        // rows of every activation buffer (covers both projections' m-blocks)
+  // gate/up kernel: n_mblocks m-blocks of MT m-tiles x ngroups1 groups of T1 tiles
+  int MT, n_mblocks, T1, ngroups1;
+  // down kernel: n_mb2 m-blocks of MT2 m-tiles x ngroups2 groups of T2 tiles,
+  // every workgroup over the whole input range
+  int MT2, n_mb2, T2, ngroups2;
+  int p32;         // h32 row pitch (floats), padded so that rows of power-of-two
+                   // length do not all start in the same L2 channel
   // workspace offsets (xq, hq, hb are fragment-ordered operand buffers of Mpad rows)
-  size_t off_xq, off_sx, off_amax, off_h32, off_hq, off_hb, off_sh, off_part, off_cnt, total;
+  size_t off_xq, off_sx, off_amax, off_h32, off_hq, off_hb, off_sh, total;
 };
 
 inline int pick_mt(int M) {
@@ -133,13 +128,42 @@ inline int pick_mt(int M) {
   return kMTMax;
 }
 
+// Down projection blocking.  Each workgroup reads its rows' activations and
+// its tiles' weights over the whole input range once, so the bytes it pulls
+// through its CU are inter * (rows * act_bytes + cols * w_bytes); the choice
+// minimises that per-CU volume (times the number of workgroup waves over the
+// 256 CUs) plus the matrix-core time of the padded rows.
+inline void pick_down(Plan& p) {
+  const int mtiles = (p.M + 15) / 16, ntiles = p.hidden / 16;
+  const double ea = p.prec == kFP8DownBF16 ? 2.0 : 1.0;
+  const double eb = p.prec == kFP8DownBF16 ? 2.0 : (p.prec == kFP4 ? 0.5 + 1.0 / 16 : 1.0);
+  const double mfma_rate = p.prec == kFP8 ? 2.0 : 1.0;   // fp8 matrix cores at twice the 16-bit rate
+  double best = 1e30;
+  for (int mt : {1, 2, 4}) {
+    for (int t : {1, 2, 4}) {
+      if (ntiles % t) continue;
+      const int nmb = (mtiles + mt - 1) / mt, ng = ntiles / t;
+      const double wgs = (double)nmb * ng;
+      const double waves = wgs <= 256 ? 1.0 : (double)((nmb * ng + 255) / 256);
+      const double l1 = (double)p.inter * 16.0 * (mt * ea + t * eb);           // bytes per workgroup
+      const double mm = (double)p.inter * 16.0 * 16.0 * mt * t / mfma_rate;   // 16-bit MACs per workgroup
+      // per CU: ~150 GB/s through L1; ~4 TMAC/s of 16-bit matrix work (us)
+      double cost = waves * (l1 / 150e3 + mm / 4e6);
+      if (wgs < 128) cost *= 128.0 / wgs;                                    // too few CUs streaming
+      if (cost < best * 0.999) {
+        best = cost;
+        p.MT2 = mt; p.T2 = t; p.n_mb2 = nmb; p.ngroups2 = ng;
+      }
+    }
+  }
+}
+
 inline Plan make_plan(int M, int hidden, int inter, int prec) {
   Plan p{};
   p.M = M; p.hidden = hidden; p.inter = inter; p.prec = prec;
   p.MT = pick_mt(M);
   int rows_per_block = 16 * p.MT;
   p.n_mblocks = (M + rows_per_block - 1) / rows_per_block;
-  p.Mpad = p.n_mblocks * rows_per_block;
   // gate/up: tiles of 8 gate + 8 up columns; 3 tiles per workgroup when that
   // still gives >= 192 workgroups (one per CU at the configured sizes)
   int nt1 = inter / 8;
@@ -148,22 +172,13 @@ inline Plan make_plan(int M, int hidden, int inter, int prec) {
     if (nt1 % t == 0 && nt1 / t >= 192) { p.T1 = t; break; }
   }
   p.ngroups1 = nt1 / p.T1;
-  // down: groups of 2 output tiles (32 columns), split over inter so that
-  // m-blocks x groups x splits is about 256 workgroups, >= 4 chunks per split
-  int nt2 = hidden / 16;
-  int c2 = inter / kChunk;
-  p.T2 = nt2 % 2 == 0 ? 2 : 1;
-  p.ngroups2 = nt2 / p.T2;
-  int target = 256 / p.n_mblocks;
-  int ns = target / p.ngroups2;
-  if (ns < 1) ns = 1;
-  if (ns > c2 / 4) ns = c2 / 4 > 0 ? c2 / 4 : 1;
-  p.chunks_per_split2 = (c2 + ns - 1) / ns;
-  p.nsplit2 = (c2 + p.chunks_per_split2 - 1) / p.chunks_per_split2;
+  pick_down(p);
+  const int rows1 = p.n_mblocks * 16 * p.MT, rows2 = p.n_mb2 * 16 * p.MT2;
+  p.Mpad = rows1 > rows2 ? rows1 : rows2;
   // workspace
   size_t Mp = p.Mpad;
   size_t o = 0;
-  p.p32 = inter + 32; p.pp = hidden + 32;
+  p.p32 = inter + 32;
   p.off_xq = o;   o = align_up(o + Mp * hidden);
   p.off_sx = o;   o = align_up(o + Mp * 4);
   p.off_amax = o; o = align_up(o + (size_t)p.ngroups1 * Mp * 4);   // per-workgroup row maxima of |h|
@@ -171,8 +186,6 @@ inline Plan make_plan(int M, int hidden, int inter, int prec) {
   p.off_hq = o;   o = align_up(o + (prec == kFP8DownBF16 ? 0 : Mp * inter));
   p.off_hb = o;   o = align_up(o + (prec == kFP8DownBF16 ? Mp * inter * 2 : 0));
   p.off_sh = o;   o = align_up(o + Mp * 4);
-  p.off_part = o; o = align_up(o + (p.nsplit2 > 1 ? (size_t)p.nsplit2 * Mp * p.pp * 4 : 0));
-  p.off_cnt = o;  o = align_up(o + (size_t)p.n_mblocks * p.ngroups2 * 4);
   p.total = o;
   return p;
 }

@@ -1,19 +1,17 @@
-// Matrix-core main loops of the skinny GEMMs (activations [rows x K] times
-// weight tiles [16 x K]), in two decompositions:
+// Matrix-core main loop of the skinny GEMMs (activations [rows x K] times
+// weight tiles [16 x K]).
 //
-//  K-split (few rows, M <= 64): the NW waves of a workgroup take the chunks of
-//    the input range round-robin; every wave loads its weight fragments
-//    straight from HBM into registers (non-temporal 16 B per lane, two chunks
-//    in flight) and keeps accumulators for all rows; the NW partial tiles are
-//    summed in LDS in wave order (deterministic).  With one or two chunks per
-//    wave, all of a workgroup's weight loads are in flight at once.
-//
-//  M-split (many rows): each wave owns a quarter of the m-tiles and runs over
-//    every chunk; the weight chunk is loaded once per workgroup (units spread
-//    over the waves), converted once to the matrix-core operand format and
-//    staged in a two-slot LDS ring; activations are prefetched per wave into
-//    a ring of register buffers.  One workgroup barrier per chunk; no
-//    cross-wave reduction.
+// A workgroup owns a block of m-tiles (16 rows each) x T weight tiles and the
+// whole input range.  Its waves form an MS x KS grid: wave (ms, ks) holds the
+// accumulators of m-tiles ms*MTW .. ms*MTW+MTW-1 and runs over the chunks
+// (128 inputs) ks, ks+KS, ks+2KS, ...  Every wave loads its own operand
+// fragments straight from memory into registers (16 B per lane per load,
+// weights non-temporal), D chunks ahead, and converts them to the matrix-core
+// format in registers; there is no LDS traffic and no barrier in the loop, so
+// the waves never wait for each other.  Each (row, input) and each (weight
+// row, input) pair is loaded by exactly one wave of the workgroup when MS = 1,
+// weights by MS waves otherwise.  After the loop the KS partial tiles of every
+// m-tile are summed in LDS in a fixed order (deterministic).
 //
 // Accumulator layout (MFMA 16x16 fp32): lane l holds rows 4 (l/16) + i,
 // i = 0..3, of column l % 16 of the tile.
@@ -33,24 +31,27 @@ struct ChunkRegs {
 
 // Global operand pointers of one lane.
 struct LanePtrs {
-  const uint8_t* a;    // activation block (m-tile 0, chunk 0) + lane * 16 (fragment order)
+  const uint8_t* a;    // activation block (first m-tile, chunk 0) + lane * 16 (fragment order)
   size_t a_mt_stride;  // bytes between m-tiles (all chunks of 16 rows)
   int a_chunk;         // bytes per (m-tile, chunk) block
+  int a_nvalid;        // m-tiles of this wave that exist; later ones reload the last
   const uint8_t* w;    // weight tile 0 of the group, + lane * 16
   size_t w_tile;       // bytes per weight tile
   const uint8_t* wb;   // NVFP4 block-scale groups of tile 0, + lane * 16
   size_t wb_tile;
 };
 
-// A: fragment-ordered activations of the workgroup's first m-tile, K inputs
+// A: fragment-ordered activations of the wave's first m-tile, K inputs;
+// nvalid: wave-uniform count of its m-tiles that exist
 template <int BF>
-__device__ __forceinline__ LanePtrs lane_ptrs(const void* A, int K, const uint8_t* W, size_t w_tile,
+__device__ __forceinline__ LanePtrs lane_ptrs(const void* A, int K, int nvalid, const uint8_t* W, size_t w_tile,
                                               const uint8_t* Wb, size_t wb_tile) {
   const int lane = threadIdx.x & 63;
   LanePtrs p;
   p.a = (const uint8_t*)A + lane * 16;
   p.a_chunk = AGeom<BF>::kBlk;
   p.a_mt_stride = (size_t)(K / kChunk) * AGeom<BF>::kBlk;
+  p.a_nvalid = nvalid;
   p.w = W + lane * 16;
   p.w_tile = w_tile;
   p.wb = Wb + lane * 16;
@@ -69,7 +70,8 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<BF, MT, T>& r, const LanePt
       r.sb[t] = *(const uint16_t*)(p.wb + t * p.wb_tile + (size_t)(c >> 3) * 1024 + 2 * (c & 7));
   }
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) load_a<BF>(r.a[mt], p.a + mt * p.a_mt_stride + (size_t)c * p.a_chunk);
+  for (int mt = 0; mt < MT; ++mt)
+    load_a<BF>(r.a[mt], p.a + (mt < p.a_nvalid ? mt : p.a_nvalid - 1) * p.a_mt_stride + (size_t)c * p.a_chunk);
 }
 
 // B operand of tile t, sub-step i, from raw registers
@@ -181,20 +183,20 @@ __device__ __forceinline__ void zero_b(ChunkRegs<BF, MT, T>& r) {
 // Every wave runs the same number of iterations, rounded up to a multiple of
 // the prefetch depth D (D chunks in flight); a chunk index past the range is
 // clamped to the last chunk for the loads and its weight operand is zeroed,
-// so no load depends on the wave or the iteration.
-template <int BF, int MT, int T, int NW, int D>
-__device__ __forceinline__ void ks_mainloop(const LanePtrs& p, int c0, int c1, v4f (&acc)[MT][T]) {
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int nk = ((c1 - c0 + NW - 1) / NW + D - 1) / D * D;
+// so no load depends on the wave or the iteration.  kidx: the wave's K-split
+// index (wave-uniform), KS: number of K-split waves.
+template <int BF, int MT, int T, int KS, int D>
+__device__ __forceinline__ void ks_mainloop(const LanePtrs& p, int kidx, int c0, int c1, v4f (&acc)[MT][T]) {
+  const int nk = ((c1 - c0 + KS - 1) / KS + D - 1) / D * D;
   ChunkRegs<BF, MT, T> r[D];
   pipelined<D>(
       nk,
       [&](int d, int k) {
-        const int c = c0 + wave + k * NW;
+        const int c = c0 + kidx + k * KS;
         load_chunk(r[d], p, c < c1 ? c : c1 - 1);
       },
       [&](int d, int k) {
-        if (c0 + wave + k * NW >= c1) zero_b(r[d]);
+        if (c0 + kidx + k * KS >= c1) zero_b(r[d]);
         compute_chunk<BF, MT, T>(acc, r[d].a, MT, [&](int t, int i) { return b_from_regs(r[d], t, i); });
       });
 }
@@ -212,109 +214,13 @@ __device__ __forceinline__ void ks_stash(const v4f (&acc)[MT][T], float* red) {
   __syncthreads();
 }
 
-template <int NW>
-__device__ __forceinline__ float ks_sum(const float* red, int PT, int p, int i, int ln) {
+// sum of element (pair p, i, lane ln) over the KS waves w0, w0 + ws, ...
+template <int KS>
+__device__ __forceinline__ float ks_sum(const float* red, int PT, int w0, int ws, int p, int i, int ln) {
   float s = 0.f;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) s += red[((w * PT + p) * 4 + i) * 64 + ln];
+  for (int k = 0; k < KS; ++k) s += red[(((w0 + k * ws) * PT + p) * 4 + i) * 64 + ln];
   return s;
-}
-
-// ---------------------------------------------------------------- M-split main loop
-
-constexpr int kMsWaves = 4;
-
-template <int BF, int MT, int T>
-struct MsGeom {
-  static constexpr int MTW = (MT + kMsWaves - 1) / kMsWaves;     // m-tiles per wave (max)
-  static constexpr int UPT = Fmt<BF>::kUnits;                    // 1 KB global units per tile-chunk
-  static constexpr int NU = T * UPT;
-  static constexpr int KU = (NU + kMsWaves - 1) / kMsWaves;       // units per wave
-  static constexpr int D = Fmt<BF>::kA16 ? 2 : 4;                // register prefetch depth (chunks)
-  static constexpr int SLOT = T * Fmt<BF>::kLds;                 // LDS bytes per ring slot
-};
-
-template <int BF, int MT, int T>
-struct MsBuf {
-  AFrag<BF> a[MsGeom<BF, MT, T>::MTW];
-  v4i bu[MsGeom<BF, MT, T>::KU];
-  uint32_t sb[MsGeom<BF, MT, T>::KU];
-};
-
-// All loads unconditional: a unit index past the tile set is clamped to the
-// last unit (duplicate load and identical LDS write) and a padding m-tile
-// (wave + 4 j >= MT) reloads the wave's first m-tile (an L1 hit); its
-// accumulators are discarded by the caller.
-template <int BF, int MT, int T>
-__device__ __forceinline__ void ms_load(MsBuf<BF, MT, T>& b, const LanePtrs& p, int c) {
-  using G = MsGeom<BF, MT, T>;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-#pragma unroll
-  for (int k = 0; k < G::KU; ++k) {
-    const int u = min(wave + kMsWaves * k, G::NU - 1);
-    const int t = u / G::UPT, h = u % G::UPT;
-    b.bu[k] = ld_nt((const v4i*)(p.w + t * p.w_tile + (size_t)c * Fmt<BF>::kGlobal + h * 1024));
-    if constexpr (BF == kB_FP4_F16)
-      b.sb[k] = *(const uint16_t*)(p.wb + t * p.wb_tile + (size_t)(c >> 3) * 1024 + 2 * (c & 7));
-  }
-#pragma unroll
-  for (int j = 0; j < G::MTW; ++j) {
-    const int mt = wave + kMsWaves * j < MT ? wave + kMsWaves * j : wave;
-    load_a<BF>(b.a[j], p.a + mt * p.a_mt_stride + (size_t)c * p.a_chunk);
-  }
-}
-
-// convert this wave's weight units to operand format and write them to the slot
-// (slot layout: FP8 [t][h][lane][16 B]; others [t][i][lane][16 B])
-template <int BF, int MT, int T>
-__device__ __forceinline__ void ms_stage(const MsBuf<BF, MT, T>& b, v4i* slot) {
-  using G = MsGeom<BF, MT, T>;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-#pragma unroll
-  for (int k = 0; k < G::KU; ++k) {
-    {
-      const int u = min(wave + kMsWaves * k, G::NU - 1);
-      const int t = u / G::UPT, h = u % G::UPT;
-      if constexpr (BF == kB_FP8 || BF == kB_BF16) {
-        slot[(t * G::UPT + h) * 64 + lane] = b.bu[k];
-      } else if constexpr (BF == kB_FP8_F16) {
-        const v8h lo = e4m3x8_to_f16((uint32_t)b.bu[k][0], (uint32_t)b.bu[k][1]);
-        const v8h hi = e4m3x8_to_f16((uint32_t)b.bu[k][2], (uint32_t)b.bu[k][3]);
-        slot[(t * 4 + 2 * h) * 64 + lane] = __builtin_bit_cast(v4i, lo);
-        slot[(t * 4 + 2 * h + 1) * 64 + lane] = __builtin_bit_cast(v4i, hi);
-      } else {
-        v2h s0, s1;
-        e4m3x2_scales(b.sb[k], s0, s1);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          slot[(t * 4 + i) * 64 + lane] = __builtin_bit_cast(v4i, e2m1x8_to_f16((uint32_t)b.bu[k][i], i < 2 ? s0 : s1));
-      }
-    }
-  }
-}
-
-template <int BF, int MT, int T>
-__device__ __forceinline__ void ms_mainloop(const LanePtrs& p, int c0, int c1, v4i* lds,
-                                            v4f (&acc)[MsGeom<BF, MT, T>::MTW][T]) {
-  using G = MsGeom<BF, MT, T>;
-  const int lane = threadIdx.x & 63;
-  MsBuf<BF, MT, T> buf[G::D];
-  pipelined<G::D>(
-      c1 - c0, [&](int d, int k) { ms_load(buf[d], p, c0 + k); },
-      [&](int d, int k) {
-        v4i* slot = lds + (k & 1) * (G::SLOT / 16);
-        ms_stage(buf[d], slot);
-        __syncthreads();
-        compute_chunk<BF, G::MTW, T>(acc, buf[d].a, G::MTW, [&](int t, int i) {
-          if constexpr (BF == kB_FP8) {
-            return cat(slot[(t * 2) * 64 + lane], slot[(t * 2 + 1) * 64 + lane]);
-          } else if constexpr (BF == kB_BF16) {
-            return __builtin_bit_cast(v8bf, slot[(t * 4 + i) * 64 + lane]);
-          } else {
-            return __builtin_bit_cast(v8h, slot[(t * 4 + i) * 64 + lane]);
-          }
-        });
-      });
 }
 
 }  // namespace ocq

@@ -51,14 +51,14 @@ __global__ __launch_bounds__(64 * NW) void ks_down(DownArgs d) {
   const int C = d.I / kChunk;
   const int row0 = mb * MT * 16;
   const size_t wt = (size_t)C * Fmt<BF>::kGlobal, bt = (size_t)((C + 7) / 8) * 1024;
-  const LanePtrs lp = lane_ptrs<BF>((const uint8_t*)d.A + (size_t)(row0 / 16) * C * AGeom<BF>::kBlk, d.I,
+  const LanePtrs lp = lane_ptrs<BF>((const uint8_t*)d.A + (size_t)(row0 / 16) * C * AGeom<BF>::kBlk, d.I, MT,
                                     d.wcodes + (size_t)ng * T * wt, wt, d.wbscales + (size_t)ng * T * bt, bt);
   v4f acc[MT][T];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int t = 0; t < T; ++t) acc[mt][t] = v4f{0.f, 0.f, 0.f, 0.f};
-  ks_mainloop<BF, MT, T, NW, D>(lp, 0, C, acc);
+  ks_mainloop<BF, MT, T, NW, D>(lp, __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), 0, C, acc);
   ks_stash<MT, T>(acc, red);
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, gq = lane >> 4, r = lane & 15;
@@ -72,7 +72,7 @@ __global__ __launch_bounds__(64 * NW) void ks_down(DownArgs d) {
     const float cs = col_scale<BF>(d, j);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float v = ks_sum<NW>(red, MT * T, q, i, lane);
+      const float v = ks_sum<NW>(red, MT * T, 0, 1, q, i, lane);
       if (mbase + i < d.M) d.y[(size_t)(mbase + i) * d.H + j] = (uint16_t)bf16_bits(v * rs[i] * cs);
     }
   }

@@ -3,7 +3,7 @@
 // G = xq Wg^T and U = xq Wu^T with exact products and fp32 accumulation
 // (operands converted in registers to fp16; MFMA 16x16x32 f16), then
 // h = SiLU(G sx sw_g) * (U sx sw_u) per element, with the row maximum of |h|
-// over the workgroup's columns written to amax_part[group][row] (reduced by
+// over the workgroup's columns written to amax_part[row][group] (reduced by
 // the requantization), or bf16(h) written for a BF16 down projection.
 // ("OCRia 推理栈：单卡 B200 提速近 10 倍", German page "Wie es funktioniert":
 // SiLU fused with the quantization, intermediates in registers; section
@@ -17,22 +17,22 @@ namespace ocq {
 namespace {
 
 // Epilogue operands of one lane, loaded together before they are used:
-// row scales sx of the lane's 4 rows of each of NMT m-tiles, and the gate / up
+// row scales sx of the lane's 4 rows of each of Q m-tiles, and the gate / up
 // column scales of its column in each of the T tiles.
-template <int BF, int NMT, int T>
+template <int Q, int T>
 struct EpiScales {
-  float xs[NMT][4];
+  float xs[Q][4];
   float cg[T], cu[T];
 };
 
-template <int BF, int NMT, int T, class MtOf>
-__device__ __forceinline__ void load_epi(EpiScales<BF, NMT, T>& e, const GateUpArgs& g, int row0, int tile0,
-                                         MtOf mt_of) {
+// q_of(j): row block (m-tile index from row0) of the wave's j-th epilogue m-tile
+template <int BF, int Q, int T, class QOf>
+__device__ __forceinline__ void load_epi(EpiScales<Q, T>& e, const GateUpArgs& g, int row0, int tile0, QOf q_of) {
   const int lane = threadIdx.x & 63, gq = lane >> 4, r = lane & 15;
 #pragma unroll
-  for (int j = 0; j < NMT; ++j)
+  for (int j = 0; j < Q; ++j)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) e.xs[j][i] = g.sx[row0 + mt_of(j) * 16 + 4 * gq + i];
+    for (int i = 0; i < 4; ++i) e.xs[j][i] = g.sx[row0 + q_of(j) * 16 + 4 * gq + i];
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     if constexpr (BF == kB_FP4_F16) {
@@ -47,122 +47,105 @@ __device__ __forceinline__ void load_epi(EpiScales<BF, NMT, T>& e, const GateUpA
 }
 
 // Epilogue of one 16x16 tile pair for one m-tile: v = accumulated tile (gate
-// in lanes r < 8, up in lanes r + 8), m_base = first row of the m-tile.
-template <bool BF16H>
+// in lanes r < 8, up in lanes r + 8 of each 16-lane row, rows 4 gq + i),
+// m_base = first row of the m-tile, col = column of h within the workgroup's
+// block (t * 8 + r % 8), n = column of h.  One DPP exchange gives gate lane
+// r the up values of rows 0, 1 and up lane r + 8 the gate values of rows 2, 3,
+// so every lane evaluates two of the four h values.  amax[e] accumulates |h|
+// of the lane's row e (rows 0, 1 in gate lanes, 2, 3 in up lanes).
+template <bool BF16H, int W>
 __device__ __forceinline__ void gateup_tile_epilogue(const GateUpArgs& g, const v4f& v, const float (&xs)[4],
-                                                     float cg, float cu, int m_base, int tile, float (&rowmax)[4]) {
+                                                     float cg, float cu, int m_base, int ng, int t,
+                                                     float (&amax)[2]) {
   const int lane = threadIdx.x & 63, gq = lane >> 4, r = lane & 15;
-  const int n = tile * 8 + (r & 7);
+  const bool lo = r < 8;
+  const int col = t * 8 + (r & 7), n = ng * W + col;
+  const float p0 = dpp<0x128>(lo ? v[2] : v[0]);
+  const float p1 = dpp<0x128>(lo ? v[3] : v[1]);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int e = 0; e < 2; ++e) {
+    const int i = lo ? e : 2 + e;
+    const float gv = lo ? v[e] : (e ? p1 : p0);
+    const float uv = lo ? (e ? p1 : p0) : v[2 + e];
+    const float xsi = xs[i];
+    const float hv = silu(gv * xsi * cg) * (uv * xsi * cu);
     const int m = m_base + 4 * gq + i;
-    const float up = __shfl_xor(v[i], 8);
-    float hv = 0.f;
-    if (r < 8) {
-      const float gv = v[i] * xs[i] * cg;
-      const float uv = up * xs[i] * cu;
-      hv = silu(gv) * uv;
-      if constexpr (BF16H) {
-        const uint16_t hb = (uint16_t)bf16_bits(hv);
-        g.hb[frag_off16(m, n, g.I / 128)] = hb;
-        if (g.tap_hb && m < g.M) g.tap_hb[(size_t)m * g.I + n] = hb;
-      } else {
-        g.h32[(size_t)m * g.p32 + n] = hv;
-      }
-    }
-    if constexpr (!BF16H) {
-      float am = fabsf(hv);
-      am = fmaxf(am, __shfl_xor(am, 1));
-      am = fmaxf(am, __shfl_xor(am, 2));
-      am = fmaxf(am, __shfl_xor(am, 4));
-      rowmax[i] = fmaxf(rowmax[i], am);
+    if constexpr (BF16H) {
+      const uint16_t hb = (uint16_t)bf16_bits(hv);
+      g.hb[frag_off16(m, n, g.I / 128)] = hb;
+      if (g.tap_hb && m < g.M) g.tap_hb[(size_t)m * g.I + n] = hb;
+    } else {
+      g.h32[((size_t)ng * g.Mpad + m) * W + col] = hv;
+      amax[e] = fmaxf(amax[e], fabsf(hv));
     }
   }
 }
 
-// fragment-ordered operand block of the workgroup's first m-tile
-template <int BF>
-__device__ __forceinline__ const uint8_t* a_base(const void* A, int row0, int K) {
-  return (const uint8_t*)A + (size_t)(row0 / 16) * (K / kChunk) * AGeom<BF>::kBlk;
+// workgroup -> (m-block, column group); groups shared by several m-blocks are
+// numbered 8 apart (one XCD under round-robin placement) when possible
+__device__ __forceinline__ void gateup_block(const GateUpArgs& g, int ngroups, int& mb, int& ng) {
+  const int b = blockIdx.x;
+  if (g.n_mb > 1 && ngroups % 8 == 0) {
+    const int q = b >> 3;
+    mb = q % g.n_mb;
+    ng = (q / g.n_mb) * 8 + (b & 7);
+  } else {
+    mb = b % g.n_mb;
+    ng = b / g.n_mb;
+  }
 }
 
-// ---- K-split (few rows)
-constexpr int kKsWaves = 8;
-
-template <int BF, int MT, int T, bool BF16H>
-__global__ __launch_bounds__(64 * kKsWaves) void ks_gateup(GateUpArgs g) {
+// MT m-tiles per workgroup, MS x KS waves, MTW = ceil(MT / MS) m-tiles per wave
+template <int BF, int MT, int T, int MS, int KS, int D, bool BF16H>
+__global__ __launch_bounds__(64 * MS * KS) void ks_gateup(GateUpArgs g) {
+  constexpr int MTW = (MT + MS - 1) / MS;
   extern __shared__ float red[];
-  const int mb = blockIdx.x % g.n_mb, ng = blockIdx.x / g.n_mb;
+  int mb, ng;
+  gateup_block(g, (g.I / 8) / T, mb, ng);
   const int C = g.H / kChunk;
   const int row0 = mb * MT * 16;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int ms = wave % MS, kidx = wave / MS;
+  const int nvalid = MT - ms * MTW < MTW ? MT - ms * MTW : MTW;
   const size_t wt = (size_t)C * Fmt<BF>::kGlobal, bt = (size_t)((C + 7) / 8) * 1024;
-  const LanePtrs lp = lane_ptrs<BF>(a_base<BF>(g.xq, row0, g.H), g.H, g.wcodes + (size_t)ng * T * wt, wt,
-                                    g.wbscales + (size_t)ng * T * bt, bt);
-  v4f acc[MT][T];
+  const LanePtrs lp = lane_ptrs<BF>(g.xq + (size_t)(row0 / 16 + ms * MTW) * C * AGeom<BF>::kBlk, g.H, nvalid,
+                                    g.wcodes + (size_t)ng * T * wt, wt, g.wbscales + (size_t)ng * T * bt, bt);
+  v4f acc[MTW][T];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+  for (int j = 0; j < MTW; ++j)
 #pragma unroll
-    for (int t = 0; t < T; ++t) acc[mt][t] = v4f{0.f, 0.f, 0.f, 0.f};
-  ks_mainloop<BF, MT, T, kKsWaves, 2>(lp, 0, C, acc);
-  ks_stash<MT, T>(acc, red);
+    for (int t = 0; t < T; ++t) acc[j][t] = v4f{0.f, 0.f, 0.f, 0.f};
+  ks_mainloop<BF, MTW, T, KS, D>(lp, kidx, 0, C, acc);
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   // one wave per m-tile (rows are owned by exactly one wave, so the row
-  // maxima need no cross-wave combination)
-  for (int mt = wave; mt < MT; mt += kKsWaves) {
-    EpiScales<BF, 1, T> es;
-    load_epi<BF, 1, T>(es, g, row0 + mt * 16, ng * T, [](int) { return 0; });
-    float rowmax[4] = {0.f, 0.f, 0.f, 0.f};
+  // maxima need no cross-wave combination); m-tile q = (ms, j) was
+  // accumulated by waves ms, ms + MS, ... (pairs j*T + t of each).  The
+  // epilogue scales are loaded before the partial tiles go through LDS.
+  constexpr int NW = MS * KS, Q = (MT + NW - 1) / NW;
+  EpiScales<Q, T> es;
+  load_epi<BF, Q, T>(es, g, row0, ng * T, [&](int j) { return wave + NW * j < MT ? wave + NW * j : wave; });
+  ks_stash<MTW, T>(acc, red);
+#pragma unroll
+  for (int jq = 0; jq < Q; ++jq) {
+    const int q = wave + NW * jq;
+    if (q >= MT) break;
+    const int qm = q / MTW, qj = q % MTW;
+    float amax[2] = {0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       v4f v;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = ks_sum<kKsWaves>(red, MT * T, mt * T + t, i, lane);
-      gateup_tile_epilogue<BF16H>(g, v, es.xs[0], es.cg[t], es.cu[t], row0 + mt * 16, ng * T + t, rowmax);
+      for (int i = 0; i < 4; ++i) v[i] = ks_sum<KS>(red, MTW * T, qm, MS, qj * T + t, i, lane);
+      gateup_tile_epilogue<BF16H, 8 * T>(g, v, es.xs[jq], es.cg[t], es.cu[t], row0 + q * 16, ng, t, amax);
     }
     if constexpr (!BF16H) {
-      if ((lane & 15) == 0)
+      const int ngroups = (g.I / 8) / T;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) g.amax_part[(size_t)ng * g.Mpad + row0 + mt * 16 + 4 * (lane >> 4) + i] = rowmax[i];
-    }
-  }
-}
-
-// ---- M-split (many rows)
-template <int BF, int MT, int T, bool BF16H>
-__global__ __launch_bounds__(64 * kMsWaves) void ms_gateup(GateUpArgs g) {
-  using G = MsGeom<BF, MT, T>;
-  __shared__ v4i lds[2 * G::SLOT / 16];
-  const int mb = blockIdx.x % g.n_mb, ng = blockIdx.x / g.n_mb;
-  const int C = g.H / kChunk;
-  const int row0 = mb * MT * 16;
-  const size_t wt = (size_t)C * Fmt<BF>::kGlobal, bt = (size_t)((C + 7) / 8) * 1024;
-  const LanePtrs lp = lane_ptrs<BF>(a_base<BF>(g.xq, row0, g.H), g.H, g.wcodes + (size_t)ng * T * wt, wt,
-                                    g.wbscales + (size_t)ng * T * bt, bt);
-  v4f acc[G::MTW][T];
+      for (int e = 0; e < 2; ++e) amax[e] = max8(amax[e]);
+      if ((lane & 7) == 0) {      // lane 16 gq (rows 0, 1) and 16 gq + 8 (rows 2, 3)
+        const int m = row0 + q * 16 + 4 * (lane >> 4) + ((lane & 8) ? 2 : 0);
 #pragma unroll
-  for (int j = 0; j < G::MTW; ++j)
-#pragma unroll
-    for (int t = 0; t < T; ++t) acc[j][t] = v4f{0.f, 0.f, 0.f, 0.f};
-  ms_mainloop<BF, MT, T>(lp, 0, C, lds, acc);
-
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  // padding m-tiles (wave + 4 j >= MT) read the wave's first m-tile's scales
-  auto mt_of = [&](int j) { return wave + kMsWaves * j < MT ? wave + kMsWaves * j : wave; };
-  EpiScales<BF, G::MTW, T> es;
-  load_epi<BF, G::MTW, T>(es, g, row0, ng * T, mt_of);
-#pragma unroll
-  for (int j = 0; j < G::MTW; ++j) {
-    const int mt = wave + kMsWaves * j;
-    if (mt < MT) {
-      float rowmax[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int t = 0; t < T; ++t)
-        gateup_tile_epilogue<BF16H>(g, acc[j][t], es.xs[j], es.cg[t], es.cu[t], row0 + mt * 16, ng * T + t, rowmax);
-      if constexpr (!BF16H) {
-        if ((lane & 15) == 0)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) g.amax_part[(size_t)ng * g.Mpad + row0 + mt * 16 + 4 * (lane >> 4) + i] = rowmax[i];
+        for (int e = 0; e < 2; ++e) g.amax_part[(size_t)(m + e) * ngroups + ng] = amax[e];
       }
     }
   }
@@ -170,21 +153,25 @@ __global__ __launch_bounds__(64 * kMsWaves) void ms_gateup(GateUpArgs g) {
 
 // ---------------------------------------------------------------- dispatch
 
+// Wave grid per m-tile count: up to 4 m-tiles, 8 waves all splitting K (the
+// whole weight range of a workgroup is in flight at once); 7 m-tiles, 4
+// K-split waves; 13 m-tiles, 2 x 2 (each wave half the rows and half the
+// inputs), which keeps a wave's accumulators and two chunks of operands in
+// registers.
 template <int BF, bool BF16H, int MT, int T>
 hipError_t go(const GateUpArgs& g, int grid, hipStream_t st) {
-  if constexpr (MT <= 4) {
-    auto fn = ks_gateup<BF, MT, T, BF16H>;
-    const size_t lds = (size_t)kKsWaves * MT * T * 256 * sizeof(float);
-    static bool attr = false;   // idempotent; a race only repeats the call
-    if (!attr) {
-      hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (e != hipSuccess) return e;
-      attr = true;
-    }
-    hipLaunchKernelGGL(fn, dim3(grid), dim3(64 * kKsWaves), lds, st, g);
-  } else {
-    hipLaunchKernelGGL((ms_gateup<BF, MT, T, BF16H>), dim3(grid), dim3(64 * kMsWaves), 0, st, g);
+  constexpr int MS = MT >= 13 ? 2 : 1;
+  constexpr int KS = MT <= 4 ? 8 : (MT >= 13 ? 2 : 4);
+  constexpr int MTW = (MT + MS - 1) / MS;
+  auto fn = ks_gateup<BF, MT, T, MS, KS, 2, BF16H>;
+  const size_t lds = (size_t)MS * KS * MTW * T * 256 * sizeof(float);
+  static bool attr = false;   // idempotent; a race only repeats the call
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr = true;
   }
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(64 * MS * KS), lds, st, g);
   return hipGetLastError();
 }
 

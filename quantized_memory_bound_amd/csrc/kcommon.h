@@ -42,12 +42,12 @@ struct GateUpArgs {
   const float* wscales;     // FP8: [2][I] per-row scales
   const uint8_t* wbscales;  // NVFP4: block-scale groups
   const float* tscales;     // NVFP4: blob header s_gate, s_up
-  float* h32;               // [Mpad][p32] (FP8 / NVFP4 down modes)
+  float* h32;               // FP8 / NVFP4 down modes: [ngroups][Mpad][8 T] (each workgroup's
+                            // columns of h form one contiguous block)
   uint16_t* hb;             // bf16(h), fragment order (BF16-down mode)
   uint16_t* tap_hb;         // optional plain [M][I] copy of bf16(h) (BF16-down mode)
-  float* amax_part;         // [ngroups][Mpad] max |h| of each row over each workgroup's columns
+  float* amax_part;         // [Mpad][ngroups] max |h| of each row over each workgroup's columns
   int H, I, M, n_mb, Mpad;
-  int p32;                  // h32 row pitch (floats)
 };
 
 struct DownArgs {
@@ -120,13 +120,37 @@ __device__ __forceinline__ void e4m3x2_scales(uint32_t two, v2h& s0, v2h& s1) {
   s1 = v2h{sc[1], sc[1]};
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+// SiLU(g) = g / (1 + e^-g): hardware exp2, correctly rounded fp32 division
+// (h feeds bf16 / E4M3 rounding decisions, so the division is kept exact);
+// e^-g overflowing to +inf gives -0 for very negative g.
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+
+// Cross-lane moves inside 16-lane rows through DPP (no LDS round trip).
+// CTRL: 0x128 row_ror:8 (lane r <- r ^ 8), 0xB1 quad_perm [1,0,3,2] (r ^ 1),
+// 0x4E quad_perm [2,3,0,1] (r ^ 2), 0x141 row_half_mirror (r <- 7 - r in
+// each half-row).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+// maximum over each group of 8 lanes (lanes 8k .. 8k+7)
+__device__ __forceinline__ float max8(float v) {
+  v = fmaxf(v, dpp<0xB1>(v));
+  v = fmaxf(v, dpp<0x4E>(v));
+  return fmaxf(v, dpp<0x141>(v));
+}
+
+// maximum over the wave, returned in every lane: 16-lane rows through DPP
+// (0x140 row_mirror, r <- 15 - r), then the four row results via readlane
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(max8(v), dpp<0x140>(max8(v)));
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
 
 template <class T>
 __device__ __forceinline__ T ld_nt(const T* p) { return __builtin_nontemporal_load(p); }

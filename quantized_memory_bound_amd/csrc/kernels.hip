@@ -102,7 +102,7 @@ __global__ __launch_bounds__(kThreads) void k_xquant(const uint16_t* __restrict_
 
 // ---------------------------------------------------------------- k_requant
 
-// amax_part[g][m] holds the |h| maximum of row m over the columns of gate/up
+// amax_part[m][g] holds the |h| maximum of row m over the columns of gate/up
 // workgroup g; every block first reduces the row's ngroups partial maxima.
 // Rows M..Mpad-1 (padding, possibly beyond the gate/up m-blocks) get zero
 // codes and scale 0 without reading h.
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(kThreads) void k_xquant(const uint16_t* __restrict_
 // receive the plain [M][I] codes and [M] scales.
 __global__ __launch_bounds__(kThreads) void k_requant(const float* __restrict__ h32,
                                                       const float* __restrict__ amax_part, int ngroups, int M,
-                                                      int Mpad, int I, int p32, uint8_t* __restrict__ hq,
+                                                      int Mpad, int I, int W, uint8_t* __restrict__ hq,
                                                       float* __restrict__ sh, uint8_t* __restrict__ tap_q,
                                                       float* __restrict__ tap_s) {
   __shared__ float s_max[kWaves];
@@ -124,7 +124,7 @@ __global__ __launch_bounds__(kThreads) void k_requant(const float* __restrict__ 
     return;
   }
   float a = 0.0f;
-  for (int g = threadIdx.x; g < ngroups; g += kThreads) a = fmaxf(a, amax_part[(size_t)g * Mpad + m]);
+  for (int g = threadIdx.x; g < ngroups; g += kThreads) a = fmaxf(a, amax_part[(size_t)m * ngroups + g]);
   a = wave_max(a);
   if (lane == 0) s_max[wave] = a;
   __syncthreads();
@@ -136,7 +136,9 @@ __global__ __launch_bounds__(kThreads) void k_requant(const float* __restrict__ 
   }
   const int k = (blockIdx.x * kThreads + threadIdx.x) * 4;
   if (k >= I) return;
-  const v4f v = *(const v4f*)(h32 + (size_t)m * p32 + k);
+  // h32 holds each gate/up workgroup's W columns as one [Mpad][W] block;
+  // 4 consecutive columns never straddle two blocks (W is a multiple of 8)
+  const v4f v = *(const v4f*)(h32 + ((size_t)(k / W) * Mpad + m) * W + k % W);
   uint32_t out = 0u;
   if (s > 0.0f) {
 #pragma unroll
@@ -183,14 +185,13 @@ int launch_forward(const Plan& p, const FwdArgs& a) {
   g.h32 = h32; g.hb = hb; g.amax_part = amax_part;
   g.tap_hb = bf16_down ? (uint16_t*)a.taps.h_out : nullptr;
   g.H = p.hidden; g.I = p.inter; g.M = p.M; g.n_mb = p.n_mblocks; g.Mpad = p.Mpad;
-  g.p32 = p.p32;
   e = launch_gateup(p, g, st);
   if (e != hipSuccess) return (int)e;
   stage(a, 2);
 
   if (!bf16_down) {
     hipLaunchKernelGGL(k_requant, dim3((p.inter + 1023) / 1024, p.Mpad), dim3(kThreads), 0, st, h32, amax_part,
-                       p.ngroups1, p.M, p.Mpad, p.inter, p.p32, hq, sh, (uint8_t*)a.taps.h_out,
+                       p.ngroups1, p.M, p.Mpad, p.inter, 8 * p.T1, hq, sh, (uint8_t*)a.taps.h_out,
                        (float*)a.taps.h_scales);
     e = hipGetLastError();
     if (e != hipSuccess) return (int)e;

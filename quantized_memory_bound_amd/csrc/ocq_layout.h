@@ -115,8 +115,6 @@ struct Plan {
   // down kernel: n_mb2 m-blocks of MT2 m-tiles x ngroups2 groups of T2 tiles,
   // every workgroup over the whole input range
   int MT2, n_mb2, T2, ngroups2;
-  int p32;         // h32 row pitch (floats), padded so that rows of power-of-two
-                   // length do not all start in the same L2 channel
   // workspace offsets (xq, hq, hb are fragment-ordered operand buffers of Mpad rows)
   size_t off_xq, off_sx, off_amax, off_h32, off_hq, off_hb, off_sh, total;
 };
@@ -178,11 +176,10 @@ inline Plan make_plan(int M, int hidden, int inter, int prec) {
   // workspace
   size_t Mp = p.Mpad;
   size_t o = 0;
-  p.p32 = inter + 32;
   p.off_xq = o;   o = align_up(o + Mp * hidden);
   p.off_sx = o;   o = align_up(o + Mp * 4);
   p.off_amax = o; o = align_up(o + (size_t)p.ngroups1 * Mp * 4);   // per-workgroup row maxima of |h|
-  p.off_h32 = o;  o = align_up(o + (prec == kFP8DownBF16 ? 0 : Mp * p.p32 * 4));
+  p.off_h32 = o;  o = align_up(o + (prec == kFP8DownBF16 ? 0 : Mp * inter * 4));   // [ngroups1][Mpad][8 T1]
   p.off_hq = o;   o = align_up(o + (prec == kFP8DownBF16 ? 0 : Mp * inter));
   p.off_hb = o;   o = align_up(o + (prec == kFP8DownBF16 ? Mp * inter * 2 : 0));
   p.off_sh = o;   o = align_up(o + Mp * 4);

@@ -123,6 +123,13 @@ __global__ __launch_bounds__(kThreads) void k_requant(const float* __restrict__ 
     if (k < I) *(uint32_t*)(hq + frag_off8(m, k, I / 128)) = 0u;
     return;
   }
+  // this thread's 4 values of h are requested before the row maximum, so the
+  // two loads are in flight together.  h32 holds each gate/up workgroup's W
+  // columns as one [Mpad][W] block; 4 consecutive columns never straddle two
+  // blocks (W is a multiple of 8).
+  const int k = (blockIdx.x * kThreads + threadIdx.x) * 4;
+  const bool has = k < I;
+  const v4f v = has ? *(const v4f*)(h32 + ((size_t)(k / W) * Mpad + m) * W + k % W) : v4f{0.f, 0.f, 0.f, 0.f};
   float a = 0.0f;
   for (int g = threadIdx.x; g < ngroups; g += kThreads) a = fmaxf(a, amax_part[(size_t)m * ngroups + g]);
   a = wave_max(a);
@@ -134,11 +141,7 @@ __global__ __launch_bounds__(kThreads) void k_requant(const float* __restrict__ 
     sh[m] = s;
     if (tap_s) tap_s[m] = s;
   }
-  const int k = (blockIdx.x * kThreads + threadIdx.x) * 4;
-  if (k >= I) return;
-  // h32 holds each gate/up workgroup's W columns as one [Mpad][W] block;
-  // 4 consecutive columns never straddle two blocks (W is a multiple of 8)
-  const v4f v = *(const v4f*)(h32 + ((size_t)(k / W) * Mpad + m) * W + k % W);
+  if (!has) return;
   uint32_t out = 0u;
   if (s > 0.0f) {
 #pragma unroll

@@ -201,6 +201,112 @@ __device__ __forceinline__ void ks_mainloop(const LanePtrs& p, int kidx, int c0,
       });
 }
 
+// Main loop for the f16-converting formats with E4M3 activations (gate/up),
+// for waves that hold many m-tiles and cannot afford a second register copy
+// of a chunk.  Each operand fragment is two 16 B units per lane: unit 0 feeds
+// sub-steps 0-1, unit 1 sub-steps 2-3.  As soon as a unit has been consumed
+// its registers are reloaded in place: activations with the next chunk,
+// weights with the chunk after next (two weight buffers alternate), so the
+// L2 latency of the activations and the HBM latency of the weights are
+// covered by the remaining work of the current chunk.  NVFP4 weights are one
+// unit per tile, reloaded after sub-step 3.  Scheduling fences keep every
+// reload at the point where its unit is free, so the compiler neither
+// hoists it (which would need more registers) nor waits on it early.  EXACT:
+// every wave has the same even number of chunks (no padding chunk, no
+// zeroing); otherwise the count is rounded up to even, chunk indices past the
+// range are clamped for the loads and their weight operand is zeroed.
+// NK > 0: every wave has exactly NK chunks and the loop is fully unrolled, so
+// the compiler knows which loads each wait is for (across a loop back-edge it
+// waits for all of them).
+template <int BF, int MT, int T, int KS, bool EXACT, int NK = 0>
+__device__ __forceinline__ void ks_mainloop_roll(const LanePtrs& p, int kidx, int c0, int c1, v4f (&acc)[MT][T]) {
+  static_assert(BF == kB_FP8_F16 || BF == kB_FP4_F16, "f16-converting weight formats only");
+  constexpr int UB = Fmt<BF>::kUnits;
+  const int nk = NK > 0 ? NK : ((c1 - c0 + KS - 1) / KS + 1) / 2 * 2;
+  auto cidx = [&](int k) { const int c = c0 + kidx + k * KS; return c < c1 ? c : c1 - 1; };
+  auto a_ld = [&](int mt, int c, int u) {
+    return *(const v4i*)(p.a + (mt < p.a_nvalid ? mt : p.a_nvalid - 1) * p.a_mt_stride + (size_t)c * p.a_chunk +
+                         u * 1024);
+  };
+  auto b_ld = [&](int t, int c, int u) {
+    return ld_nt((const v4i*)(p.w + t * p.w_tile + (size_t)c * Fmt<BF>::kGlobal + u * 1024));
+  };
+  auto sb_ld = [&](int t, int c) {
+    return (uint32_t) * (const uint16_t*)(p.wb + t * p.wb_tile + (size_t)(c >> 3) * 1024 + 2 * (c & 7));
+  };
+  v4i a[MT][2];
+  v4i b[2][T][UB];
+  uint32_t sb[2][T];
+#pragma unroll
+  for (int d = 0; d < 2; ++d)
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+#pragma unroll
+      for (int u = 0; u < UB; ++u) b[d][t][u] = b_ld(t, cidx(d), u);
+      sb[d][t] = BF == kB_FP4_F16 ? sb_ld(t, cidx(d)) : 0u;
+    }
+#pragma unroll
+  for (int j = 0; j < MT; ++j) {
+    a[j][0] = a_ld(j, cidx(0), 0);
+    a[j][1] = a_ld(j, cidx(0), 1);
+  }
+#pragma unroll
+  for (int k0 = 0; k0 < (NK > 0 ? NK : nk); k0 += 2) {
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      const int k = k0 + d;
+      const int cn = cidx(k + 1), cb = cidx(k + 2);
+      if constexpr (!EXACT) {
+        if (c0 + kidx + k * KS >= c1) {
+#pragma unroll
+          for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int u = 0; u < UB; ++u) b[d][t][u] = v4i{0, 0, 0, 0};
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v8h bv[T];
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          if constexpr (BF == kB_FP8_F16) {
+            const v4i& w = b[d][t][i >> 1];
+            bv[t] = e4m3x8_to_f16((uint32_t)w[2 * (i & 1)], (uint32_t)w[2 * (i & 1) + 1]);
+          } else {
+            v2h s0, s1;
+            e4m3x2_scales(sb[d][t], s0, s1);
+            bv[t] = e2m1x8_to_f16((uint32_t)b[d][t][0][i], i < 2 ? s0 : s1);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < MT; ++j) {
+          const v4i& w = a[j][i >> 1];
+          const v8h av = e4m3x8_to_f16((uint32_t)w[2 * (i & 1)], (uint32_t)w[2 * (i & 1) + 1]);
+#pragma unroll
+          for (int t = 0; t < T; ++t) acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv[t], acc[j][t], 0, 0, 0);
+        }
+        if (i == 1 || i == 3) {
+          const int u = i >> 1;
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int j = 0; j < MT; ++j) a[j][u] = a_ld(j, cn, u);
+          if constexpr (BF == kB_FP8_F16) {
+#pragma unroll
+            for (int t = 0; t < T; ++t) b[d][t][u] = b_ld(t, cb, u);
+          } else if (i == 3) {
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+              b[d][t][0] = b_ld(t, cb, 0);
+              sb[d][t] = sb_ld(t, cb);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+  }
+}
+
 // LDS partial tiles [wave][pair][i][lane]; returns after a workgroup barrier
 template <int MT, int T>
 __device__ __forceinline__ void ks_stash(const v4f (&acc)[MT][T], float* red) {

@@ -96,6 +96,8 @@ __device__ __forceinline__ void gateup_block(const GateUpArgs& g, int ngroups, i
 }
 
 // MT m-tiles per workgroup, MS x KS waves, MTW = ceil(MT / MS) m-tiles per wave
+// D > 0: prefetch depth of ks_mainloop; D = -1: ks_mainloop_roll with
+// padding chunks; D <= -2: ks_mainloop_roll with exactly -D chunks per wave
 template <int BF, int MT, int T, int MS, int KS, int D, bool BF16H>
 __global__ __launch_bounds__(64 * MS * KS) void ks_gateup(GateUpArgs g) {
   constexpr int MTW = (MT + MS - 1) / MS;
@@ -115,37 +117,52 @@ __global__ __launch_bounds__(64 * MS * KS) void ks_gateup(GateUpArgs g) {
   for (int j = 0; j < MTW; ++j)
 #pragma unroll
     for (int t = 0; t < T; ++t) acc[j][t] = v4f{0.f, 0.f, 0.f, 0.f};
-  ks_mainloop<BF, MTW, T, KS, D>(lp, kidx, 0, C, acc);
+  if constexpr (D == -1) ks_mainloop_roll<BF, MTW, T, KS, false>(lp, kidx, 0, C, acc);
+  else if constexpr (D < -1) ks_mainloop_roll<BF, MTW, T, KS, true, -D>(lp, kidx, 0, C, acc);
+  else ks_mainloop<BF, MTW, T, KS, D>(lp, kidx, 0, C, acc);
 
-  // one wave per m-tile (rows are owned by exactly one wave, so the row
-  // maxima need no cross-wave combination); m-tile q = (ms, j) was
-  // accumulated by waves ms, ms + MS, ... (pairs j*T + t of each).  The
-  // epilogue scales are loaded before the partial tiles go through LDS.
+  // Epilogue, one wave per m-tile (rows are owned by exactly one wave, so the
+  // row maxima need no cross-wave combination).  The partial tiles go through
+  // LDS one weight tile t at a time ([wave][m-tile][i][lane], NW * MTW KB);
+  // m-tile q = (ms, j) was accumulated by waves ms, ms + MS, ...  The
+  // epilogue scales are loaded before the first exchange.
   constexpr int NW = MS * KS, Q = (MT + NW - 1) / NW;
   EpiScales<Q, T> es;
   load_epi<BF, Q, T>(es, g, row0, ng * T, [&](int j) { return wave + NW * j < MT ? wave + NW * j : wave; });
-  ks_stash<MTW, T>(acc, red);
+  float amax[Q][2];
 #pragma unroll
-  for (int jq = 0; jq < Q; ++jq) {
-    const int q = wave + NW * jq;
-    if (q >= MT) break;
-    const int qm = q / MTW, qj = q % MTW;
-    float amax[2] = {0.f, 0.f};
+  for (int jq = 0; jq < Q; ++jq) amax[jq][0] = amax[jq][1] = 0.f;
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-      v4f v;
+  for (int t = 0; t < T; ++t) {
+    if (t) __syncthreads();              // the previous tile's partials have been read
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = ks_sum<KS>(red, MTW * T, qm, MS, qj * T + t, i, lane);
-      gateup_tile_epilogue<BF16H, 8 * T>(g, v, es.xs[jq], es.cg[t], es.cu[t], row0 + q * 16, ng, t, amax);
+    for (int j = 0; j < MTW; ++j) *(v4f*)&red[((wave * MTW + j) * 64 + lane) * 4] = acc[j][t];
+    __syncthreads();
+#pragma unroll
+    for (int jq = 0; jq < Q; ++jq) {
+      const int q = wave + NW * jq;
+      if (q < MT) {
+        const int qm = q / MTW, qj = q % MTW;
+        v4f v = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) v += *(const v4f*)&red[(((qm + MS * ks) * MTW + qj) * 64 + lane) * 4];
+        gateup_tile_epilogue<BF16H, 8 * T>(g, v, es.xs[jq], es.cg[t], es.cu[t], row0 + q * 16, ng, t, amax[jq]);
+      }
     }
-    if constexpr (!BF16H) {
-      const int ngroups = (g.I / 8) / T;
+  }
+  if constexpr (!BF16H) {
+    const int ngroups = (g.I / 8) / T;
 #pragma unroll
-      for (int e = 0; e < 2; ++e) amax[e] = max8(amax[e]);
-      if ((lane & 7) == 0) {      // lane 16 gq (rows 0, 1) and 16 gq + 8 (rows 2, 3)
-        const int m = row0 + q * 16 + 4 * (lane >> 4) + ((lane & 8) ? 2 : 0);
+    for (int jq = 0; jq < Q; ++jq) {
+      const int q = wave + NW * jq;
+      if (q < MT) {
 #pragma unroll
-        for (int e = 0; e < 2; ++e) g.amax_part[(size_t)(m + e) * ngroups + ng] = amax[e];
+        for (int e = 0; e < 2; ++e) amax[jq][e] = max8(amax[jq][e]);
+        if ((lane & 7) == 0) {      // lane 16 gq (rows 0, 1) and 16 gq + 8 (rows 2, 3)
+          const int m = row0 + q * 16 + 4 * (lane >> 4) + ((lane & 8) ? 2 : 0);
+#pragma unroll
+          for (int e = 0; e < 2; ++e) g.amax_part[(size_t)(m + e) * ngroups + ng] = amax[jq][e];
+        }
       }
     }
   }
@@ -153,18 +170,11 @@ __global__ __launch_bounds__(64 * MS * KS) void ks_gateup(GateUpArgs g) {
 
 // ---------------------------------------------------------------- dispatch
 
-// Wave grid per m-tile count: up to 4 m-tiles, 8 waves all splitting K (the
-// whole weight range of a workgroup is in flight at once); 7 m-tiles, 4
-// K-split waves; 13 m-tiles, 2 x 2 (each wave half the rows and half the
-// inputs), which keeps a wave's accumulators and two chunks of operands in
-// registers.
-template <int BF, bool BF16H, int MT, int T>
-hipError_t go(const GateUpArgs& g, int grid, hipStream_t st) {
-  constexpr int MS = MT >= 13 ? 2 : 1;
-  constexpr int KS = MT <= 4 ? 8 : (MT >= 13 ? 2 : 4);
+template <int BF, bool BF16H, int MT, int T, int MS, int KS, int D>
+hipError_t launch_ks(const GateUpArgs& g, int grid, hipStream_t st) {
   constexpr int MTW = (MT + MS - 1) / MS;
-  auto fn = ks_gateup<BF, MT, T, MS, KS, 2, BF16H>;
-  const size_t lds = (size_t)MS * KS * MTW * T * 256 * sizeof(float);
+  auto fn = ks_gateup<BF, MT, T, MS, KS, D, BF16H>;
+  const size_t lds = (size_t)MS * KS * MTW * 256 * sizeof(float);
   static bool attr = false;   // idempotent; a race only repeats the call
   if (!attr) {
     hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -173,6 +183,24 @@ hipError_t go(const GateUpArgs& g, int grid, hipStream_t st) {
   }
   hipLaunchKernelGGL(fn, dim3(grid), dim3(64 * MS * KS), lds, st, g);
   return hipGetLastError();
+}
+
+// Eight waves (two per SIMD: each CU keeps enough operand loads in flight)
+// in an MS x KS grid: up to 7 m-tiles all eight split K; 13 m-tiles, 2 x 4
+// (each wave 7 m-tiles).  Up to 4 m-tiles a wave keeps two whole chunks in
+// flight; with 7 m-tiles per wave the operands are reloaded in place unit by
+// unit (ks_mainloop_roll), which fits the 256 registers a wave has at two
+// waves per SIMD.
+template <int BF, bool BF16H, int MT, int T>
+hipError_t go(const GateUpArgs& g, int grid, hipStream_t st) {
+  constexpr int MS = MT >= 13 ? 2 : 1;
+  constexpr int KS = 8 / MS;
+  constexpr int MTW = (MT + MS - 1) / MS;
+  const int C = g.H / kChunk;
+  if constexpr (MTW <= 4) return launch_ks<BF, BF16H, MT, T, MS, KS, 2>(g, grid, st);
+  else if (C == 4 * KS) return launch_ks<BF, BF16H, MT, T, MS, KS, -4>(g, grid, st);
+  else if (C == 8 * KS) return launch_ks<BF, BF16H, MT, T, MS, KS, -8>(g, grid, st);
+  else return launch_ks<BF, BF16H, MT, T, MS, KS, -1>(g, grid, st);
 }
 
 template <int BF, bool BF16H, int MT>

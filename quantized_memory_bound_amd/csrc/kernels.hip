@@ -24,6 +24,24 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 
+// Row-per-workgroup kernels write one row's pieces of 16-row fragment blocks.
+// Workgroup b handles row 16 mt + r (and slice `rest`) with
+//   b = ((rest * G + mt / 8) * 16 + r) * 8 + mt % 8,   G = ceil(mtiles / 8),
+// so the 16 rows of an m-tile are 8 workgroups apart: under round-robin
+// placement they run on one XCD and complete every cache line of their
+// blocks in that XCD's L2.  Returns false for the unused slots of the last
+// group of 8 m-tiles.
+__device__ __forceinline__ bool tile_row_of(int b, int mtiles, int& m, int& rest) {
+  const int G = (mtiles + 7) / 8;
+  const int x = b & 7, r = (b >> 3) & 15, q = b >> 7;
+  const int mt = (q % G) * 8 + x;
+  rest = q / G;
+  m = mt * 16 + r;
+  return mt < mtiles;
+}
+
+inline int tile_row_grid(int mtiles, int nrest) { return (mtiles + 7) / 8 * 128 * nrest; }
+
 // ---------------------------------------------------------------- k_xquant
 
 // One workgroup per row (all 256 threads), so the row's loads are all in
@@ -37,7 +55,8 @@ __global__ __launch_bounds__(kThreads) void k_xquant(const uint16_t* __restrict_
                                                      uint8_t* __restrict__ tap_q, float* __restrict__ tap_s) {
   __shared__ float s_max[kWaves];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int m = blockIdx.x;
+  int m, rest;
+  if (!tile_row_of(blockIdx.x, Mpad / 16, m, rest)) return;
   const int C = H / 128;
   if (m >= M) {                                     // padding row: zero codes, zero scale
     for (int k = threadIdx.x * 8; k < H; k += kThreads * 8) *(v2u*)(xq + frag_off8(m, k, C)) = v2u{0u, 0u};
@@ -115,11 +134,12 @@ __global__ __launch_bounds__(kThreads) void k_requant(const float* __restrict__ 
                                                       float* __restrict__ sh, uint8_t* __restrict__ tap_q,
                                                       float* __restrict__ tap_s) {
   __shared__ float s_max[kWaves];
-  const int m = blockIdx.y;
+  int m, xb;
+  if (!tile_row_of(blockIdx.x, Mpad / 16, m, xb)) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   if (m >= M) {
-    if (blockIdx.x == 0 && threadIdx.x == 0) sh[m] = 0.0f;
-    const int k = (blockIdx.x * kThreads + threadIdx.x) * 4;
+    if (xb == 0 && threadIdx.x == 0) sh[m] = 0.0f;
+    const int k = (xb * kThreads + threadIdx.x) * 4;
     if (k < I) *(uint32_t*)(hq + frag_off8(m, k, I / 128)) = 0u;
     return;
   }
@@ -127,7 +147,7 @@ __global__ __launch_bounds__(kThreads) void k_requant(const float* __restrict__ 
   // two loads are in flight together.  h32 holds each gate/up workgroup's W
   // columns as one [Mpad][W] block; 4 consecutive columns never straddle two
   // blocks (W is a multiple of 8).
-  const int k = (blockIdx.x * kThreads + threadIdx.x) * 4;
+  const int k = (xb * kThreads + threadIdx.x) * 4;
   const bool has = k < I;
   const v4f v = has ? *(const v4f*)(h32 + ((size_t)(k / W) * Mpad + m) * W + k % W) : v4f{0.f, 0.f, 0.f, 0.f};
   float a = 0.0f;
@@ -137,7 +157,7 @@ __global__ __launch_bounds__(kThreads) void k_requant(const float* __restrict__ 
   __syncthreads();
   a = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
   const float s = a / 448.0f;
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
+  if (xb == 0 && threadIdx.x == 0) {
     sh[m] = s;
     if (tap_s) tap_s[m] = s;
   }
@@ -173,7 +193,7 @@ int launch_forward(const Plan& p, const FwdArgs& a) {
 
   stage(a, 0);
   const bool bf16_down = p.prec == kFP8DownBF16;
-  hipLaunchKernelGGL(k_xquant, dim3(p.Mpad), dim3(kThreads), 0, st, a.x, p.M, p.hidden, p.Mpad, xq, sx,
+  hipLaunchKernelGGL(k_xquant, dim3(tile_row_grid(p.Mpad / 16, 1)), dim3(kThreads), 0, st, a.x, p.M, p.hidden, p.Mpad, xq, sx,
                      (uint8_t*)a.taps.x_codes, (float*)a.taps.x_scales);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return (int)e;
@@ -193,7 +213,8 @@ int launch_forward(const Plan& p, const FwdArgs& a) {
   stage(a, 2);
 
   if (!bf16_down) {
-    hipLaunchKernelGGL(k_requant, dim3((p.inter + 1023) / 1024, p.Mpad), dim3(kThreads), 0, st, h32, amax_part,
+    hipLaunchKernelGGL(k_requant, dim3(tile_row_grid(p.Mpad / 16, (p.inter + 1023) / 1024)), dim3(kThreads), 0, st,
+                       h32, amax_part,
                        p.ngroups1, p.M, p.Mpad, p.inter, 8 * p.T1, hq, sh, (uint8_t*)a.taps.h_out,
                        (float*)a.taps.h_scales);
     e = hipGetLastError();

@@ -134,10 +134,10 @@ __global__ __launch_bounds__(64 * MS * KS) void ks_gateup(GateUpArgs g) {
   for (int jq = 0; jq < Q; ++jq) amax[jq][0] = amax[jq][1] = 0.f;
 #pragma unroll
   for (int t = 0; t < T; ++t) {
-    if (t) __syncthreads();              // the previous tile's partials have been read
+    if (t) lds_barrier();                // the previous tile's partials have been read
 #pragma unroll
     for (int j = 0; j < MTW; ++j) *(v4f*)&red[((wave * MTW + j) * 64 + lane) * 4] = acc[j][t];
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int jq = 0; jq < Q; ++jq) {
       const int q = wave + NW * jq;

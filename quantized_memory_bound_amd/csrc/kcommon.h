@@ -155,6 +155,13 @@ __device__ __forceinline__ float wave_max(float v) {
 template <class T>
 __device__ __forceinline__ T ld_nt(const T* p) { return __builtin_nontemporal_load(p); }
 
+// Workgroup barrier for LDS exchanges only: waits for this wave's LDS
+// operations, not for its outstanding global stores (a __syncthreads() is a
+// workgroup-scope release and would wait for those too).  Correct where no
+// wave of the workgroup reads what the others stored to global memory.  The
+// memory clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 __device__ __forceinline__ v8i cat(v4i lo, v4i hi) {
   return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }

@@ -59,13 +59,19 @@ __device__ __forceinline__ LanePtrs lane_ptrs(const void* A, int K, int nvalid, 
   return p;
 }
 
-template <int BF, int MT, int T>
+// WNT: weight loads carry the non-temporal hint.  Right when every weight
+// byte is read by one workgroup only; where several workgroups on one XCD
+// share weight tiles (the down projection's m-blocks) plain loads keep the
+// lines in L2 for the others.
+template <int BF, int MT, int T, bool WNT = true>
 __device__ __forceinline__ void load_chunk(ChunkRegs<BF, MT, T>& r, const LanePtrs& p, int c) {
 #pragma unroll
   for (int t = 0; t < T; ++t) {
 #pragma unroll
-    for (int u = 0; u < Fmt<BF>::kUnits; ++u)
-      r.b[t][u] = ld_nt((const v4i*)(p.w + t * p.w_tile + (size_t)c * Fmt<BF>::kGlobal + u * 1024));
+    for (int u = 0; u < Fmt<BF>::kUnits; ++u) {
+      const v4i* q = (const v4i*)(p.w + t * p.w_tile + (size_t)c * Fmt<BF>::kGlobal + u * 1024);
+      r.b[t][u] = WNT ? ld_nt(q) : *q;
+    }
     if constexpr (BF == kB_FP4_F16)
       r.sb[t] = *(const uint16_t*)(p.wb + t * p.wb_tile + (size_t)(c >> 3) * 1024 + 2 * (c & 7));
   }
@@ -185,7 +191,7 @@ __device__ __forceinline__ void zero_b(ChunkRegs<BF, MT, T>& r) {
 // clamped to the last chunk for the loads and its weight operand is zeroed,
 // so no load depends on the wave or the iteration.  kidx: the wave's K-split
 // index (wave-uniform), KS: number of K-split waves.
-template <int BF, int MT, int T, int KS, int D>
+template <int BF, int MT, int T, int KS, int D, bool WNT = true>
 __device__ __forceinline__ void ks_mainloop(const LanePtrs& p, int kidx, int c0, int c1, v4f (&acc)[MT][T]) {
   const int nk = ((c1 - c0 + KS - 1) / KS + D - 1) / D * D;
   ChunkRegs<BF, MT, T> r[D];
@@ -193,7 +199,7 @@ __device__ __forceinline__ void ks_mainloop(const LanePtrs& p, int kidx, int c0,
       nk,
       [&](int d, int k) {
         const int c = c0 + kidx + k * KS;
-        load_chunk(r[d], p, c < c1 ? c : c1 - 1);
+        load_chunk<BF, MT, T, WNT>(r[d], p, c < c1 ? c : c1 - 1);
       },
       [&](int d, int k) {
         if (c0 + kidx + k * KS >= c1) zero_b(r[d]);
@@ -228,8 +234,8 @@ __device__ __forceinline__ void ks_mainloop_roll(const LanePtrs& p, int kidx, in
     return *(const v4i*)(p.a + (mt < p.a_nvalid ? mt : p.a_nvalid - 1) * p.a_mt_stride + (size_t)c * p.a_chunk +
                          u * 1024);
   };
-  auto b_ld = [&](int t, int c, int u) {
-    return ld_nt((const v4i*)(p.w + t * p.w_tile + (size_t)c * Fmt<BF>::kGlobal + u * 1024));
+  auto b_ld = [&](int t, int c, int u) {   // plain loads (measured faster than non-temporal here)
+    return *(const v4i*)(p.w + t * p.w_tile + (size_t)c * Fmt<BF>::kGlobal + u * 1024);
   };
   auto sb_ld = [&](int t, int c) {
     return (uint32_t) * (const uint16_t*)(p.wb + t * p.wb_tile + (size_t)(c >> 3) * 1024 + 2 * (c & 7));

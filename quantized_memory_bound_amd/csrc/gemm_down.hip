@@ -58,7 +58,7 @@ __global__ __launch_bounds__(64 * NW) void ks_down(DownArgs d) {
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int t = 0; t < T; ++t) acc[mt][t] = v4f{0.f, 0.f, 0.f, 0.f};
-  ks_mainloop<BF, MT, T, NW, D>(lp, __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), 0, C, acc);
+  ks_mainloop<BF, MT, T, NW, D, false>(lp, __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), 0, C, acc);
   ks_stash<MT, T>(acc, red);
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, gq = lane >> 4, r = lane & 15;

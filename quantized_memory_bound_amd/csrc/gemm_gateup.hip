@@ -48,34 +48,35 @@ __device__ __forceinline__ void load_epi(EpiScales<Q, T>& e, const GateUpArgs& g
 
 // Epilogue of one 16x16 tile pair for one m-tile: v = accumulated tile (gate
 // in lanes r < 8, up in lanes r + 8 of each 16-lane row, rows 4 gq + i),
-// m_base = first row of the m-tile, col = column of h within the workgroup's
-// block (t * 8 + r % 8), n = column of h.  One DPP exchange gives gate lane
-// r the up values of rows 0, 1 and up lane r + 8 the gate values of rows 2, 3,
-// so every lane evaluates two of the four h values.  amax[e] accumulates |h|
-// of the lane's row e (rows 0, 1 in gate lanes, 2, 3 in up lanes).
-template <bool BF16H, int W>
+// m_base = first row of the m-tile, n = column of h.  One DPP exchange gives
+// gate lane r the up values of rows 0, 2 and up lane r + 8 the gate values of
+// rows 1, 3, so every lane evaluates two of the four h values: value e is row
+// 4 gq + 2 e (gate lanes) or 4 gq + 2 e + 1 (up lanes).  Each 16-lane group
+// then stores two adjacent rows of the tile's 8 columns: 64 contiguous bytes
+// of the [tile][row][8] h32 block.  amax[e] accumulates |h| of value e.
+template <bool BF16H, int T>
 __device__ __forceinline__ void gateup_tile_epilogue(const GateUpArgs& g, const v4f& v, const float (&xs)[4],
                                                      float cg, float cu, int m_base, int ng, int t,
                                                      float (&amax)[2]) {
   const int lane = threadIdx.x & 63, gq = lane >> 4, r = lane & 15;
   const bool lo = r < 8;
-  const int col = t * 8 + (r & 7), n = ng * W + col;
-  const float p0 = dpp<0x128>(lo ? v[2] : v[0]);
-  const float p1 = dpp<0x128>(lo ? v[3] : v[1]);
+  const int c = r & 7, n = (ng * T + t) * 8 + c;
+  // gate lanes send G of rows 1, 3 and receive U of rows 0, 2
+  const float p0 = dpp<0x128>(lo ? v[1] : v[0]);
+  const float p1 = dpp<0x128>(lo ? v[3] : v[2]);
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
-    const int i = lo ? e : 2 + e;
-    const float gv = lo ? v[e] : (e ? p1 : p0);
-    const float uv = lo ? (e ? p1 : p0) : v[2 + e];
-    const float xsi = xs[i];
-    const float hv = silu(gv * xsi * cg) * (uv * xsi * cu);
+    const int i = 2 * e + (lo ? 0 : 1);
+    const float gv = lo ? v[i] : (e ? p1 : p0);
+    const float uv = lo ? (e ? p1 : p0) : v[i];
+    const float hv = silu(gv * xs[i] * cg) * (uv * xs[i] * cu);
     const int m = m_base + 4 * gq + i;
     if constexpr (BF16H) {
       const uint16_t hb = (uint16_t)bf16_bits(hv);
       g.hb[frag_off16(m, n, g.I / 128)] = hb;
       if (g.tap_hb && m < g.M) g.tap_hb[(size_t)m * g.I + n] = hb;
     } else {
-      g.h32[((size_t)ng * g.Mpad + m) * W + col] = hv;
+      g.h32[((size_t)(ng * T + t) * g.Mpad + m) * 8 + c] = hv;
       amax[e] = fmaxf(amax[e], fabsf(hv));
     }
   }
@@ -146,7 +147,7 @@ __global__ __launch_bounds__(64 * MS * KS) void ks_gateup(GateUpArgs g) {
         v4f v = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) v += *(const v4f*)&red[(((qm + MS * ks) * MTW + qj) * 64 + lane) * 4];
-        gateup_tile_epilogue<BF16H, 8 * T>(g, v, es.xs[jq], es.cg[t], es.cu[t], row0 + q * 16, ng, t, amax[jq]);
+        gateup_tile_epilogue<BF16H, T>(g, v, es.xs[jq], es.cg[t], es.cu[t], row0 + q * 16, ng, t, amax[jq]);
       }
     }
   }
@@ -158,10 +159,10 @@ __global__ __launch_bounds__(64 * MS * KS) void ks_gateup(GateUpArgs g) {
       if (q < MT) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) amax[jq][e] = max8(amax[jq][e]);
-        if ((lane & 7) == 0) {      // lane 16 gq (rows 0, 1) and 16 gq + 8 (rows 2, 3)
-          const int m = row0 + q * 16 + 4 * (lane >> 4) + ((lane & 8) ? 2 : 0);
+        if ((lane & 7) == 0) {      // lane 16 gq (rows 0, 2) and 16 gq + 8 (rows 1, 3)
+          const int m = row0 + q * 16 + 4 * (lane >> 4) + ((lane & 8) ? 1 : 0);
 #pragma unroll
-          for (int e = 0; e < 2; ++e) g.amax_part[(size_t)(m + e) * ngroups + ng] = amax[jq][e];
+          for (int e = 0; e < 2; ++e) g.amax_part[(size_t)(m + 2 * e) * ngroups + ng] = amax[jq][e];
         }
       }
     }

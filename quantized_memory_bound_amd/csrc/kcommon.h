@@ -42,8 +42,8 @@ struct GateUpArgs {
   const float* wscales;     // FP8: [2][I] per-row scales
   const uint8_t* wbscales;  // NVFP4: block-scale groups
   const float* tscales;     // NVFP4: blob header s_gate, s_up
-  float* h32;               // FP8 / NVFP4 down modes: [ngroups][Mpad][8 T] (each workgroup's
-                            // columns of h form one contiguous block)
+  float* h32;               // FP8 / NVFP4 down modes: [I / 8][Mpad][8]: each 8-column tile
+                            // of h is one contiguous [row][8] block
   uint16_t* hb;             // bf16(h), fragment order (BF16-down mode)
   uint16_t* tap_hb;         // optional plain [M][I] copy of bf16(h) (BF16-down mode)
   float* amax_part;         // [Mpad][ngroups] max |h| of each row over each workgroup's columns

@@ -130,7 +130,7 @@ __global__ __launch_bounds__(kThreads) void k_xquant(const uint16_t* __restrict_
 // receive the plain [M][I] codes and [M] scales.
 __global__ __launch_bounds__(kThreads) void k_requant(const float* __restrict__ h32,
                                                       const float* __restrict__ amax_part, int ngroups, int M,
-                                                      int Mpad, int I, int W, uint8_t* __restrict__ hq,
+                                                      int Mpad, int I, uint8_t* __restrict__ hq,
                                                       float* __restrict__ sh, uint8_t* __restrict__ tap_q,
                                                       float* __restrict__ tap_s) {
   __shared__ float s_max[kWaves];
@@ -144,12 +144,11 @@ __global__ __launch_bounds__(kThreads) void k_requant(const float* __restrict__ 
     return;
   }
   // this thread's 4 values of h are requested before the row maximum, so the
-  // two loads are in flight together.  h32 holds each gate/up workgroup's W
-  // columns as one [Mpad][W] block; 4 consecutive columns never straddle two
-  // blocks (W is a multiple of 8).
+  // two loads are in flight together.  h32 holds each 8-column tile of h as
+  // one [Mpad][8] block; 4 consecutive columns (k % 4 == 0) lie in one tile.
   const int k = (xb * kThreads + threadIdx.x) * 4;
   const bool has = k < I;
-  const v4f v = has ? *(const v4f*)(h32 + ((size_t)(k / W) * Mpad + m) * W + k % W) : v4f{0.f, 0.f, 0.f, 0.f};
+  const v4f v = has ? *(const v4f*)(h32 + ((size_t)(k / 8) * Mpad + m) * 8 + k % 8) : v4f{0.f, 0.f, 0.f, 0.f};
   float a = 0.0f;
   for (int g = threadIdx.x; g < ngroups; g += kThreads) a = fmaxf(a, amax_part[(size_t)m * ngroups + g]);
   a = wave_max(a);
@@ -215,7 +214,7 @@ int launch_forward(const Plan& p, const FwdArgs& a) {
   if (!bf16_down) {
     hipLaunchKernelGGL(k_requant, dim3(tile_row_grid(p.Mpad / 16, (p.inter + 1023) / 1024)), dim3(kThreads), 0, st,
                        h32, amax_part,
-                       p.ngroups1, p.M, p.Mpad, p.inter, 8 * p.T1, hq, sh, (uint8_t*)a.taps.h_out,
+                       p.ngroups1, p.M, p.Mpad, p.inter, hq, sh, (uint8_t*)a.taps.h_out,
                        (float*)a.taps.h_scales);
     e = hipGetLastError();
     if (e != hipSuccess) return (int)e;

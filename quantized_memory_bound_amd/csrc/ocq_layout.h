@@ -179,7 +179,7 @@ inline Plan make_plan(int M, int hidden, int inter, int prec) {
   p.off_xq = o;   o = align_up(o + Mp * hidden);
   p.off_sx = o;   o = align_up(o + Mp * 4);
   p.off_amax = o; o = align_up(o + (size_t)p.ngroups1 * Mp * 4);   // per-workgroup row maxima of |h|
-  p.off_h32 = o;  o = align_up(o + (prec == kFP8DownBF16 ? 0 : Mp * inter * 4));   // [ngroups1][Mpad][8 T1]
+  p.off_h32 = o;  o = align_up(o + (prec == kFP8DownBF16 ? 0 : Mp * inter * 4));   // [inter / 8][Mpad][8]
   p.off_hq = o;   o = align_up(o + (prec == kFP8DownBF16 ? 0 : Mp * inter));
   p.off_hb = o;   o = align_up(o + (prec == kFP8DownBF16 ? Mp * inter * 2 : 0));
   p.off_sh = o;   o = align_up(o + Mp * 4);

@@ -144,6 +144,7 @@ hipError_t go_mt(const DownArgs& d, int MT, int T, int grid, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_down(const Plan& p, const DownArgs& d, hipStream_t st) {
+  if (p.lg2) return launch_down_large(p, d, st);
   const int grid = p.n_mb2 * p.ngroups2;
   if (p.prec == kFP8) return go_mt<kB_FP8>(d, p.MT2, p.T2, grid, st);
   if (p.prec == kFP8DownBF16) return go_mt<kB_BF16>(d, p.MT2, p.T2, grid, st);

@@ -229,6 +229,7 @@ hipError_t go_mt(const GateUpArgs& g, int MT, int T, int grid, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_gateup(const Plan& p, const GateUpArgs& g, hipStream_t st) {
+  if (p.lg1) return launch_gateup_large(p, g, st);
   const int grid = p.ngroups1 * p.n_mblocks;
   if (p.prec == kFP8) return go_mt<kB_FP8_F16, false>(g, p.MT, p.T1, grid, st);
   if (p.prec == kFP8DownBF16) return go_mt<kB_FP8_F16, true>(g, p.MT, p.T1, grid, st);

@@ -1,0 +1,441 @@
+// LDS-tiled GEMMs for many rows (large verify batches).
+//
+// With several 208-row m-blocks the skinny kernels pull the activations
+// through every CU once per small weight group.  Here a workgroup owns RM
+// m-tiles x RT weight tiles over the whole input range and both operands pass
+// through LDS once per workgroup:
+//
+//   * a stage is UPS 1 KB units (16 B per lane of a fragment) of every m-tile
+//     and every weight tile; stages stream into an NSTG-deep LDS ring with
+//     direct-to-LDS loads, every wave issuing a fixed share, so the buffering
+//     costs no registers;
+//   * one workgroup barrier per stage: before it each wave waits until its own
+//     loads of the stage have landed (a fixed count per wave), after it every
+//     wave reads its MTW m-tiles x TW tiles of the stage from LDS, converts
+//     E4M3 to fp16 in registers where needed and runs the MFMAs;
+//   * KW waves share each output tile and split every stage's unit positions
+//     (KW > 1: one LDS reduction after the loop, fixed order).
+//
+// Gate/up: E4M3 weights x E4M3 activations through MFMA 16x16x32 f16 (exact
+// products, fp32 sums); the activations arrive as fp16 values of their codes
+// (written so by the x quantization), which saves the four waves that share
+// an m-tile converting it each,
+// then SiLU(gate) * up, stored as by the skinny gate/up epilogue (fp32 h and
+// per-row partial maxima for the E4M3 / NVFP4 down modes, bf16(h) in fragment
+// order for the BF16 down mode).  Down, BF16 mode (a layer kept at higher
+// precision: "OCRia 推理栈：单卡 B200 提速近 10 倍", section "Reducing the data
+// moved: workload-aware quantization"): bf16(h) x bf16 weights through MFMA
+// 16x16x32 bf16, y = bf16(Y).
+#include <type_traits>
+
+#include "gemm_core.h"
+
+namespace ocq {
+namespace {
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// s_waitcnt for vector-memory count <= N only (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14; expcnt 6:4 and lgkmcnt 11:8 left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Geometry of one LDS-tiled kernel.  BF: weight format (kB_FP8_F16: E4M3
+// codes, two MFMA sub-steps per unit; kB_BF16: one).  A16: the activations
+// are 16-bit values in fragment order (one unit per sub-step: AU units per
+// weight unit) rather than E4M3 codes.  NSTG: ring depth in stages.
+template <int BF_, bool A16_, int RM_, int RT_, int WM_, int WT_, int KW_, int UPS_, int NSTG_>
+struct Lg {
+  static constexpr int BF = BF_, RM = RM_, RT = RT_, WM = WM_, WT = WT_, KW = KW_, UPS = UPS_, NSTG = NSTG_;
+  static constexpr bool A16 = A16_;
+  static constexpr int NW = WM * WT * KW;
+  static constexpr int MTW = (RM + WM - 1) / WM;     // m-tiles per wave (the last may be padding)
+  static constexpr int TW = RT / WT;                 // weight tiles per wave
+  static constexpr int SUB = BF == kB_BF16 ? 1 : 2;  // MFMA sub-steps (32 inputs each) per weight unit
+  static constexpr int AU = A16 ? SUB : 1;           // activation units per weight unit
+  static constexpr int AW = WM * MTW * AU;           // activation units per unit position
+  static constexpr int UT = AW + RT;                 // units per unit position: activations, then weights
+  static constexpr int NU = UPS * UT;                // units per stage
+  static constexpr int PW = (NU + NW - 1) / NW;      // loads per wave per stage (waves < FULL) ...
+  static constexpr int FULL = NU - (PW - 1) * NW;    // ... the others PW - 1
+  static constexpr int UPC = 4 / SUB;                // weight units per 128-input chunk
+  static constexpr int SPC = UPC / UPS;              // stages per chunk
+  static constexpr int UPK = UPS / KW;               // unit positions of a stage per K-wave
+  static constexpr int A_BLK = A16 ? 4096 : 2048;    // activation bytes per (m-tile, chunk)
+  static constexpr int LDS = NSTG * NU * 1024;
+  static constexpr int THREADS = 64 * NW;
+  static_assert(BF == kB_FP8_F16 || (BF == kB_BF16 && A16), "formats");
+  static_assert(RT % WT == 0, "weight tiles split evenly over the wave columns");
+  static_assert(UPC % UPS == 0 && UPS % KW == 0 && SPC % 2 == 0, "stage and K-wave split of a chunk");
+  static_assert(NSTG >= 2 && PW >= 2 && (NSTG - 1) * PW < 64, "outstanding loads within the vmcnt range");
+  static_assert((KW - 1) * WM * WT * MTW * TW * 1024 <= LDS, "reduction fits the ring");
+  static_assert(LDS <= 160 * 1024, "LDS of one CU");
+};
+
+// Issue this wave's loads of stage s into `slot`.  a: activation block of the
+// workgroup's first m-tile (+ lane * 16), nva: m-tiles that exist (later ones
+// reload the last; their results are dropped); w: weight tile 0 (+ lane * 16).
+// Unit x of the stage goes to slot + x KB: unit position x / UT, then
+// (m-tile, activation unit) or weight tile by x % UT.
+template <class G>
+__device__ __forceinline__ void lg_issue(const uint8_t* a, int nva, size_t a_mt, const uint8_t* w, size_t w_tile,
+                                         int s, uint8_t* slot, int wave) {
+  const int c = s / G::SPC, u0 = (s % G::SPC) * G::UPS;
+#pragma unroll
+  for (int q = 0; q < G::PW; ++q) {
+    const int x = wave + q * G::NW;   // wave-uniform
+    if (q == G::PW - 1 && x >= G::NU) break;
+    const int uu = x / G::UT, y = x % G::UT;
+    const uint8_t* src;
+    if (y < G::AW) {
+      const int mt = y / G::AU < nva ? y / G::AU : nva - 1;
+      src = a + mt * a_mt + (size_t)c * G::A_BLK + ((u0 + uu) * G::AU + y % G::AU) * 1024;
+    } else {
+      src = w + (y - G::AW) * w_tile + (size_t)c * Fmt<G::BF>::kGlobal + (u0 + uu) * 1024;
+    }
+    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(slot + x * 1024), 16, 0, 0);
+  }
+}
+
+// wait until at most K stages of this wave's loads are outstanding
+template <class G, int K>
+__device__ __forceinline__ void lg_wait(bool full) {
+  if (full) wait_vm<K * G::PW>();
+  else wait_vm<K * (G::PW - 1)>();
+}
+
+// Operand registers of one piece of a wave's work: its MTW activation
+// units and (once per stage) its TW weight units.  A piece is one sub-step
+// for 16-bit activations (units hold one sub-step each), else a whole unit.
+template <class G>
+struct LgFrag {
+  v4i a[G::MTW];
+};
+template <class G>
+struct LgWFrag {
+  v4i b[G::TW];
+};
+
+// LDS reads of piece qa of this wave's unit position in the stage at `base`
+// (lane offset included)
+template <class G>
+__device__ __forceinline__ void lg_read_a(LgFrag<G>& f, const uint8_t* base, int wm, int kw, int qa) {
+  const uint8_t* ub = base + (size_t)kw * G::UT * 1024;
+#pragma unroll
+  for (int j = 0; j < G::MTW; ++j) f.a[j] = *(const v4i*)(ub + (size_t)((wm * G::MTW + j) * G::AU + qa) * 1024);
+}
+template <class G>
+__device__ __forceinline__ void lg_read_b(LgWFrag<G>& f, const uint8_t* base, int wt, int kw) {
+  const uint8_t* ub = base + (size_t)kw * G::UT * 1024;
+#pragma unroll
+  for (int t = 0; t < G::TW; ++t) f.b[t] = *(const v4i*)(ub + (size_t)(G::AW + wt * G::TW + t) * 1024);
+}
+
+// MFMAs of one piece.  A lane's 16 B of a weight unit: E4M3 codes of two
+// sub-steps (bytes 0-7, 8-15) or bf16 values of one; 16-bit activations hold
+// one sub-step per unit, E4M3 ones two like the weights.  Both operands order
+// the inputs of a sub-step alike, so each sub-step is one MFMA over 32 inputs.
+template <class G>
+__device__ __forceinline__ void lg_mfma(const LgFrag<G>& fa, const LgWFrag<G>& fb, int qa,
+                                        v4f (&acc)[G::MTW][G::TW]) {
+  if constexpr (G::BF == kB_BF16) {
+#pragma unroll
+    for (int j = 0; j < G::MTW; ++j) {
+      const v8bf av = __builtin_bit_cast(v8bf, fa.a[j]);
+#pragma unroll
+      for (int t = 0; t < G::TW; ++t)
+        acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(v8bf, fb.b[t]), acc[j][t], 0, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int ii = 0; ii < (G::A16 ? 1 : G::SUB); ++ii) {
+      const int i = G::A16 ? qa : ii;
+      v8h bv[G::TW];
+#pragma unroll
+      for (int t = 0; t < G::TW; ++t) bv[t] = e4m3x8_to_f16((uint32_t)fb.b[t][2 * i], (uint32_t)fb.b[t][2 * i + 1]);
+#pragma unroll
+      for (int j = 0; j < G::MTW; ++j) {
+        v8h av;
+        if constexpr (G::A16) av = __builtin_bit_cast(v8h, fa.a[j]);
+        else av = e4m3x8_to_f16((uint32_t)fa.a[j][2 * i], (uint32_t)fa.a[j][2 * i + 1]);
+#pragma unroll
+        for (int t = 0; t < G::TW; ++t)
+          acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv[t], acc[j][t], 0, 0, 0);
+      }
+    }
+  }
+}
+
+// acc over all NS stages (NS even).  All NSTG slots are filled up front;
+// after the barrier of stage s + 1 every wave has finished its LDS reads of
+// stage s, so stage s + NSTG goes into that slot.  Stage indices past the
+// last are clamped (the loads repeat the last stage into a slot whose reads
+// are over, and the reads after the last stage fetch registers nobody uses),
+// so every wave has the same number of loads outstanding at each wait.
+// Register ping-pong: the LDS reads of the next piece are issued before the
+// MFMAs of the current one, so after each barrier the matrix cores have work
+// that does not depend on the reads just issued.  On return no load of the
+// wave is outstanding.
+template <class G>
+__device__ __forceinline__ void lg_mainloop(const uint8_t* a, int nva, size_t a_mt, const uint8_t* w, size_t w_tile,
+                                            int NS, uint8_t* lds, int wave, int wm, int wt, int kw,
+                                            v4f (&acc)[G::MTW][G::TW]) {
+  constexpr int NP = G::A16 ? G::SUB : 1;   // pieces per stage
+  static_assert(G::UPK == 1, "one unit position per wave and stage");
+  const int lane = threadIdx.x & 63;
+  const bool full = wave < G::FULL;
+  auto slot = [&](int s) { return lds + (size_t)(s % G::NSTG) * G::NU * 1024 + lane * 16; };
+  auto issue = [&](int s) {
+    lg_issue<G>(a, nva, a_mt, w, w_tile, s < NS ? s : NS - 1, lds + (size_t)(s % G::NSTG) * G::NU * 1024, wave);
+  };
+#pragma unroll
+  for (int s = 0; s < G::NSTG; ++s) issue(s);
+  lg_wait<G, G::NSTG - 1>(full);
+  lds_barrier();
+  // lgkmcnt(0) through the builtin as well: the compiler's wait tracking
+  // does not see the one inside the barrier, and would otherwise treat
+  // earlier scalar loads as pending in the loop and wait for every LDS read
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  LgFrag<G> fa[2];
+  LgWFrag<G> fb[2];
+  lg_read_a<G>(fa[0], slot(0), wm, kw, 0);
+  lg_read_b<G>(fb[0], slot(0), wt, kw);
+  // one stage with B buffer E (compile-time), A buffers fixed per piece when
+  // a stage has two pieces, else alternating with the stage
+  auto stage = [&](int s, auto ec) {
+    constexpr int E = decltype(ec)::value;
+#pragma unroll
+    for (int q = 0; q < NP; ++q) {
+      const int cur = NP == 2 ? q : E;
+      if (q + 1 < NP) {
+        lg_read_a<G>(fa[1 - cur], slot(s), wm, kw, q + 1);
+      } else {   // also after the last stage: no branch, so no conservative wait at a join
+        lg_wait<G, G::NSTG - 2>(full);
+        lds_barrier();
+        issue(s + G::NSTG);
+        lg_read_a<G>(fa[1 - cur], slot(s + 1), wm, kw, 0);
+        lg_read_b<G>(fb[1 - E], slot(s + 1), wt, kw);
+      }
+      // fences: the compiler would otherwise sink the reads to their uses
+      __builtin_amdgcn_sched_barrier(0);
+      lg_mfma<G>(fa[cur], fb[E], q, acc);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  for (int s = 0; s < NS; s += 2) {
+    stage(s, std::integral_constant<int, 0>{});
+    stage(s + 1, std::integral_constant<int, 1>{});
+  }
+  wait_vm<0>();
+}
+
+// Sum the KW partial tiles into the kw = 0 waves in a fixed order, reusing
+// the ring once every wave has finished reading it.
+template <class G>
+__device__ __forceinline__ void lg_reduce(uint8_t* lds, int wmt, int kw, v4f (&acc)[G::MTW][G::TW]) {
+  if constexpr (G::KW > 1) {
+    const int lane = threadIdx.x & 63;
+    v4f* red = (v4f*)lds;
+    auto at = [&](int k, int j, int t) { return (((k * G::WM * G::WT + wmt) * G::MTW + j) * G::TW + t) * 64 + lane; };
+    lds_barrier();
+    if (kw > 0) {
+#pragma unroll
+      for (int j = 0; j < G::MTW; ++j)
+#pragma unroll
+        for (int t = 0; t < G::TW; ++t) red[at(kw - 1, j, t)] = acc[j][t];
+    }
+    lds_barrier();
+    if (kw == 0) {
+#pragma unroll
+      for (int k = 1; k < G::KW; ++k)
+#pragma unroll
+        for (int j = 0; j < G::MTW; ++j)
+#pragma unroll
+          for (int t = 0; t < G::TW; ++t) acc[j][t] += red[at(k - 1, j, t)];
+    }
+  }
+}
+
+// workgroup -> (m-block, column group); groups shared by the m-blocks are
+// numbered 8 apart (one XCD under round-robin placement) when possible
+__device__ __forceinline__ void lg_block(int n_mb, int ngroups, int& mb, int& ng) {
+  const int b = blockIdx.x;
+  if (ngroups % 8 == 0) {
+    const int q = b >> 3;
+    mb = q % n_mb;
+    ng = (q / n_mb) * 8 + (b & 7);
+  } else {
+    mb = b % n_mb;
+    ng = b / n_mb;
+  }
+}
+
+// ---------------------------------------------------------------- gate/up
+
+template <class G, bool BF16H>
+__global__ __launch_bounds__(G::THREADS) void lg_gateup(GateUpArgs g) {
+  extern __shared__ float lds_f[];
+  uint8_t* lds = (uint8_t*)lds_f;
+  const int ngroups = (g.I / 8) / G::RT;
+  int mb, ng;
+  lg_block(g.n_mb, ngroups, mb, ng);
+  const int C = g.H / kChunk;
+  const int row0 = mb * G::RM * 16;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave % G::WM, wt = (wave / G::WM) % G::WT, kw = wave / (G::WM * G::WT);
+  const int left = g.Mpad / 16 - row0 / 16;
+  const int nva = left < G::RM ? left : G::RM;
+  const size_t wtile = (size_t)C * Fmt<G::BF>::kGlobal;
+  v4f acc[G::MTW][G::TW];
+#pragma unroll
+  for (int j = 0; j < G::MTW; ++j)
+#pragma unroll
+    for (int t = 0; t < G::TW; ++t) acc[j][t] = v4f{0.f, 0.f, 0.f, 0.f};
+  lg_mainloop<G>(g.xq + (size_t)(row0 / 16) * C * G::A_BLK + lane * 16, nva, (size_t)C * G::A_BLK,
+                 g.wcodes + (size_t)ng * G::RT * wtile + lane * 16, wtile, C * G::SPC, lds, wave, wm, wt, kw, acc);
+  lg_reduce<G>(lds, wave % (G::WM * G::WT), kw, acc);
+  if (kw > 0) return;
+
+  // epilogue: m-tiles wm*MTW + j (those that exist) x tiles tile0 + t.  The
+  // pairing of gate and up lanes and the h32 layout ([tile][row][8]) are
+  // those of the skinny gate/up epilogue.
+  const int tile0 = ng * G::RT + wt * G::TW;
+  const int r = lane & 15, c = r & 7;
+  const bool lo = r < 8;
+  float cg[G::TW], cu[G::TW];
+#pragma unroll
+  for (int t = 0; t < G::TW; ++t) {
+    const int n = (tile0 + t) * 8 + c;
+    cg[t] = g.wscales[n];
+    cu[t] = g.wscales[g.I + n];
+  }
+  const int ngp = ngroups * G::WT;   // partial row maxima per row
+#pragma unroll
+  for (int j = 0; j < G::MTW; ++j) {
+    const int mt = wm * G::MTW + j;
+    if (mt >= nva) break;
+    const int m_base = row0 + mt * 16 + 4 * (lane >> 4);
+    float xs[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xs[i] = g.sx[m_base + i];
+    float amax[2] = {0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < G::TW; ++t) {
+      const int tile = tile0 + t, n = tile * 8 + c;
+      const v4f& v = acc[j][t];
+      const float p0 = dpp<0x128>(lo ? v[1] : v[0]);
+      const float p1 = dpp<0x128>(lo ? v[3] : v[2]);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int i = 2 * e + (lo ? 0 : 1);
+        const float gv = lo ? v[i] : (e ? p1 : p0);
+        const float uv = lo ? (e ? p1 : p0) : v[i];
+        const float hv = silu(gv * xs[i] * cg[t]) * (uv * xs[i] * cu[t]);
+        const int m = m_base + i;
+        if constexpr (BF16H) {
+          const uint16_t hb = (uint16_t)bf16_bits(hv);
+          g.hb[frag_off16(m, n, g.I / 128)] = hb;
+          if (g.tap_hb && m < g.M) g.tap_hb[(size_t)m * g.I + n] = hb;
+        } else {
+          g.h32[((size_t)tile * g.Mpad + m) * 8 + c] = hv;
+          amax[e] = fmaxf(amax[e], fabsf(hv));
+        }
+      }
+    }
+    if constexpr (!BF16H) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) amax[e] = max8(amax[e]);
+      if ((lane & 7) == 0) {   // lanes 16 gq (rows 0, 2) and 16 gq + 8 (rows 1, 3)
+        const int m = m_base + ((lane & 8) ? 1 : 0);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) g.amax_part[(size_t)(m + 2 * e) * ngp + ng * G::WT + wt] = amax[e];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- down, BF16 mode
+
+template <class G>
+__global__ __launch_bounds__(G::THREADS) void lg_down_bf16(DownArgs d) {
+  extern __shared__ float lds_f[];
+  uint8_t* lds = (uint8_t*)lds_f;
+  const int ngroups = (d.H / 16) / G::RT;
+  int mb, ng;
+  lg_block(d.n_mb, ngroups, mb, ng);
+  const int C = d.I / kChunk;
+  const int row0 = mb * G::RM * 16;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave % G::WM, wt = (wave / G::WM) % G::WT, kw = wave / (G::WM * G::WT);
+  const int left = (d.M + 15) / 16 - row0 / 16;
+  const int nva = left < G::RM ? left : G::RM;
+  const size_t wtile = (size_t)C * Fmt<G::BF>::kGlobal;
+  v4f acc[G::MTW][G::TW];
+#pragma unroll
+  for (int j = 0; j < G::MTW; ++j)
+#pragma unroll
+    for (int t = 0; t < G::TW; ++t) acc[j][t] = v4f{0.f, 0.f, 0.f, 0.f};
+  lg_mainloop<G>((const uint8_t*)d.A + (size_t)(row0 / 16) * C * G::A_BLK + lane * 16, nva, (size_t)C * G::A_BLK,
+                 d.wcodes + (size_t)ng * G::RT * wtile + lane * 16, wtile, C * G::SPC, lds, wave, wm, wt, kw, acc);
+  lg_reduce<G>(lds, wave % (G::WM * G::WT), kw, acc);
+  if (kw > 0) return;
+  const int r = lane & 15;
+#pragma unroll
+  for (int j = 0; j < G::MTW; ++j) {
+    const int mt = wm * G::MTW + j;
+    if (mt >= nva) break;
+#pragma unroll
+    for (int t = 0; t < G::TW; ++t) {
+      const int col = (ng * G::RT + wt * G::TW + t) * 16 + r;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = row0 + mt * 16 + 4 * (lane >> 4) + i;
+        if (m < d.M) d.y[(size_t)m * d.H + col] = (uint16_t)bf16_bits(acc[j][t][i]);
+      }
+    }
+  }
+}
+
+template <class G, class Arg>
+hipError_t lg_launch(void (*fn)(Arg), int grid, const Arg& arg, hipStream_t st, bool& attr) {
+  if (!attr) {   // idempotent; a race only repeats the call
+    hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(G::THREADS), G::LDS, st, arg);
+  return hipGetLastError();
+}
+
+// gate/up: 13 m-tiles x 12 tiles per workgroup; 2 x 4 waves of 7 m-tiles x 3
+// tiles, one weight unit position per stage (64 inputs), three stages (120 KB)
+using GUL = Lg<kB_FP8_F16, true, kLgRM, kLgRT1, 2, kLgWT1, 1, 1, 3>;
+// down: 13 m-tiles x 4 tiles per workgroup; 2 x 2 waves of 7 m-tiles x 2 tiles,
+// each pair of K-waves splitting the two unit positions of a stage (64
+// inputs), four stages (144 KB)
+using GDL = Lg<kB_BF16, true, kLgRM, kLgRT2, 2, 2, 2, 2, 4>;
+
+}  // namespace
+
+hipError_t launch_gateup_large(const Plan& p, const GateUpArgs& g, hipStream_t st) {
+  if ((p.inter / 8) % GUL::RT || p.hidden % kChunk) return hipErrorInvalidValue;
+  const int grid = p.n_mblocks * ((p.inter / 8) / GUL::RT);
+  if (p.prec == kFP8DownBF16) {
+    static bool attr = false;
+    return lg_launch<GUL>(lg_gateup<GUL, true>, grid, g, st, attr);
+  }
+  static bool attr = false;
+  return lg_launch<GUL>(lg_gateup<GUL, false>, grid, g, st, attr);
+}
+
+hipError_t launch_down_large(const Plan& p, const DownArgs& d, hipStream_t st) {
+  if ((p.hidden / 16) % GDL::RT || p.inter % kChunk || p.prec != kFP8DownBF16) return hipErrorInvalidValue;
+  const int grid = p.n_mb2 * ((p.hidden / 16) / GDL::RT);
+  static bool attr = false;
+  return lg_launch<GDL>(lg_down_bf16<GDL>, grid, d, st, attr);
+}
+
+}  // namespace ocq

@@ -63,6 +63,8 @@ struct DownArgs {
 
 hipError_t launch_gateup(const Plan& p, const GateUpArgs& g, hipStream_t st);
 hipError_t launch_down(const Plan& p, const DownArgs& d, hipStream_t st);
+hipError_t launch_gateup_large(const Plan& p, const GateUpArgs& g, hipStream_t st);
+hipError_t launch_down_large(const Plan& p, const DownArgs& d, hipStream_t st);
 
 // ---------------------------------------------------------------- scalar codecs
 

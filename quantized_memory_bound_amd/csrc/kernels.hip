@@ -47,11 +47,12 @@ inline int tile_row_grid(int mtiles, int nrest) { return (mtiles + 7) / 8 * 128 
 // One workgroup per row (all 256 threads), so the row's loads are all in
 // flight at once; |x| max reduced over the wavefront, then across the four
 // waves in LDS.  Codes go to the fragment-ordered operand buffer (8
-// consecutive inputs = 8 contiguous bytes there); rows M..Mpad-1 are written
-// as zero codes with scale 0.  tap_q / tap_s (nullable) receive the plain
+// consecutive inputs = 8 contiguous bytes there), or with f16 set their exact
+// fp16 values in the 16-bit fragment order (16 contiguous bytes); rows
+// M..Mpad-1 are written as zero codes with scale 0.  tap_q / tap_s (nullable) receive the plain
 // [M][H] codes and [M] scales.
 __global__ __launch_bounds__(kThreads) void k_xquant(const uint16_t* __restrict__ x, int M, int H, int Mpad,
-                                                     uint8_t* __restrict__ xq, float* __restrict__ sx,
+                                                     uint8_t* __restrict__ xq, int f16, float* __restrict__ sx,
                                                      uint8_t* __restrict__ tap_q, float* __restrict__ tap_s) {
   __shared__ float s_max[kWaves];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -59,7 +60,10 @@ __global__ __launch_bounds__(kThreads) void k_xquant(const uint16_t* __restrict_
   if (!tile_row_of(blockIdx.x, Mpad / 16, m, rest)) return;
   const int C = H / 128;
   if (m >= M) {                                     // padding row: zero codes, zero scale
-    for (int k = threadIdx.x * 8; k < H; k += kThreads * 8) *(v2u*)(xq + frag_off8(m, k, C)) = v2u{0u, 0u};
+    for (int k = threadIdx.x * 8; k < H; k += kThreads * 8) {
+      if (f16) *(v4i*)((uint16_t*)xq + frag_off16(m, k, C)) = v4i{0, 0, 0, 0};
+      else *(v2u*)(xq + frag_off8(m, k, C)) = v2u{0u, 0u};
+    }
     if (threadIdx.x == 0) sx[m] = 0.0f;
     return;
   }
@@ -109,7 +113,8 @@ __global__ __launch_bounds__(kThreads) void k_xquant(const uint16_t* __restrict_
           out[q >> 1] |= (c0 | (c1 << 8)) << (16 * (q & 1));
         }
       }
-      *(v2u*)(xq + frag_off8(m, k, C)) = v2u{out[0], out[1]};
+      if (f16) *(v8h*)((uint16_t*)xq + frag_off16(m, k, C)) = e4m3x8_to_f16(out[0], out[1]);
+      else *(v2u*)(xq + frag_off8(m, k, C)) = v2u{out[0], out[1]};
       if (tap_q) *(v2u*)(tap_q + (size_t)m * H + k) = v2u{out[0], out[1]};
     }
   }
@@ -192,7 +197,7 @@ int launch_forward(const Plan& p, const FwdArgs& a) {
 
   stage(a, 0);
   const bool bf16_down = p.prec == kFP8DownBF16;
-  hipLaunchKernelGGL(k_xquant, dim3(tile_row_grid(p.Mpad / 16, 1)), dim3(kThreads), 0, st, a.x, p.M, p.hidden, p.Mpad, xq, sx,
+  hipLaunchKernelGGL(k_xquant, dim3(tile_row_grid(p.Mpad / 16, 1)), dim3(kThreads), 0, st, a.x, p.M, p.hidden, p.Mpad, xq, p.lg1, sx,
                      (uint8_t*)a.taps.x_codes, (float*)a.taps.x_scales);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return (int)e;

@@ -107,6 +107,14 @@ inline BlobLayout blob_layout(int hidden, int inter, int prec) {
 constexpr int kMTChoices[] = {1, 2, 4, 7, 13};
 constexpr int kMTMax = 13;
 
+// LDS-tiled kernels for many rows (both projections' m-blocks are kLgRM
+// m-tiles); chosen from kLgMinRows rows on
+constexpr int kLgRM = 13;        // m-tiles per workgroup
+constexpr int kLgRT1 = 12;       // gate/up: interleaved tiles per workgroup
+constexpr int kLgWT1 = 4;        // gate/up: wave columns (partial row maxima per workgroup)
+constexpr int kLgRT2 = 4;        // down: output tiles per workgroup
+constexpr int kLgMinRows = 384;
+
 struct Plan {
   int M, hidden, inter, prec;
   int Mpad;        // rows of every activation buffer (covers both projections' m-blocks)
@@ -115,6 +123,9 @@ struct Plan {
   // down kernel: n_mb2 m-blocks of MT2 m-tiles x ngroups2 groups of T2 tiles,
   // every workgroup over the whole input range
   int MT2, n_mb2, T2, ngroups2;
+  // LDS-tiled kernels selected (gate/up, down); then ngroups1 counts the
+  // partial row maxima per row (workgroups x wave columns)
+  int lg1, lg2;
   // workspace offsets (xq, hq, hb are fragment-ordered operand buffers of Mpad rows)
   size_t off_xq, off_sx, off_amax, off_h32, off_hq, off_hb, off_sh, total;
 };
@@ -171,12 +182,27 @@ inline Plan make_plan(int M, int hidden, int inter, int prec) {
   }
   p.ngroups1 = nt1 / p.T1;
   pick_down(p);
+  const bool many = M >= kLgMinRows;
+  p.lg1 = many && (prec == kFP8 || prec == kFP8DownBF16) && nt1 % kLgRT1 == 0 && hidden >= 256;
+  if (p.lg1) {
+    p.MT = kLgRM;
+    p.n_mblocks = (M + 16 * kLgRM - 1) / (16 * kLgRM);
+    p.T1 = kLgRT1;
+    p.ngroups1 = nt1 / kLgRT1 * kLgWT1;
+  }
+  p.lg2 = many && prec == kFP8DownBF16 && (hidden / 16) % kLgRT2 == 0 && inter >= 256;
+  if (p.lg2) {
+    p.MT2 = kLgRM;
+    p.T2 = kLgRT2;
+    p.n_mb2 = (M + 16 * kLgRM - 1) / (16 * kLgRM);
+    p.ngroups2 = hidden / 16 / kLgRT2;
+  }
   const int rows1 = p.n_mblocks * 16 * p.MT, rows2 = p.n_mb2 * 16 * p.MT2;
   p.Mpad = rows1 > rows2 ? rows1 : rows2;
   // workspace
   size_t Mp = p.Mpad;
   size_t o = 0;
-  p.off_xq = o;   o = align_up(o + Mp * hidden);
+  p.off_xq = o;   o = align_up(o + Mp * hidden * (p.lg1 ? 2 : 1));   // E4M3 codes, or their fp16 values
   p.off_sx = o;   o = align_up(o + Mp * 4);
   p.off_amax = o; o = align_up(o + (size_t)p.ngroups1 * Mp * 4);   // per-workgroup row maxima of |h|
   p.off_h32 = o;  o = align_up(o + (prec == kFP8DownBF16 ? 0 : Mp * inter * 4));   // [inter / 8][Mpad][8]

@@ -70,8 +70,10 @@ def compare(g, r, prec, rows=None, what=""):
     return check_y(sel(g["y"]), r["y"], what + " y")
 
 
+# the last two take the LDS-tiled kernels for many rows (E4M3 gate/up; BF16
+# down): 3 and 4 m-blocks of 208 rows with a ragged last block
 SMALL = [(256, 512, 1), (256, 512, 4), (384, 640, 17), (512, 1024, 37), (256, 768, 100), (128, 384, 208),
-         (256, 512, 300), (640, 384, 65)]
+         (256, 512, 300), (640, 384, 65), (256, 768, 420), (384, 1152, 640)]
 
 
 @pytest.mark.parametrize("prec", [0, 1, 2])

@@ -214,9 +214,11 @@ def main():
         torch.cuda.synchronize()
     ms_step = t_start.elapsed_time(t_end) / K
 
-    # --- gate/up kernel duration: the library's stage events around the
-    # gate/up launch of each step, steps enqueued behind a GPU spin
+    # --- gate/up kernel duration: stage events 1 and 2 are recorded by the
+    # gate/up launch itself (start and end of that kernel's execution); steps
+    # enqueued behind a GPU spin so they run back to back
     gu_ms = None
+    gu_how = None
     if not args.no_stage_events:
         Kr = min(256, args.steps)
         ga = [ev.create() for _ in range(Kr)]
@@ -230,6 +232,7 @@ def main():
         torch.cuda.synchronize()
         gu = [ev.elapsed_ms(a, b) for a, b in zip(ga, gb)]
         gu_ms = sum(gu) / len(gu)
+        gu_how = "start/end events of the gate/up launch, %d eager steps" % len(gu)
         for e in ga + gb:
             ev.destroy(e)
 
@@ -254,6 +257,7 @@ def main():
                     "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": traffic}
         roof["kernel"] = "k_gateup (gate/up GEMM + SiLU*up + per-token amax)"
         roof["us_per_launch"] = round(gu_ms * 1e3, 3)
+        roof["timing"] = gu_how
         roof["alg_bytes_per_launch"] = gbytes
         roof["alg_flops_per_launch"] = gflops
         roof["hbm_frac_at_this_duration"] = round(gbytes / (gu_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)

@@ -139,10 +139,14 @@ ocq_status ocq_check_blob(const void* packed_dev, size_t packed_bytes, int hidde
 /* Per-stage timing hook (profiling).  When set, every later ocq_mlp_forward
  * on this thread records events[i] (hipEvent_t passed as void*, owned by the
  * caller; NULL entries are skipped) on the call's stream at stage boundary i:
- *   0 before the x quantization, 1 before gate/up + SiLU, 2 after gate/up,
- *   3 before the down projection, 4 after the down projection.
- * count must be 5 to enable, 0 (or events == NULL) to disable.  The pointer
- * array is copied; the events must stay valid while the hook is set. */
+ *   0 before the x quantization, 1 start of the gate/up + SiLU kernel,
+ *   2 end of the gate/up kernel, 3 before the down projection, 4 after it.
+ * Events 1 and 2 are taken by the gate/up launch itself (the kernel's own
+ * start and end), so their difference is that kernel's execution time; the
+ * others are recorded on the stream between launches.  Not for use while the
+ * stream is being captured into a graph.  count must be 5 to enable, 0 (or
+ * events == NULL) to disable.  The pointer array is copied; the events must
+ * stay valid while the hook is set. */
 ocq_status ocq_set_stage_events(void* const* events, int count);
 
 /* Message for the last failure on this thread ("" if none). */

@@ -172,7 +172,7 @@ __global__ __launch_bounds__(64 * MS * KS) void ks_gateup(GateUpArgs g) {
 // ---------------------------------------------------------------- dispatch
 
 template <int BF, bool BF16H, int MT, int T, int MS, int KS, int D>
-hipError_t launch_ks(const GateUpArgs& g, int grid, hipStream_t st) {
+hipError_t launch_ks(const GateUpArgs& g, int grid, hipStream_t st, const LaunchEvents& ev) {
   constexpr int MTW = (MT + MS - 1) / MS;
   auto fn = ks_gateup<BF, MT, T, MS, KS, D, BF16H>;
   const size_t lds = (size_t)MS * KS * MTW * 256 * sizeof(float);
@@ -182,7 +182,7 @@ hipError_t launch_ks(const GateUpArgs& g, int grid, hipStream_t st) {
     if (e != hipSuccess) return e;
     attr = true;
   }
-  hipLaunchKernelGGL(fn, dim3(grid), dim3(64 * MS * KS), lds, st, g);
+  launch_kernel(fn, dim3(grid), dim3(64 * MS * KS), lds, st, ev, g);
   return hipGetLastError();
 }
 
@@ -193,47 +193,47 @@ hipError_t launch_ks(const GateUpArgs& g, int grid, hipStream_t st) {
 // unit (ks_mainloop_roll), which fits the 256 registers a wave has at two
 // waves per SIMD.
 template <int BF, bool BF16H, int MT, int T>
-hipError_t go(const GateUpArgs& g, int grid, hipStream_t st) {
+hipError_t go(const GateUpArgs& g, int grid, hipStream_t st, const LaunchEvents& ev) {
   constexpr int MS = MT >= 13 ? 2 : 1;
   constexpr int KS = 8 / MS;
   constexpr int MTW = (MT + MS - 1) / MS;
   const int C = g.H / kChunk;
-  if constexpr (MTW <= 4) return launch_ks<BF, BF16H, MT, T, MS, KS, 2>(g, grid, st);
-  else if (C == 4 * KS) return launch_ks<BF, BF16H, MT, T, MS, KS, -4>(g, grid, st);
-  else if (C == 8 * KS) return launch_ks<BF, BF16H, MT, T, MS, KS, -8>(g, grid, st);
-  else return launch_ks<BF, BF16H, MT, T, MS, KS, -1>(g, grid, st);
+  if constexpr (MTW <= 4) return launch_ks<BF, BF16H, MT, T, MS, KS, 2>(g, grid, st, ev);
+  else if (C == 4 * KS) return launch_ks<BF, BF16H, MT, T, MS, KS, -4>(g, grid, st, ev);
+  else if (C == 8 * KS) return launch_ks<BF, BF16H, MT, T, MS, KS, -8>(g, grid, st, ev);
+  else return launch_ks<BF, BF16H, MT, T, MS, KS, -1>(g, grid, st, ev);
 }
 
 template <int BF, bool BF16H, int MT>
-hipError_t go_t(const GateUpArgs& g, int T, int grid, hipStream_t st) {
+hipError_t go_t(const GateUpArgs& g, int T, int grid, hipStream_t st, const LaunchEvents& ev) {
   switch (T) {
-    case 1: return go<BF, BF16H, MT, 1>(g, grid, st);
-    case 2: return go<BF, BF16H, MT, 2>(g, grid, st);
-    case 3: return go<BF, BF16H, MT, 3>(g, grid, st);
+    case 1: return go<BF, BF16H, MT, 1>(g, grid, st, ev);
+    case 2: return go<BF, BF16H, MT, 2>(g, grid, st, ev);
+    case 3: return go<BF, BF16H, MT, 3>(g, grid, st, ev);
   }
   return hipErrorInvalidValue;
 }
 
 template <int BF, bool BF16H>
-hipError_t go_mt(const GateUpArgs& g, int MT, int T, int grid, hipStream_t st) {
+hipError_t go_mt(const GateUpArgs& g, int MT, int T, int grid, hipStream_t st, const LaunchEvents& ev) {
   switch (MT) {
-    case 1: return go_t<BF, BF16H, 1>(g, T, grid, st);
-    case 2: return go_t<BF, BF16H, 2>(g, T, grid, st);
-    case 4: return go_t<BF, BF16H, 4>(g, T, grid, st);
-    case 7: return go_t<BF, BF16H, 7>(g, T, grid, st);
-    case 13: return go_t<BF, BF16H, 13>(g, T, grid, st);
+    case 1: return go_t<BF, BF16H, 1>(g, T, grid, st, ev);
+    case 2: return go_t<BF, BF16H, 2>(g, T, grid, st, ev);
+    case 4: return go_t<BF, BF16H, 4>(g, T, grid, st, ev);
+    case 7: return go_t<BF, BF16H, 7>(g, T, grid, st, ev);
+    case 13: return go_t<BF, BF16H, 13>(g, T, grid, st, ev);
   }
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_gateup(const Plan& p, const GateUpArgs& g, hipStream_t st) {
-  if (p.lg1) return launch_gateup_large(p, g, st);
+hipError_t launch_gateup(const Plan& p, const GateUpArgs& g, hipStream_t st, const LaunchEvents& ev) {
+  if (p.lg1) return launch_gateup_large(p, g, st, ev);
   const int grid = p.ngroups1 * p.n_mblocks;
-  if (p.prec == kFP8) return go_mt<kB_FP8_F16, false>(g, p.MT, p.T1, grid, st);
-  if (p.prec == kFP8DownBF16) return go_mt<kB_FP8_F16, true>(g, p.MT, p.T1, grid, st);
-  return go_mt<kB_FP4_F16, false>(g, p.MT, p.T1, grid, st);
+  if (p.prec == kFP8) return go_mt<kB_FP8_F16, false>(g, p.MT, p.T1, grid, st, ev);
+  if (p.prec == kFP8DownBF16) return go_mt<kB_FP8_F16, true>(g, p.MT, p.T1, grid, st, ev);
+  return go_mt<kB_FP4_F16, false>(g, p.MT, p.T1, grid, st, ev);
 }
 
 }  // namespace ocq

@@ -400,13 +400,14 @@ __global__ __launch_bounds__(G::THREADS) void lg_down_bf16(DownArgs d) {
 }
 
 template <class G, class Arg>
-hipError_t lg_launch(void (*fn)(Arg), int grid, const Arg& arg, hipStream_t st, bool& attr) {
+hipError_t lg_launch(void (*fn)(Arg), int grid, const Arg& arg, hipStream_t st, bool& attr,
+                     const LaunchEvents& ev = LaunchEvents{}) {
   if (!attr) {   // idempotent; a race only repeats the call
     hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS);
     if (e != hipSuccess) return e;
     attr = true;
   }
-  hipLaunchKernelGGL(fn, dim3(grid), dim3(G::THREADS), G::LDS, st, arg);
+  launch_kernel(fn, dim3(grid), dim3(G::THREADS), G::LDS, st, ev, arg);
   return hipGetLastError();
 }
 
@@ -420,15 +421,15 @@ using GDL = Lg<kB_BF16, true, kLgRM, kLgRT2, 2, 2, 2, 2, 4>;
 
 }  // namespace
 
-hipError_t launch_gateup_large(const Plan& p, const GateUpArgs& g, hipStream_t st) {
+hipError_t launch_gateup_large(const Plan& p, const GateUpArgs& g, hipStream_t st, const LaunchEvents& ev) {
   if ((p.inter / 8) % GUL::RT || p.hidden % kChunk) return hipErrorInvalidValue;
   const int grid = p.n_mblocks * ((p.inter / 8) / GUL::RT);
   if (p.prec == kFP8DownBF16) {
     static bool attr = false;
-    return lg_launch<GUL>(lg_gateup<GUL, true>, grid, g, st, attr);
+    return lg_launch<GUL>(lg_gateup<GUL, true>, grid, g, st, attr, ev);
   }
   static bool attr = false;
-  return lg_launch<GUL>(lg_gateup<GUL, false>, grid, g, st, attr);
+  return lg_launch<GUL>(lg_gateup<GUL, false>, grid, g, st, attr, ev);
 }
 
 hipError_t launch_down_large(const Plan& p, const DownArgs& d, hipStream_t st) {

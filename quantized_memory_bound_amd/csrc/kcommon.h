@@ -1,5 +1,6 @@
 // Device-side building blocks shared by the ocq kernels (gfx950 / CDNA4).
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
@@ -61,9 +62,21 @@ struct DownArgs {
   int H, I, M, n_mb, ngroups;
 };
 
-hipError_t launch_gateup(const Plan& p, const GateUpArgs& g, hipStream_t st);
+// Events recorded by a launch itself at the kernel's start and end (nullable).
+struct LaunchEvents {
+  hipEvent_t start = nullptr, end = nullptr;
+};
+
+template <class K, class... Args>
+inline void launch_kernel(K fn, dim3 grid, dim3 block, size_t lds, hipStream_t st, const LaunchEvents& ev,
+                          Args... args) {
+  if (ev.start || ev.end) hipExtLaunchKernelGGL(fn, grid, block, (uint32_t)lds, st, ev.start, ev.end, 0, args...);
+  else hipLaunchKernelGGL(fn, grid, block, lds, st, args...);
+}
+
+hipError_t launch_gateup(const Plan& p, const GateUpArgs& g, hipStream_t st, const LaunchEvents& ev);
 hipError_t launch_down(const Plan& p, const DownArgs& d, hipStream_t st);
-hipError_t launch_gateup_large(const Plan& p, const GateUpArgs& g, hipStream_t st);
+hipError_t launch_gateup_large(const Plan& p, const GateUpArgs& g, hipStream_t st, const LaunchEvents& ev);
 hipError_t launch_down_large(const Plan& p, const DownArgs& d, hipStream_t st);
 
 // ---------------------------------------------------------------- scalar codecs

@@ -202,7 +202,6 @@ int launch_forward(const Plan& p, const FwdArgs& a) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return (int)e;
 
-  stage(a, 1);
   GateUpArgs g{};
   g.xq = xq; g.sx = sx;
   g.wcodes = a.blob + L.off_gu_codes;
@@ -212,9 +211,13 @@ int launch_forward(const Plan& p, const FwdArgs& a) {
   g.h32 = h32; g.hb = hb; g.amax_part = amax_part;
   g.tap_hb = bf16_down ? (uint16_t*)a.taps.h_out : nullptr;
   g.H = p.hidden; g.I = p.inter; g.M = p.M; g.n_mb = p.n_mblocks; g.Mpad = p.Mpad;
-  e = launch_gateup(p, g, st);
+  LaunchEvents gev;   // stage events 1 and 2 are taken by the gate/up launch itself
+  if (a.stage_events) {
+    gev.start = (hipEvent_t)a.stage_events[1];
+    gev.end = (hipEvent_t)a.stage_events[2];
+  }
+  e = launch_gateup(p, g, st, gev);
   if (e != hipSuccess) return (int)e;
-  stage(a, 2);
 
   if (!bf16_down) {
     hipLaunchKernelGGL(k_requant, dim3(tile_row_grid(p.Mpad / 16, (p.inter + 1023) / 1024)), dim3(kThreads), 0, st,

@@ -131,7 +131,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--workload", default="spec_verify_fp8")
+    ap.add_argument("--workload", default="spec_verify_fp8",
+                    help="a block workload (inputs.WORKLOADS) or a stack of blocks (inputs.STACKS)")
     ap.add_argument("--M", type=int, default=None, help="leading rows of the workload (NVFP4 sweep)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -153,6 +154,8 @@ def main():
     from quantized_memory_bound_amd import inputs as I
     from quantized_memory_bound_amd import ocq
 
+    if args.workload in I.STACKS:
+        return run_stack(args)
     cfg = I.WORKLOADS[args.workload]
     H, Iw, prec = cfg["hidden"], cfg["inter"], cfg["prec_mode"]
     inp = I.workload_inputs(args.workload, M=args.M)
@@ -290,6 +293,101 @@ def main():
         "tokens_per_s": round(tok_s, 1),
         "us_per_block": round(ms_step * 1e3, 3),
         "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def run_stack(args):
+    """A stack of blocks with a precision mode per layer: a step is one pass
+    of the whole stack (block l's output is block l+1's input).  Weight sets
+    of the stack are rotated (R x stack bytes >= 512 MB) and R steps replay as
+    one captured graph, as for one block."""
+    import numpy as np
+    import torch
+    from quantized_memory_bound_amd import inputs as I
+    from quantized_memory_bound_amd import ocq
+
+    cfg = I.STACKS[args.workload]
+    H, Iw, M, modes = cfg["hidden"], cfg["inter"], cfg["M"], list(cfg["modes"])
+    x_bits, layers = I.stack_inputs(args.workload)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    blobs0 = [ocq.pack_weights(wg, wu, wd, m) for (wg, wu, wd), m in zip(layers, modes)]
+    stack_bytes = sum(b.numel() for b in blobs0)
+    R = max(2, -(-2 * MALL_BYTES // stack_bytes))
+    sets = [blobs0] + [[b.clone() for b in blobs0] for _ in range(R - 1)]
+    x = torch.from_numpy(x_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    y = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(ocq.stack_workspace_bytes(M, H, Iw, modes), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step(i):
+        ocq.mlp_stack_forward(sets[i % R], modes, x, H, Iw, y=y, workspace=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    cs = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cs):
+        for i in range(R):
+            step(i)
+    for _ in range(2):
+        graph.replay()
+    torch.cuda.synchronize()
+    n_rep = max(1, -(-args.steps // R))
+    K = n_rep * R
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(n_rep):
+        graph.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / K
+
+    ab = sum(alg_bytes(M, H, Iw, m) for m in modes)
+    gbps = ab / (ms_step * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_info
+        from oracle import mlp as O
+        packed = [O.pack_block(wg, wu, wd, m) for (wg, wu, wd), m in zip(layers, modes)]
+        O.stack_forward(x_bits, packed)
+        reps, c0 = 0, time.perf_counter()
+        while True:
+            O.stack_forward(x_bits, packed)
+            reps += 1
+            if time.perf_counter() - c0 >= args.cpu_seconds:
+                break
+        dt = (time.perf_counter() - c0) / reps
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+        cpu = {"value": round(ab / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+               "sample": "whole stack, all %d rows, weights pre-packed, %d repetitions (%.2f s each)" % (M, reps, dt),
+               "tokens_per_s": round(M / dt, 1)}
+    names = {0: "fp8", 1: "fp8+bf16down", 2: "nvfp4"}
+    out = {
+        "metric": "achieved HBM GB/s (% of peak) + verified tokens/s per MLP stack (" + str(len(modes)) + " blocks)",
+        "value": round(gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "mode": "graph",
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "per layer: " + ",".join(names[m] for m in modes),
+        "data": "synthetic (seeded; shapes and distributions of the workload)",
+        "config": {"workload": args.workload, "hidden": H, "inter": Iw, "M": M, "layers": len(modes),
+                   "prec_modes": modes, "weight_sets_rotated": R, "alg_bytes_per_step": ab,
+                   "weight_bytes_per_step": stack_bytes},
+        "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "tokens_per_s": round(M / (ms_step * 1e-3), 1),
+        "us_per_step": round(ms_step * 1e3, 3),
+        "us_per_layer": round(ms_step * 1e3 / len(modes), 3),
+        "roofline": None,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -131,6 +131,34 @@ ocq_status ocq_mlp_forward(const void* packed_dev, size_t packed_bytes, const vo
                            void* workspace_dev, size_t workspace_bytes, const ocq_taps* taps,
                            void* stream);
 
+/* A stack of L MLP blocks with a precision mode per layer (the pages'
+ * mixed-precision scheme at model scale: each layer's weights in the
+ * precision chosen for it, BF16 kept for sensitive layers; "OCRia 推理栈：单卡
+ * B200 提速近 10 倍", section "Reducing the data moved: workload-aware
+ * quantization").  Block l takes the previous block's bf16 output as its x
+ * (block 0 takes x_bf16_dev) and the last block writes y_bf16_dev; each block
+ * computes exactly what ocq_mlp_forward computes for its mode.
+ *
+ * ocq_stack_workspace_bytes: device workspace for the call shape (0 if any
+ * argument is invalid): the largest block workspace of the schedule plus one
+ * bf16 [M, hidden] buffer for the alternating intermediate outputs.
+ *
+ * ocq_mlp_stack_forward (asynchronous, on `stream`):
+ * packed_devs[l]: blob of layer l packed for (hidden, inter, prec_modes[l]),
+ *             packed_bytes[l] >= ocq_packed_bytes(hidden, inter, prec_modes[l]);
+ * prec_modes: L modes (0, 1 or 2); 1 <= L <= 1024; host arrays, read during
+ *             the call only.
+ * x_bf16_dev, y_bf16_dev: bf16 [M, hidden]; x is only read, and y must not
+ *             overlap x or the workspace.
+ * workspace_dev: >= ocq_stack_workspace_bytes(...) bytes.
+ * Errors: as ocq_mlp_forward, checked for every layer before any launch.
+ * Stage events (ocq_set_stage_events) are not recorded by stack calls. */
+size_t ocq_stack_workspace_bytes(int M, int hidden, int inter, const int* prec_modes, int L);
+ocq_status ocq_mlp_stack_forward(const void* const* packed_devs, const size_t* packed_bytes,
+                                 const int* prec_modes, int L, const void* x_bf16_dev, int M,
+                                 int hidden, int inter, void* y_bf16_dev, void* workspace_dev,
+                                 size_t workspace_bytes, void* stream);
+
 /* Synchronously read a device blob's header and check it against
  * (hidden, inter, prec_mode): OCQ_OK or OCQ_ERR_BAD_BLOB. */
 ocq_status ocq_check_blob(const void* packed_dev, size_t packed_bytes, int hidden, int inter,

@@ -230,3 +230,17 @@ def forward(x_bits, packed):
 def block_reference(x_bits, w_gate, w_up, w_down, prec_mode):
     """Pack and run in one call."""
     return forward(x_bits, pack_block(w_gate, w_up, w_down, prec_mode))
+
+
+def stack_forward(x_bits, packed_layers):
+    """L blocks in sequence: block l's bf16 output y is block l+1's x (the
+    per-layer precision schedule of "OCRia 推理栈：单卡 B200 提速近 10 倍",
+    section "Reducing the data moved: workload-aware quantization", applied
+    along a stack).  Returns the list of every block's forward() result."""
+    outs = []
+    x = x_bits
+    for packed in packed_layers:
+        o = forward(x, packed)
+        outs.append(o)
+        x = o["y"]
+    return outs

@@ -154,4 +154,58 @@ ocq_status ocq_mlp_forward(const void* packed_dev, size_t packed_bytes, const vo
   return OCQ_OK;
 }
 
+static size_t stack_ws(int M, int hidden, int inter, const int* modes, int L, size_t* act_off) {
+  size_t w = 0;
+  for (int l = 0; l < L; ++l) {
+    const size_t t = make_plan(M, hidden, inter, modes[l]).total;
+    w = t > w ? t : w;
+  }
+  w = align_up(w);
+  if (act_off) *act_off = w;
+  return w + align_up((size_t)M * hidden * 2);
+}
+
+size_t ocq_stack_workspace_bytes(int M, int hidden, int inter, const int* prec_modes, int L) {
+  if (!prec_modes || L < 1 || L > 1024 || M < 1 || M > 8192 || !shape_ok(hidden, inter)) return 0;
+  for (int l = 0; l < L; ++l)
+    if (prec_modes[l] < 0 || prec_modes[l] > 2) return 0;
+  return stack_ws(M, hidden, inter, prec_modes, L, nullptr);
+}
+
+ocq_status ocq_mlp_stack_forward(const void* const* packed_devs, const size_t* packed_bytes, const int* prec_modes,
+                                 int L, const void* x_bf16_dev, int M, int hidden, int inter, void* y_bf16_dev,
+                                 void* workspace_dev, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  if (!packed_devs || !packed_bytes || !prec_modes) return set_error(OCQ_ERR_INVALID_ARG, "null host array");
+  if (L < 1 || L > 1024) return set_error(OCQ_ERR_INVALID_ARG, "L must be in [1, 1024]");
+  if (M < 1 || M > 8192) return set_error(OCQ_ERR_INVALID_ARG, "M must be in [1, 8192]");
+  for (int l = 0; l < L; ++l) {
+    ocq_status st = check_shape(hidden, inter, prec_modes[l]);
+    if (st != OCQ_OK) return st;
+    if (!packed_devs[l]) return set_error(OCQ_ERR_INVALID_ARG, "null device pointer");
+    if (!aligned16(packed_devs[l])) return set_error(OCQ_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+    if (packed_bytes[l] < blob_layout(hidden, inter, prec_modes[l]).total)
+      return set_error(OCQ_ERR_BUFFER_TOO_SMALL, "packed_bytes[l] < ocq_packed_bytes()");
+  }
+  if (!x_bf16_dev || !y_bf16_dev || !workspace_dev) return set_error(OCQ_ERR_INVALID_ARG, "null device pointer");
+  if (!aligned16(x_bf16_dev) || !aligned16(y_bf16_dev) || !aligned16(workspace_dev))
+    return set_error(OCQ_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  size_t act_off = 0;
+  if (workspace_bytes < stack_ws(M, hidden, inter, prec_modes, L, &act_off))
+    return set_error(OCQ_ERR_BUFFER_TOO_SMALL, "workspace_bytes < ocq_stack_workspace_bytes()");
+  // outputs alternate between y and the workspace's activation buffer so
+  // that the last block writes y and no block writes its own input
+  uint16_t* act = (uint16_t*)((uint8_t*)workspace_dev + act_off);
+  const uint16_t* in = (const uint16_t*)x_bf16_dev;
+  for (int l = 0; l < L; ++l) {
+    uint16_t* out = ((L - 1 - l) % 2 == 0) ? (uint16_t*)y_bf16_dev : act;
+    const Plan p = make_plan(M, hidden, inter, prec_modes[l]);
+    FwdArgs a{(const uint8_t*)packed_devs[l], in, out, (uint8_t*)workspace_dev, stream, nullptr, ocq_taps{}};
+    int rc = launch_forward(p, a);
+    if (rc != 0) return set_hip_error((hipError_t)rc, "kernel launch");
+    in = out;
+  }
+  return OCQ_OK;
+}
+
 }  // extern "C"

@@ -30,6 +30,15 @@ WORKLOADS = {
 }
 NVFP4_M_SWEEP = (1, 13, 52, 208)
 
+# Stacks of blocks with a precision mode per layer (0 FP8, 1 FP8 gate/up with
+# BF16 down, 2 NVFP4), spec-verify shape: the first and last layers are taken
+# as the sensitive ones and keep a BF16 down projection, the others alternate
+# FP8 and NVFP4.  Synthetic schedule: the pages name no per-layer assignment.
+STACKS = {
+    "stack_mixed": dict(hidden=2048, inter=6144, M=208, modes=(1, 0, 2, 0, 2, 0, 2, 1), x_outliers=False,
+                        w_std=0.02),
+}
+
 
 def to_bf16_bits(x32):
     """float32 array -> bfloat16 bit patterns (uint16), via torch's RNE cast."""
@@ -64,3 +73,17 @@ def workload_inputs(name, seed=0, M=None):
         assert M <= cfg["M"]
         d["x_bits"] = d["x_bits"][:M].copy()
     return d
+
+
+def stack_inputs(name, seed=0):
+    """x bits of a named stack and its layers' float32 weights: layer l's
+    weights are those make_inputs draws with seed + 1 + l (its one-row x is
+    discarded)."""
+    cfg = STACKS[name]
+    x_bits = make_inputs(cfg["hidden"], cfg["inter"], cfg["M"], cfg["x_outliers"], cfg["w_std"], seed,
+                         with_weights=False)["x_bits"]
+    layers = []
+    for l in range(len(cfg["modes"])):
+        d = make_inputs(cfg["hidden"], cfg["inter"], 1, False, cfg["w_std"], seed + 1 + l)
+        layers.append((d["w_gate"], d["w_up"], d["w_down"]))
+    return x_bits, layers

@@ -26,7 +26,7 @@ ERR_BAD_BLOB = -5
 
 EXPORTS = ("ocq_version", "ocq_packed_bytes", "ocq_pack_weights_host", "ocq_pack_weights",
            "ocq_unpack_weights_host", "ocq_workspace_bytes", "ocq_mlp_forward", "ocq_check_blob",
-           "ocq_set_stage_events", "ocq_last_error")
+           "ocq_set_stage_events", "ocq_last_error", "ocq_stack_workspace_bytes", "ocq_mlp_stack_forward")
 
 
 class OcqError(RuntimeError):
@@ -66,6 +66,10 @@ def lib():
     L.ocq_mlp_forward.restype = i
     L.ocq_check_blob.argtypes, L.ocq_check_blob.restype = [vp, sz, i, i, i, vp], i
     L.ocq_set_stage_events.argtypes, L.ocq_set_stage_events.restype = [ctypes.POINTER(vp), i], i
+    ip = ctypes.POINTER(i)
+    L.ocq_stack_workspace_bytes.argtypes, L.ocq_stack_workspace_bytes.restype = [i, i, i, ip, i], sz
+    L.ocq_mlp_stack_forward.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(sz), ip, i, vp, i, i, i, vp, vp, sz, vp]
+    L.ocq_mlp_stack_forward.restype = i
     _lib = L
     return L
 
@@ -180,6 +184,35 @@ def mlp_forward(blob, x, hidden, inter, prec_mode, y=None, workspace=None, taps=
     _check(lib().ocq_mlp_forward(blob.data_ptr(), blob.numel(), x.data_ptr(), M, hidden, inter, prec_mode,
                                  y.data_ptr(), workspace.data_ptr(), workspace.numel(),
                                  ctypes.byref(t) if t is not None else None, _stream_handle(stream)))
+    return y
+
+
+def _int_array(vals):
+    return (ctypes.c_int * len(vals))(*[int(v) for v in vals])
+
+
+def stack_workspace_bytes(M, hidden, inter, prec_modes):
+    return lib().ocq_stack_workspace_bytes(M, hidden, inter, _int_array(prec_modes), len(prec_modes))
+
+
+def mlp_stack_forward(blobs, prec_modes, x, hidden, inter, y=None, workspace=None, stream=None):
+    """L blocks in sequence (block l's output is block l+1's input); returns the
+    last block's y (bf16 [M, hidden]).  blobs: L uint8 CUDA tensors."""
+    import torch
+    if len(blobs) != len(prec_modes):
+        raise ValueError("one prec_mode per blob")
+    M = x.shape[0]
+    if y is None:
+        y = torch.empty((M, hidden), dtype=torch.bfloat16, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(max(1, stack_workspace_bytes(M, hidden, inter, prec_modes)), dtype=torch.uint8,
+                                device=x.device)
+    n = len(blobs)
+    ptrs = (ctypes.c_void_p * n)(*[b.data_ptr() for b in blobs])
+    sizes = (ctypes.c_size_t * n)(*[b.numel() for b in blobs])
+    _check(lib().ocq_mlp_stack_forward(ptrs, sizes, _int_array(prec_modes), n, x.data_ptr(), M, hidden, inter,
+                                       y.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                       _stream_handle(stream)))
     return y
 
 

@@ -141,3 +141,40 @@ def test_forward_without_device_reports_device_error():
         pytest.skip("a GPU is present")
     st = _fwd()
     assert st == ocq.ERR_DEVICE, (st, ocq.last_error())
+
+
+def test_stack_workspace_sizes():
+    one = ocq.workspace_bytes(208, 2048, 6144, 0)
+    both = ocq.stack_workspace_bytes(208, 2048, 6144, [0, 1, 2])
+    assert both >= max(one, ocq.workspace_bytes(208, 2048, 6144, 1)) + 208 * 2048 * 2
+    assert ocq.stack_workspace_bytes(208, 2048, 6144, [0, 3]) == 0
+    assert ocq.stack_workspace_bytes(0, 2048, 6144, [0]) == 0
+    assert ocq.lib().ocq_stack_workspace_bytes(16, 2048, 6144, None, 1) == 0
+    assert ocq.stack_workspace_bytes(16, 2048, 6144, []) == 0
+
+
+def _stack(**kw):
+    a = dict(blobs=[0x10000, 0x20000], nblobs=[1 << 30, 1 << 30], modes=[0, 2], x=0x30000, M=16, hidden=2048,
+             inter=6144, y=0x40000, ws=0x50000, nws=1 << 30, stream=None)
+    a.update(kw)
+    n = len(a["modes"])
+    blobs = None if a["blobs"] is None else (ctypes.c_void_p * max(1, n))(*a["blobs"])
+    sizes = (ctypes.c_size_t * max(1, n))(*a["nblobs"])
+    modes = (ctypes.c_int * max(1, n))(*a["modes"])
+    return ocq.lib().ocq_mlp_stack_forward(blobs, sizes, modes, a.get("L", n), a["x"], a["M"], a["hidden"],
+                                           a["inter"], a["y"], a["ws"], a["nws"], a["stream"])
+
+
+def test_stack_argument_errors():
+    assert _stack(L=0) == ocq.ERR_INVALID_ARG
+    assert _stack(L=2000) == ocq.ERR_INVALID_ARG
+    assert _stack(blobs=None) == ocq.ERR_INVALID_ARG
+    assert _stack(modes=[0, 5]) == ocq.ERR_INVALID_ARG
+    assert _stack(hidden=2000) == ocq.ERR_UNSUPPORTED
+    assert _stack(M=0) == ocq.ERR_INVALID_ARG
+    assert _stack(blobs=[0x10000, 0x20008]) == ocq.ERR_INVALID_ARG      # misaligned
+    assert _stack(blobs=[0x10000, 0]) == ocq.ERR_INVALID_ARG
+    assert _stack(nblobs=[1 << 30, 1000]) == ocq.ERR_BUFFER_TOO_SMALL
+    assert _stack(x=None) == ocq.ERR_INVALID_ARG
+    assert _stack(nws=1000) == ocq.ERR_BUFFER_TOO_SMALL
+    assert "workspace" in ocq.last_error()

@@ -133,6 +133,39 @@ def test_workload_nvfp4_sweep(M):
     compare(g, r, 2, rows=rows, what="nvfp4 M=%d" % M)
 
 
+def _stack_layers(hidden, inter, modes, seed):
+    ds = [I.make_inputs(hidden, inter, 1, w_std=0.02, seed=seed + 31 * l) for l in range(len(modes))]
+    blobs = [ocq.pack_weights(d["w_gate"], d["w_up"], d["w_down"], m) for d, m in zip(ds, modes)]
+    packed = [O.pack_block(d["w_gate"], d["w_up"], d["w_down"], m) for d, m in zip(ds, modes)]
+    return blobs, packed
+
+
+# stacks of blocks with a precision mode per layer: every layer's output is
+# checked against the oracle block applied to the GPU's own input of that
+# layer (the previous layer's GPU output), so differences do not compound;
+# even and odd L exercise both placements of the alternating outputs, 420
+# rows the LDS-tiled kernels
+@pytest.mark.parametrize("hidden,inter,M,modes", [(256, 768, 37, (0, 1, 2, 1)), (256, 768, 420, (1, 0, 2)),
+                                                  (384, 640, 5, (2, 2, 0))])
+def test_stack_layerwise(hidden, inter, M, modes):
+    print("case stack hidden=%d inter=%d M=%d modes=%s" % (hidden, inter, M, modes), flush=True)
+    x_bits = I.make_inputs(hidden, inter, M, x_outliers=True, seed=M + 3, with_weights=False)["x_bits"]
+    blobs, packed = _stack_layers(hidden, inter, modes, seed=hidden + M)
+    x = _to_dev_bf16(x_bits)
+    prev = x_bits
+    for l in range(1, len(modes) + 1):
+        y = ocq.mlp_stack_forward(blobs[:l], modes[:l], x, hidden, inter)
+        torch.cuda.synchronize()
+        yb = y.view(torch.int16).cpu().numpy().view(np.uint16)
+        r = O.forward(prev, packed[l - 1])
+        rel, mx = check_y(yb, r["y"], "stack layer %d of %s" % (l, modes))
+        prev = yb
+    # the whole stack again: same bits (deterministic kernels, same schedule)
+    y2 = ocq.mlp_stack_forward(blobs, modes, x, hidden, inter)
+    torch.cuda.synchronize()
+    assert np.array_equal(y2.view(torch.int16).cpu().numpy().view(np.uint16), prev)
+
+
 @pytest.mark.parametrize("prec", [0, 1, 2])
 def test_deterministic_and_zero_rows(prec):
     print("case determinism prec=%d" % prec, flush=True)

@@ -21,7 +21,7 @@ namespace {
 // column scales of its column in each of the T tiles.
 template <int Q, int T>
 struct EpiScales {
-  float xs[Q][4];
+  v4f xs[Q];   // vectors: element selects stay in registers
   float cg[T], cu[T];
 };
 
@@ -55,7 +55,7 @@ __device__ __forceinline__ void load_epi(EpiScales<Q, T>& e, const GateUpArgs& g
 // then stores two adjacent rows of the tile's 8 columns: 64 contiguous bytes
 // of the [tile][row][8] h32 block.  amax[e] accumulates |h| of value e.
 template <bool BF16H, int T>
-__device__ __forceinline__ void gateup_tile_epilogue(const GateUpArgs& g, const v4f& v, const float (&xs)[4],
+__device__ __forceinline__ void gateup_tile_epilogue(const GateUpArgs& g, const v4f v, const v4f xs,
                                                      float cg, float cu, int m_base, int ng, int t,
                                                      float (&amax)[2]) {
   const int lane = threadIdx.x & 63, gq = lane >> 4, r = lane & 15;
@@ -66,10 +66,14 @@ __device__ __forceinline__ void gateup_tile_epilogue(const GateUpArgs& g, const 
   const float p1 = dpp<0x128>(lo ? v[3] : v[2]);
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
+    // row 2e (gate lanes) or 2e + 1 (up lanes): selects, not a lane-dependent
+    // array index, which would put xs and v in scratch memory
     const int i = 2 * e + (lo ? 0 : 1);
-    const float gv = lo ? v[i] : (e ? p1 : p0);
-    const float uv = lo ? (e ? p1 : p0) : v[i];
-    const float hv = silu(gv * xs[i] * cg) * (uv * xs[i] * cu);
+    const float vi = lo ? v[2 * e] : v[2 * e + 1];
+    const float xi = lo ? xs[2 * e] : xs[2 * e + 1];
+    const float gv = lo ? vi : (e ? p1 : p0);
+    const float uv = lo ? (e ? p1 : p0) : vi;
+    const float hv = silu(gv * xi * cg) * (uv * xi * cu);
     const int m = m_base + 4 * gq + i;
     if constexpr (BF16H) {
       const uint16_t hb = (uint16_t)bf16_bits(hv);

@@ -318,7 +318,7 @@ __global__ __launch_bounds__(G::THREADS) void lg_gateup(GateUpArgs g) {
     const int mt = wm * G::MTW + j;
     if (mt >= nva) break;
     const int m_base = row0 + mt * 16 + 4 * (lane >> 4);
-    float xs[4];
+    v4f xs;
 #pragma unroll
     for (int i = 0; i < 4; ++i) xs[i] = g.sx[m_base + i];
     float amax[2] = {0.f, 0.f};
@@ -331,9 +331,11 @@ __global__ __launch_bounds__(G::THREADS) void lg_gateup(GateUpArgs g) {
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int i = 2 * e + (lo ? 0 : 1);
-        const float gv = lo ? v[i] : (e ? p1 : p0);
-        const float uv = lo ? (e ? p1 : p0) : v[i];
-        const float hv = silu(gv * xs[i] * cg[t]) * (uv * xs[i] * cu[t]);
+        const float vi = lo ? v[2 * e] : v[2 * e + 1];
+        const float xi = lo ? xs[2 * e] : xs[2 * e + 1];
+        const float gv = lo ? vi : (e ? p1 : p0);
+        const float uv = lo ? (e ? p1 : p0) : vi;
+        const float hv = silu(gv * xi * cg[t]) * (uv * xi * cu[t]);
         const int m = m_base + i;
         if constexpr (BF16H) {
           const uint16_t hb = (uint16_t)bf16_bits(hv);

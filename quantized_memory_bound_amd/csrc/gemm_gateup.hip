@@ -106,7 +106,7 @@ __device__ __forceinline__ void gateup_block(const GateUpArgs& g, int ngroups, i
 template <int BF, int MT, int T, int MS, int KS, int D, bool BF16H>
 __global__ __launch_bounds__(64 * MS * KS) void ks_gateup(GateUpArgs g) {
   constexpr int MTW = (MT + MS - 1) / MS;
-  extern __shared__ float red[];
+  extern __shared__ v4f red4[];
   int mb, ng;
   gateup_block(g, (g.I / 8) / T, mb, ng);
   const int C = g.H / kChunk;
@@ -128,8 +128,10 @@ __global__ __launch_bounds__(64 * MS * KS) void ks_gateup(GateUpArgs g) {
 
   // Epilogue, one wave per m-tile (rows are owned by exactly one wave, so the
   // row maxima need no cross-wave combination).  The partial tiles go through
-  // LDS one weight tile t at a time ([wave][m-tile][i][lane], NW * MTW KB);
-  // m-tile q = (ms, j) was accumulated by waves ms, ms + MS, ...  The
+  // LDS one weight tile t at a time ([wave][m-tile][lane] 16 B each, NW * MTW
+  // KB per tile, two regions used alternately so a tile's partials can be
+  // written while the previous tile's are still being read: one barrier per
+  // tile); m-tile q = (ms, j) was accumulated by waves ms, ms + MS, ...  The
   // epilogue scales are loaded before the first exchange.
   constexpr int NW = MS * KS, Q = (MT + NW - 1) / NW;
   EpiScales<Q, T> es;
@@ -139,9 +141,11 @@ __global__ __launch_bounds__(64 * MS * KS) void ks_gateup(GateUpArgs g) {
   for (int jq = 0; jq < Q; ++jq) amax[jq][0] = amax[jq][1] = 0.f;
 #pragma unroll
   for (int t = 0; t < T; ++t) {
-    if (t) lds_barrier();                // the previous tile's partials have been read
+    // region t & 1 was last read for tile t - 2, before every wave passed the
+    // barrier of tile t - 1
+    v4f* red = red4 + (t & 1) * (NW * MTW * 64);
 #pragma unroll
-    for (int j = 0; j < MTW; ++j) *(v4f*)&red[((wave * MTW + j) * 64 + lane) * 4] = acc[j][t];
+    for (int j = 0; j < MTW; ++j) red[(wave * MTW + j) * 64 + lane] = acc[j][t];
     lds_barrier();
 #pragma unroll
     for (int jq = 0; jq < Q; ++jq) {
@@ -150,7 +154,7 @@ __global__ __launch_bounds__(64 * MS * KS) void ks_gateup(GateUpArgs g) {
         const int qm = q / MTW, qj = q % MTW;
         v4f v = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) v += *(const v4f*)&red[(((qm + MS * ks) * MTW + qj) * 64 + lane) * 4];
+        for (int ks = 0; ks < KS; ++ks) v += red[((qm + MS * ks) * MTW + qj) * 64 + lane];
         gateup_tile_epilogue<BF16H, T>(g, v, es.xs[jq], es.cg[t], es.cu[t], row0 + q * 16, ng, t, amax[jq]);
       }
     }
@@ -179,7 +183,7 @@ template <int BF, bool BF16H, int MT, int T, int MS, int KS, int D>
 hipError_t launch_ks(const GateUpArgs& g, int grid, hipStream_t st, const LaunchEvents& ev) {
   constexpr int MTW = (MT + MS - 1) / MS;
   auto fn = ks_gateup<BF, MT, T, MS, KS, D, BF16H>;
-  const size_t lds = (size_t)MS * KS * MTW * 256 * sizeof(float);
+  const size_t lds = (size_t)(T > 1 ? 2 : 1) * MS * KS * MTW * 64 * sizeof(v4f);
   static bool attr = false;   // idempotent; a race only repeats the call
   if (!attr) {
     hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

@@ -122,6 +122,13 @@ __global__ __launch_bounds__(64 * MS * KS) void ks_gateup(GateUpArgs g) {
   for (int j = 0; j < MTW; ++j)
 #pragma unroll
     for (int t = 0; t < T; ++t) acc[j][t] = v4f{0.f, 0.f, 0.f, 0.f};
+  // the epilogue's scales are requested before the main loop, so their
+  // latency is hidden behind it (after it for the loop with padding chunks,
+  // which has no registers to spare)
+  constexpr int NW = MS * KS, Q = (MT + NW - 1) / NW;
+  EpiScales<Q, T> es;
+  auto q_of = [&](int j) { return wave + NW * j < MT ? wave + NW * j : wave; };
+  if constexpr (D != -1) load_epi<BF, Q, T>(es, g, row0, ng * T, q_of);
   if constexpr (D == -1) ks_mainloop_roll<BF, MTW, T, KS, false>(lp, kidx, 0, C, acc);
   else if constexpr (D < -1) ks_mainloop_roll<BF, MTW, T, KS, true, -D>(lp, kidx, 0, C, acc);
   else ks_mainloop<BF, MTW, T, KS, D>(lp, kidx, 0, C, acc);
@@ -131,11 +138,8 @@ __global__ __launch_bounds__(64 * MS * KS) void ks_gateup(GateUpArgs g) {
   // LDS one weight tile t at a time ([wave][m-tile][lane] 16 B each, NW * MTW
   // KB per tile, two regions used alternately so a tile's partials can be
   // written while the previous tile's are still being read: one barrier per
-  // tile); m-tile q = (ms, j) was accumulated by waves ms, ms + MS, ...  The
-  // epilogue scales are loaded before the first exchange.
-  constexpr int NW = MS * KS, Q = (MT + NW - 1) / NW;
-  EpiScales<Q, T> es;
-  load_epi<BF, Q, T>(es, g, row0, ng * T, [&](int j) { return wave + NW * j < MT ? wave + NW * j : wave; });
+  // tile); m-tile q = (ms, j) was accumulated by waves ms, ms + MS, ...
+  if constexpr (D == -1) load_epi<BF, Q, T>(es, g, row0, ng * T, q_of);
   float amax[Q][2];
 #pragma unroll
   for (int jq = 0; jq < Q; ++jq) amax[jq][0] = amax[jq][1] = 0.f;

@@ -313,25 +313,24 @@ __device__ __forceinline__ void ks_mainloop_roll(const LanePtrs& p, int kidx, in
   }
 }
 
-// LDS partial tiles [wave][pair][i][lane]; returns after a workgroup barrier
+// LDS partial tiles [wave][pair][lane], 16 B each (one ds_write_b128 per
+// tile); returns after a workgroup barrier
 template <int MT, int T>
-__device__ __forceinline__ void ks_stash(const v4f (&acc)[MT][T], float* red) {
+__device__ __forceinline__ void ks_stash(const v4f (&acc)[MT][T], v4f* red) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int t = 0; t < T; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) red[((wave * MT * T + mt * T + t) * 4 + i) * 64 + lane] = acc[mt][t][i];
-  __syncthreads();
+    for (int t = 0; t < T; ++t) red[(wave * MT * T + mt * T + t) * 64 + lane] = acc[mt][t];
+  lds_barrier();   // no wave reads what another stored to global memory
 }
 
-// sum of element (pair p, i, lane ln) over the KS waves w0, w0 + ws, ...
+// sum of pair p (lane ln) over the KS waves w0, w0 + ws, ... in wave order
 template <int KS>
-__device__ __forceinline__ float ks_sum(const float* red, int PT, int w0, int ws, int p, int i, int ln) {
-  float s = 0.f;
+__device__ __forceinline__ v4f ks_sum(const v4f* red, int PT, int w0, int ws, int p, int ln) {
+  v4f s = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int k = 0; k < KS; ++k) s += red[(((w0 + k * ws) * PT + p) * 4 + i) * 64 + ln];
+  for (int k = 0; k < KS; ++k) s += red[((w0 + k * ws) * PT + p) * 64 + ln];
   return s;
 }
 

@@ -45,7 +45,7 @@ __device__ __forceinline__ void down_block(const DownArgs& d, int& mb, int& ng) 
 
 template <int BF, int MT, int T, int NW, int D>
 __global__ __launch_bounds__(64 * NW) void ks_down(DownArgs d) {
-  extern __shared__ float red[];
+  extern __shared__ v4f red[];
   int mb, ng;
   down_block(d, mb, ng);
   const int C = d.I / kChunk;
@@ -70,11 +70,10 @@ __global__ __launch_bounds__(64 * NW) void ks_down(DownArgs d) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) rs[i] = row_scale<BF>(d, mbase + i);   // rows < Mpad: always readable
     const float cs = col_scale<BF>(d, j);
+    const v4f v = ks_sum<NW>(red, MT * T, 0, 1, q, lane);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float v = ks_sum<NW>(red, MT * T, 0, 1, q, i, lane);
-      if (mbase + i < d.M) d.y[(size_t)(mbase + i) * d.H + j] = (uint16_t)bf16_bits(v * rs[i] * cs);
-    }
+    for (int i = 0; i < 4; ++i)
+      if (mbase + i < d.M) d.y[(size_t)(mbase + i) * d.H + j] = (uint16_t)bf16_bits(v[i] * rs[i] * cs);
   }
 }
 

@@ -182,6 +182,22 @@ def test_deterministic_and_zero_rows(prec):
     compare(g1, r, prec, what="zero rows prec=%d" % prec)
 
 
+# row counts at the edges of the kernel choice (383 and 384 rows: the last
+# skinny shape and the first LDS-tiled one) and the largest M the ABI takes
+# (8192 rows: 40 m-blocks of 208 in the LDS-tiled kernels); the oracle runs on
+# sampled rows for the largest
+@pytest.mark.parametrize("prec", [0, 1, 2])
+@pytest.mark.parametrize("M", [383, 384, 8192])
+def test_row_count_edges(M, prec):
+    print("case rows M=%d prec=%d" % (M, prec), flush=True)
+    d = I.make_inputs(256, 768, M, x_outliers=True, w_std=0.02, seed=M + prec)
+    g, _ = run_gpu(d, prec)
+    rows = _sample_rows(M, 96) if M > 1000 else None
+    xb = d["x_bits"][rows] if rows is not None else d["x_bits"]
+    r = O.block_reference(xb, d["w_gate"], d["w_up"], d["w_down"], prec)
+    compare(g, r, prec, rows=rows, what="M=%d prec=%d" % (M, prec))
+
+
 def test_lossless_grid_inputs_tight():
     # x and weights on the E4M3 grid with power-of-two scales: quantization of x
     # and the weights is exact, so the only differences left are fp32 vs fp64

@@ -37,15 +37,16 @@ MALL_BYTES = 256 << 20
 
 
 def alg_bytes(M, H, I, prec):
-    """Compulsory traffic of one block: weight codes + weight scales + x (bf16,
-    read once) + y (bf16, written once)."""
+    """Compulsory traffic of one block: weight codes + weight scales + the
+    blob's per-channel x multiplier + x (bf16, read once) + y (bf16, written
+    once)."""
     if prec == 0:
         w = 2 * I * H + 2 * I * 4 + H * I + H * 4
     elif prec == 1:
         w = 2 * I * H + 2 * I * 4 + 2 * H * I
     else:
         w = I * H + 2 * I * H // 16 + 8 + H * I // 2 + H * I // 16 + 4
-    return w + 2 * M * H * 2
+    return w + H * 4 + 2 * M * H * 2
 
 
 def gateup_alg(M, H, I, prec):

@@ -86,9 +86,43 @@ ocq_status ocq_pack_weights(const float* w_gate_host, const float* w_up_host,
                             const float* w_down_host, int hidden, int inter, int prec_mode,
                             void* packed_dev, size_t packed_bytes, void* stream);
 
+/* Activation-aware smoothing (optional).  The per-token E4M3 scale of x is
+ * set by its largest channel, so a few outlier input channels cost every
+ * other channel precision.  Per-input-channel factors s[k] move that range
+ * into the gate/up weights: the blob holds the codes of fl32(W[n][k] s[k]),
+ * and the block multiplies x by fl32(1 / s[k]) before quantizing it, which
+ * leaves x W^T unchanged in exact arithmetic.  (The pages' precision is
+ * chosen and calibrated per workload: "OCRia 推理栈：单卡 B200 提速近 10 倍",
+ * section "Reducing the data moved: workload-aware quantization"; the rule
+ * for s below is the published SmoothQuant one.)
+ *
+ * ocq_calibrate_smoothing_host: s[k] = amax_x[k]^alpha / amax_w[k]^(1-alpha)
+ * in double, rounded once to float, where amax_x[k] is max |x[t][k]| over the
+ * `rows` calibration rows (bf16 bits [rows, hidden], host) and amax_w[k] is
+ * max |W[n][k]| over the rows of both W_gate and W_up (host fp32 [inter,
+ * hidden]); s[k] = 1 where either is 0; clamped to [2^-20, 2^20].
+ * alpha in [0, 1].  s_out: host float [hidden].
+ *
+ * ocq_pack_weights_smoothed_host / ocq_pack_weights_smoothed: as the plain
+ * packers, with smooth_host = s (host float [hidden], every s[k] finite and
+ * > 0; NULL = no smoothing, the same blob as the plain packers).  The down
+ * projection is not smoothed.  Blobs are used by ocq_mlp_forward unchanged. */
+ocq_status ocq_calibrate_smoothing_host(const void* x_calib_bf16_host, int rows, int hidden,
+                                        const float* w_gate_host, const float* w_up_host, int inter,
+                                        float alpha, float* s_out);
+ocq_status ocq_pack_weights_smoothed_host(const float* w_gate_host, const float* w_up_host,
+                                          const float* w_down_host, const float* smooth_host,
+                                          int hidden, int inter, int prec_mode, void* packed_host,
+                                          size_t packed_bytes);
+ocq_status ocq_pack_weights_smoothed(const float* w_gate_host, const float* w_up_host,
+                                     const float* w_down_host, const float* smooth_host, int hidden,
+                                     int inter, int prec_mode, void* packed_dev, size_t packed_bytes,
+                                     void* stream);
+
 /* Inverse of the packing layout, for inspection and tests: from a HOST copy
  * of a blob, write one projection in plain row-major form.
- *   which = 0 gate, 1 up, 2 down.
+ *   which = 0 gate, 1 up, 2 down, 3 the x multiplier (float [hidden] into
+ *   scales_out; codes_out unused).
  *   codes_out: uint8 [rows, cols] (E4M3 or E2M1 code per byte) or uint16
  *              bf16 bits [rows, cols] for a BF16 projection.
  *   scales_out: FP8 -> float [rows]; NVFP4 -> uint8 E4M3 [rows, cols/16];

@@ -12,7 +12,9 @@ What is computed, step by step, and the passage each step follows:
             the bytes per weight; precision is mixed per layer across BF16,
             FP8 and NVFP4; sensitive layers stay at higher precision.)
   x-quant   Every row (token) of x is quantized to E4M3 with its own fp32
-            scale amax/448 (per-token FP8 activations).
+            scale amax/448 (per-token FP8 activations).  With a smoothed
+            blob, x is first multiplied per channel by fl32(1/s[k]) (see
+            pack_block and calibrate_smoothing).
   gate/up   G = x W_g^T and U = x W_u^T over all M rows at once: a verify pass
             covers every request's 1 + draft tokens, and the weights are read
             again on every step (section "Generate more tokens per target
@@ -127,8 +129,52 @@ def pack_nvfp4(w):
     return codes, sb, S
 
 
-def pack_block(w_gate, w_up, w_down, prec_mode):
-    """Quantize the three projections of one block for `prec_mode`."""
+def calibrate_smoothing(x_calib_bits, w_gate, w_up, alpha=0.5):
+    """Per-input-channel smoothing factors from calibration activations.
+
+    The pages calibrate the quantization on the workload ("OCRia 推理栈：单卡
+    B200 提速近 10 倍", section "Reducing the data moved: workload-aware
+    quantization") without giving a rule; this is the published SmoothQuant
+    rule: s[k] = amax_x[k]^alpha / amax_w[k]^(1 - alpha), amax_x[k] = max over
+    the calibration rows of |x[t, k]|, amax_w[k] = max over the rows of W_gate
+    and W_up of |W[n, k]|.  Reading: evaluated in double, rounded once to
+    float32; s = 1 where either maximum is 0; clamped to [2^-20, 2^20].
+    """
+    ax = np.max(np.abs(bf16_to_f64(x_calib_bits)), axis=0)
+    wg = np.abs(np.asarray(w_gate, dtype=np.float32).astype(np.float64))
+    wu = np.abs(np.asarray(w_up, dtype=np.float32).astype(np.float64))
+    aw = np.maximum(wg.max(axis=0), wu.max(axis=0))
+    s = np.ones_like(ax)
+    ok = (ax > 0) & (aw > 0)
+    s[ok] = np.power(ax[ok], float(np.float32(alpha))) / np.power(aw[ok], 1.0 - float(np.float32(alpha)))
+    s = np.clip(s, 2.0 ** -20, 2.0 ** 20)
+    return s.astype(np.float32)
+
+
+def pack_block(w_gate, w_up, w_down, prec_mode, smooth=None):
+    """Quantize the three projections of one block for `prec_mode`.
+
+    smooth: None, or per-input-channel factors s (float32 [hidden], > 0): the
+    gate and up weights are quantized as fl32(W[n, k] s[k]) and the block
+    multiplies x by xmul[k] = fl32(1 / s[k]) before quantizing it, which leaves
+    x W^T unchanged in exact arithmetic (SmoothQuant's migration of activation
+    outliers into the weights).
+    """
+    H = np.asarray(w_gate).shape[1]
+    if smooth is None:
+        xmul = np.ones(H, dtype=np.float32)
+    else:
+        sm = np.asarray(smooth, dtype=np.float32)
+        assert sm.shape == (H,) and np.all(sm > 0) and np.all(np.isfinite(sm))
+        w_gate = np.asarray(w_gate, dtype=np.float32) * sm[None, :]     # float32 products, RNE
+        w_up = np.asarray(w_up, dtype=np.float32) * sm[None, :]
+        xmul = np.float32(1.0) / sm
+    out = _pack_plain(w_gate, w_up, w_down, prec_mode)
+    out["xmul"] = xmul
+    return out
+
+
+def _pack_plain(w_gate, w_up, w_down, prec_mode):
     if prec_mode in (PREC_FP8, PREC_FP8_DOWN_BF16):
         g = pack_fp8(w_gate)
         u = pack_fp8(w_up)
@@ -204,6 +250,10 @@ def forward(x_bits, packed):
     """
     prec = packed["prec_mode"]
     x = bf16_to_f64(x_bits)
+    xmul = packed.get("xmul")
+    if xmul is not None:
+        # x' = fl32(x xmul): a float32 product (x is exact in float32)
+        x = (x.astype(np.float32) * np.asarray(xmul, dtype=np.float32)[None, :]).astype(np.float64)
     xq, sx = quantize_rows_e4m3(x)
     X = dec_e4m3(xq)
 

@@ -61,19 +61,44 @@ size_t ocq_packed_bytes(int hidden, int inter, int prec_mode) {
   return blob_layout(hidden, inter, prec_mode).total;
 }
 
-ocq_status ocq_pack_weights_host(const float* w_gate_host, const float* w_up_host, const float* w_down_host,
-                                 int hidden, int inter, int prec_mode, void* packed_host, size_t packed_bytes) {
+ocq_status ocq_pack_weights_smoothed_host(const float* w_gate_host, const float* w_up_host, const float* w_down_host,
+                                          const float* smooth_host, int hidden, int inter, int prec_mode,
+                                          void* packed_host, size_t packed_bytes) {
   g_err.clear();
   ocq_status st = check_shape(hidden, inter, prec_mode);
   if (st != OCQ_OK) return st;
   if (!w_gate_host || !w_up_host || !w_down_host || !packed_host)
     return set_error(OCQ_ERR_INVALID_ARG, "null weight or output pointer");
-  return pack_host(w_gate_host, w_up_host, w_down_host, hidden, inter, prec_mode, (uint8_t*)packed_host,
+  return pack_host(w_gate_host, w_up_host, w_down_host, hidden, inter, prec_mode, smooth_host, (uint8_t*)packed_host,
                    packed_bytes);
+}
+
+ocq_status ocq_pack_weights_host(const float* w_gate_host, const float* w_up_host, const float* w_down_host,
+                                 int hidden, int inter, int prec_mode, void* packed_host, size_t packed_bytes) {
+  return ocq_pack_weights_smoothed_host(w_gate_host, w_up_host, w_down_host, nullptr, hidden, inter, prec_mode,
+                                        packed_host, packed_bytes);
+}
+
+ocq_status ocq_calibrate_smoothing_host(const void* x_calib_bf16_host, int rows, int hidden, const float* w_gate_host,
+                                        const float* w_up_host, int inter, float alpha, float* s_out) {
+  g_err.clear();
+  if (!shape_ok(hidden, inter))
+    return set_error(OCQ_ERR_UNSUPPORTED, "hidden and inter must be multiples of 128 in [128, 65536]");
+  if (!x_calib_bf16_host || !w_gate_host || !w_up_host || !s_out || rows < 1)
+    return set_error(OCQ_ERR_INVALID_ARG, "null pointer or no calibration rows");
+  if (!(alpha >= 0.0f && alpha <= 1.0f)) return set_error(OCQ_ERR_INVALID_ARG, "alpha must be in [0, 1]");
+  return calibrate_host((const uint16_t*)x_calib_bf16_host, rows, hidden, w_gate_host, w_up_host, inter, alpha, s_out);
 }
 
 ocq_status ocq_pack_weights(const float* w_gate_host, const float* w_up_host, const float* w_down_host, int hidden,
                             int inter, int prec_mode, void* packed_dev, size_t packed_bytes, void* stream) {
+  return ocq_pack_weights_smoothed(w_gate_host, w_up_host, w_down_host, nullptr, hidden, inter, prec_mode, packed_dev,
+                                   packed_bytes, stream);
+}
+
+ocq_status ocq_pack_weights_smoothed(const float* w_gate_host, const float* w_up_host, const float* w_down_host,
+                                     const float* smooth_host, int hidden, int inter, int prec_mode, void* packed_dev,
+                                     size_t packed_bytes, void* stream) {
   g_err.clear();
   ocq_status st = check_shape(hidden, inter, prec_mode);
   if (st != OCQ_OK) return st;
@@ -83,7 +108,7 @@ ocq_status ocq_pack_weights(const float* w_gate_host, const float* w_up_host, co
   const size_t need = blob_layout(hidden, inter, prec_mode).total;
   if (packed_bytes < need) return set_error(OCQ_ERR_BUFFER_TOO_SMALL, "packed_bytes < ocq_packed_bytes()");
   std::vector<uint8_t> host(need);
-  st = pack_host(w_gate_host, w_up_host, w_down_host, hidden, inter, prec_mode, host.data(), need);
+  st = pack_host(w_gate_host, w_up_host, w_down_host, hidden, inter, prec_mode, smooth_host, host.data(), need);
   if (st != OCQ_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipMemcpyAsync(packed_dev, host.data(), need, hipMemcpyHostToDevice, s);

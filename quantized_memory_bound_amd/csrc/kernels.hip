@@ -49,9 +49,12 @@ inline int tile_row_grid(int mtiles, int nrest) { return (mtiles + 7) / 8 * 128 
 // waves in LDS.  Codes go to the fragment-ordered operand buffer (8
 // consecutive inputs = 8 contiguous bytes there), or with f16 set their exact
 // fp16 values in the 16-bit fragment order (16 contiguous bytes); rows
-// M..Mpad-1 are written as zero codes with scale 0.  tap_q / tap_s (nullable) receive the plain
+// M..Mpad-1 are written as zero codes with scale 0.  x is first multiplied by
+// the blob's per-channel multiplier xmul (1 unless packed with smoothing):
+// x'[k] = fl32(x[k] xmul[k]), and x' is what is quantized.  tap_q / tap_s (nullable) receive the plain
 // [M][H] codes and [M] scales.
-__global__ __launch_bounds__(kThreads) void k_xquant(const uint16_t* __restrict__ x, int M, int H, int Mpad,
+__global__ __launch_bounds__(kThreads) void k_xquant(const uint16_t* __restrict__ x, const float* __restrict__ xmul,
+                                                     int M, int H, int Mpad,
                                                      uint8_t* __restrict__ xq, int f16, float* __restrict__ sx,
                                                      uint8_t* __restrict__ tap_q, float* __restrict__ tap_s) {
   __shared__ float s_max[kWaves];
@@ -78,13 +81,18 @@ __global__ __launch_bounds__(kThreads) void k_xquant(const uint16_t* __restrict_
       v[j] = k < H ? *(const v4i*)(xr + k) : v4i{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int j = 0; j < kReg; ++j)
+    for (int j = 0; j < kReg; ++j) {
+      const int k = base + (j * kThreads + threadIdx.x) * 8;
+      if (k >= H) continue;
+      const v4f m0 = *(const v4f*)(xmul + k), m1 = *(const v4f*)(xmul + k + 4);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const uint32_t w = (uint32_t)v[j][q];
-        amax = fmaxf(amax, fabsf(__uint_as_float(w << 16)));
-        amax = fmaxf(amax, fabsf(__uint_as_float(w & 0xFFFF0000u)));
+        const float ma = q < 2 ? m0[2 * q] : m1[2 * q - 4], mb = q < 2 ? m0[2 * q + 1] : m1[2 * q - 3];
+        amax = fmaxf(amax, fabsf(__uint_as_float(w << 16) * ma));
+        amax = fmaxf(amax, fabsf(__uint_as_float(w & 0xFFFF0000u) * mb));
       }
+    }
   }
   amax = wave_max(amax);
   if (lane == 0) s_max[wave] = amax;
@@ -105,11 +113,13 @@ __global__ __launch_bounds__(kThreads) void k_xquant(const uint16_t* __restrict_
       if (k >= H) continue;
       uint32_t out[2] = {0u, 0u};
       if (s > 0.0f) {
+        const v4f m0 = *(const v4f*)(xmul + k), m1 = *(const v4f*)(xmul + k + 4);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const uint32_t w = (uint32_t)v[j][q];
-          const uint32_t c0 = enc_e4m3(__uint_as_float(w << 16) / s);
-          const uint32_t c1 = enc_e4m3(__uint_as_float(w & 0xFFFF0000u) / s);
+          const float ma = q < 2 ? m0[2 * q] : m1[2 * q - 4], mb = q < 2 ? m0[2 * q + 1] : m1[2 * q - 3];
+          const uint32_t c0 = enc_e4m3(__uint_as_float(w << 16) * ma / s);
+          const uint32_t c1 = enc_e4m3(__uint_as_float(w & 0xFFFF0000u) * mb / s);
           out[q >> 1] |= (c0 | (c1 << 8)) << (16 * (q & 1));
         }
       }
@@ -197,7 +207,8 @@ int launch_forward(const Plan& p, const FwdArgs& a) {
 
   stage(a, 0);
   const bool bf16_down = p.prec == kFP8DownBF16;
-  hipLaunchKernelGGL(k_xquant, dim3(tile_row_grid(p.Mpad / 16, 1)), dim3(kThreads), 0, st, a.x, p.M, p.hidden, p.Mpad, xq, p.lg1, sx,
+  hipLaunchKernelGGL(k_xquant, dim3(tile_row_grid(p.Mpad / 16, 1)), dim3(kThreads), 0, st, a.x,
+                     (const float*)(a.blob + L.off_xmul), p.M, p.hidden, p.Mpad, xq, p.lg1, sx,
                      (uint8_t*)a.taps.x_codes, (float*)a.taps.x_scales);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return (int)e;

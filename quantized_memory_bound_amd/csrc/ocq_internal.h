@@ -12,8 +12,12 @@ namespace ocq {
 ocq_status set_error(ocq_status st, const char* msg);
 
 // host packer (pack.cpp)
+// smooth (nullable): per-input-channel factors s[hidden] > 0; the gate/up
+// weights are packed as fl32(W[n][k] s[k]) and x is multiplied by fl32(1/s[k])
 ocq_status pack_host(const float* wg, const float* wu, const float* wd, int hidden, int inter, int prec,
-                     uint8_t* out, size_t out_bytes);
+                     const float* smooth, uint8_t* out, size_t out_bytes);
+ocq_status calibrate_host(const uint16_t* x_bf16, int rows, int hidden, const float* wg, const float* wu, int inter,
+                          float alpha, float* s_out);
 ocq_status unpack_host(const uint8_t* blob, size_t bytes, int which, void* codes_out, void* scales_out,
                        float* tensor_scale_out);
 uint8_t host_enc_e4m3(float v);

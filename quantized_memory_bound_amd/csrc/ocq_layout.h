@@ -33,7 +33,7 @@
 
 namespace ocq {
 
-constexpr uint32_t kBlobVersion = 1;
+constexpr uint32_t kBlobVersion = 2;
 constexpr char kBlobMagic[8] = {'O', 'C', 'Q', 'B', 'L', 'O', 'B', '1'};
 constexpr int kChunk = 128;           // inputs per chunk
 constexpr int kTileRows = 16;         // output rows per tile
@@ -51,9 +51,10 @@ struct BlobHeader {
   // byte offsets from the blob start
   uint64_t off_gu_codes, off_gu_scales, off_gu_bscales;
   uint64_t off_dn_codes, off_dn_scales, off_dn_bscales;
+  uint64_t off_xmul;           // fp32 [hidden]: x is multiplied by it before its quantization
   uint64_t total_bytes;
   float s_gate, s_up, s_down;  // NVFP4 per-tensor scales (0 otherwise)
-  uint8_t pad[256 - 8 - 4 - 12 - 7 * 8 - 12];
+  uint8_t pad[256 - 8 - 4 - 12 - 8 * 8 - 12];
 };
 static_assert(sizeof(BlobHeader) == 256, "header is 256 bytes");
 
@@ -75,6 +76,7 @@ struct BlobLayout {
   WeightKind gu, dn;
   uint64_t off_gu_codes, off_gu_scales, off_gu_bscales;
   uint64_t off_dn_codes, off_dn_scales, off_dn_bscales;
+  uint64_t off_xmul;
   uint64_t total;
 };
 
@@ -95,6 +97,8 @@ inline BlobLayout blob_layout(int hidden, int inter, int prec) {
   L.off_dn_codes = o;   o = align_up(o + codes_bytes(L.dn, H, I));
   L.off_dn_scales = o;  o = align_up(o + (L.dn == kWFP8 ? H * sizeof(float) : 0));
   L.off_dn_bscales = o; o = align_up(o + bscale_bytes(L.dn, H, I));
+  // per-input-channel multiplier of x (1 everywhere unless packed with smoothing)
+  L.off_xmul = o;       o = align_up(o + H * sizeof(float));
   L.total = o;
   return L;
 }

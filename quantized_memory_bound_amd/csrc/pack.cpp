@@ -9,6 +9,7 @@
 //         sb = E4M3(fl32(amax_b / (6 S))); code = E2M1(fl32(w / (dec(sb) S))).
 //   Zero scale -> all codes 0.  Encoders: nearest, ties to even, saturating.
 // The codes are then written in the fragment order described in ocq_layout.h.
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <vector>
@@ -183,18 +184,38 @@ static void read_fp8_frags(const uint8_t* src, uint8_t* a, uint8_t* b, bool inte
 // ---- entry points (host) ----------------------------------------------------
 
 ocq_status pack_host(const float* wg, const float* wu, const float* wd, int hidden, int inter, int prec,
-                     uint8_t* out, size_t out_bytes) {
+                     const float* smooth, uint8_t* out, size_t out_bytes) {
   BlobLayout L = blob_layout(hidden, inter, prec);
   if (out_bytes < L.total) return set_error(OCQ_ERR_BUFFER_TOO_SMALL, "packed buffer smaller than ocq_packed_bytes");
-  std::memset(out, 0, L.total);
   size_t H = hidden, I = inter;
+  // per-input-channel smoothing: W'[n][k] = fl32(W[n][k] s[k]) for gate and up,
+  // x'[k] = fl32(x[k] fl32(1 / s[k])) at run time
+  std::vector<float> sg, su;
+  if (smooth) {
+    for (size_t k = 0; k < H; ++k)
+      if (!(smooth[k] > 0.0f) || !std::isfinite(smooth[k]))
+        return set_error(OCQ_ERR_INVALID_ARG, "smoothing factors must be finite and > 0");
+    sg.resize(I * H);
+    su.resize(I * H);
+    for (size_t n = 0; n < I; ++n)
+      for (size_t k = 0; k < H; ++k) {
+        sg[n * H + k] = wg[n * H + k] * smooth[k];
+        su[n * H + k] = wu[n * H + k] * smooth[k];
+      }
+    wg = sg.data();
+    wu = su.data();
+  }
+  std::memset(out, 0, L.total);
   BlobHeader hd{};
   std::memcpy(hd.magic, kBlobMagic, 8);
   hd.version = kBlobVersion;
   hd.hidden = hidden; hd.inter = inter; hd.prec_mode = prec;
   hd.off_gu_codes = L.off_gu_codes; hd.off_gu_scales = L.off_gu_scales; hd.off_gu_bscales = L.off_gu_bscales;
   hd.off_dn_codes = L.off_dn_codes; hd.off_dn_scales = L.off_dn_scales; hd.off_dn_bscales = L.off_dn_bscales;
+  hd.off_xmul = L.off_xmul;
   hd.total_bytes = L.total;
+  float* xmul = reinterpret_cast<float*>(out + L.off_xmul);
+  for (size_t k = 0; k < H; ++k) xmul[k] = smooth ? 1.0f / smooth[k] : 1.0f;
   if (L.gu == kWFP8) {
     FP8Plain g = quant_fp8_rows(wg, I, H), u = quant_fp8_rows(wu, I, H);
     write_fp8_frags(out + L.off_gu_codes, g.codes.data(), u.codes.data(), true, I / 8, H);
@@ -223,6 +244,33 @@ ocq_status pack_host(const float* wg, const float* wu, const float* wd, int hidd
   return OCQ_OK;
 }
 
+// Smoothing factors from calibration activations (SmoothQuant's rule):
+// s[k] = amax_x[k]^alpha / amax_w[k]^(1 - alpha), amax_x over the calibration
+// rows of x, amax_w over the rows of both gate and up; evaluated in double and
+// rounded once to float; 1 where either maximum is 0; clamped to [2^-20, 2^20].
+ocq_status calibrate_host(const uint16_t* x_bf16, int rows, int hidden, const float* wg, const float* wu, int inter,
+                          float alpha, float* s_out) {
+  const size_t H = hidden, I = inter;
+  std::vector<float> ax(H, 0.0f), aw(H, 0.0f);
+  for (size_t t = 0; t < (size_t)rows; ++t)
+    for (size_t k = 0; k < H; ++k) {
+      uint32_t b = (uint32_t)x_bf16[t * H + k] << 16;
+      float v;
+      std::memcpy(&v, &b, 4);
+      ax[k] = std::max(ax[k], std::fabs(v));
+    }
+  for (size_t n = 0; n < I; ++n)
+    for (size_t k = 0; k < H; ++k)
+      aw[k] = std::max(aw[k], std::max(std::fabs(wg[n * H + k]), std::fabs(wu[n * H + k])));
+  for (size_t k = 0; k < H; ++k) {
+    double v = 1.0;
+    if (ax[k] > 0.0f && aw[k] > 0.0f) v = std::pow((double)ax[k], (double)alpha) / std::pow((double)aw[k], 1.0 - alpha);
+    v = std::min(std::max(v, 0x1p-20), 0x1p20);
+    s_out[k] = (float)v;
+  }
+  return OCQ_OK;
+}
+
 ocq_status unpack_host(const uint8_t* blob, size_t bytes, int which, void* codes_out, void* scales_out,
                        float* tensor_scale_out) {
   if (bytes < sizeof(BlobHeader)) return set_error(OCQ_ERR_BUFFER_TOO_SMALL, "blob smaller than its header");
@@ -234,8 +282,14 @@ ocq_status unpack_host(const uint8_t* blob, size_t bytes, int which, void* codes
     return set_error(OCQ_ERR_BAD_BLOB, "blob header holds an invalid shape or mode");
   BlobLayout L = blob_layout(hd.hidden, hd.inter, hd.prec_mode);
   if (bytes < L.total) return set_error(OCQ_ERR_BUFFER_TOO_SMALL, "blob smaller than its layout");
-  if (which < 0 || which > 2 || !codes_out) return set_error(OCQ_ERR_INVALID_ARG, "which must be 0..2, codes_out non-null");
   size_t H = hd.hidden, I = hd.inter;
+  if (which == 3) {   // the x multiplier (1 / smoothing factor per input channel)
+    if (!scales_out) return set_error(OCQ_ERR_INVALID_ARG, "which = 3 needs scales_out");
+    std::memcpy(scales_out, blob + L.off_xmul, H * 4);
+    if (tensor_scale_out) *tensor_scale_out = 0.0f;
+    return OCQ_OK;
+  }
+  if (which < 0 || which > 2 || !codes_out) return set_error(OCQ_ERR_INVALID_ARG, "which must be 0..3, codes_out non-null");
   bool gu = which < 2;
   WeightKind k = gu ? L.gu : L.dn;
   size_t rows = gu ? I : H, cols = gu ? H : I;

@@ -26,7 +26,8 @@ ERR_BAD_BLOB = -5
 
 EXPORTS = ("ocq_version", "ocq_packed_bytes", "ocq_pack_weights_host", "ocq_pack_weights",
            "ocq_unpack_weights_host", "ocq_workspace_bytes", "ocq_mlp_forward", "ocq_check_blob",
-           "ocq_set_stage_events", "ocq_last_error", "ocq_stack_workspace_bytes", "ocq_mlp_stack_forward")
+           "ocq_set_stage_events", "ocq_last_error", "ocq_stack_workspace_bytes", "ocq_mlp_stack_forward",
+           "ocq_calibrate_smoothing_host", "ocq_pack_weights_smoothed_host", "ocq_pack_weights_smoothed")
 
 
 class OcqError(RuntimeError):
@@ -59,6 +60,12 @@ def lib():
     L.ocq_pack_weights_host.restype = i
     L.ocq_pack_weights.argtypes = [vp, vp, vp, i, i, i, vp, sz, vp]
     L.ocq_pack_weights.restype = i
+    L.ocq_pack_weights_smoothed_host.argtypes = [vp, vp, vp, vp, i, i, i, vp, sz]
+    L.ocq_pack_weights_smoothed_host.restype = i
+    L.ocq_pack_weights_smoothed.argtypes = [vp, vp, vp, vp, i, i, i, vp, sz, vp]
+    L.ocq_pack_weights_smoothed.restype = i
+    L.ocq_calibrate_smoothing_host.argtypes = [vp, i, i, vp, vp, i, f, vp]
+    L.ocq_calibrate_smoothing_host.restype = i
     L.ocq_unpack_weights_host.argtypes = [vp, sz, i, vp, vp, ctypes.POINTER(f)]
     L.ocq_unpack_weights_host.restype = i
     L.ocq_workspace_bytes.argtypes, L.ocq_workspace_bytes.restype = [i, i, i, i], sz
@@ -100,16 +107,31 @@ def _f32c(a):
     return np.ascontiguousarray(a, dtype=np.float32)
 
 
-def pack_weights_host(w_gate, w_up, w_down, prec_mode):
-    """Quantize + pack on the host; returns the blob as a uint8 numpy array."""
+def calibrate_smoothing(x_calib_bits, w_gate, w_up, alpha=0.5):
+    """Per-input-channel smoothing factors (float32 [hidden]) from calibration
+    activations (bf16 bits [rows, hidden]) and the gate/up weights."""
+    xb = np.ascontiguousarray(x_calib_bits, dtype=np.uint16)
+    wg, wu = _f32c(w_gate), _f32c(w_up)
+    inter, hidden = wg.shape
+    s = np.empty(hidden, dtype=np.float32)
+    _check(lib().ocq_calibrate_smoothing_host(xb.ctypes.data, xb.shape[0], hidden, wg.ctypes.data, wu.ctypes.data,
+                                              inter, float(alpha), s.ctypes.data))
+    return s
+
+
+def pack_weights_host(w_gate, w_up, w_down, prec_mode, smooth=None):
+    """Quantize + pack on the host; returns the blob as a uint8 numpy array.
+    smooth: None or per-input-channel factors (float32 [hidden])."""
     wg, wu, wd = _f32c(w_gate), _f32c(w_up), _f32c(w_down)
     inter, hidden = wg.shape
     n = packed_bytes(hidden, inter, prec_mode)
     if n == 0:
         raise OcqError(ERR_UNSUPPORTED, "invalid shape or prec_mode")
     out = np.empty(n, dtype=np.uint8)
-    _check(lib().ocq_pack_weights_host(wg.ctypes.data, wu.ctypes.data, wd.ctypes.data, hidden, inter,
-                                       prec_mode, out.ctypes.data, n))
+    sm = None if smooth is None else _f32c(smooth)
+    _check(lib().ocq_pack_weights_smoothed_host(wg.ctypes.data, wu.ctypes.data, wd.ctypes.data,
+                                                None if sm is None else sm.ctypes.data, hidden, inter,
+                                                prec_mode, out.ctypes.data, n))
     return out
 
 
@@ -118,6 +140,10 @@ def unpack_weights_host(blob, which, hidden, inter, prec_mode):
     blob = np.ascontiguousarray(blob, dtype=np.uint8)
     rows, cols = (inter, hidden) if which < 2 else (hidden, inter)
     bf16 = prec_mode == PREC_FP8_DOWN_BF16 and which == 2
+    if which == 3:
+        xm = np.zeros(hidden, dtype=np.float32)
+        _check(lib().ocq_unpack_weights_host(blob.ctypes.data, blob.nbytes, 3, None, xm.ctypes.data, None))
+        return None, xm, 0.0
     codes = np.zeros((rows, cols), dtype=np.uint16 if bf16 else np.uint8)
     if prec_mode == PREC_FP4:
         scales = np.zeros((rows, cols // 16), dtype=np.uint8)
@@ -138,8 +164,9 @@ def _stream_handle(stream):
     return getattr(stream, "cuda_stream", stream)
 
 
-def pack_weights(w_gate, w_up, w_down, prec_mode, device="cuda", stream=None):
-    """Quantize + pack and upload; returns a uint8 torch tensor on `device`."""
+def pack_weights(w_gate, w_up, w_down, prec_mode, device="cuda", stream=None, smooth=None):
+    """Quantize + pack and upload; returns a uint8 torch tensor on `device`.
+    smooth: None or per-input-channel factors (float32 [hidden])."""
     import torch
     wg, wu, wd = _f32c(w_gate), _f32c(w_up), _f32c(w_down)
     inter, hidden = wg.shape
@@ -147,8 +174,10 @@ def pack_weights(w_gate, w_up, w_down, prec_mode, device="cuda", stream=None):
     if n == 0:
         raise OcqError(ERR_UNSUPPORTED, "invalid shape or prec_mode")
     blob = torch.empty(n, dtype=torch.uint8, device=device)
-    _check(lib().ocq_pack_weights(wg.ctypes.data, wu.ctypes.data, wd.ctypes.data, hidden, inter, prec_mode,
-                                  blob.data_ptr(), n, _stream_handle(stream)))
+    sm = None if smooth is None else _f32c(smooth)
+    _check(lib().ocq_pack_weights_smoothed(wg.ctypes.data, wu.ctypes.data, wd.ctypes.data,
+                                           None if sm is None else sm.ctypes.data, hidden, inter, prec_mode,
+                                           blob.data_ptr(), n, _stream_handle(stream)))
     return blob
 
 

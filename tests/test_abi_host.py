@@ -178,3 +178,51 @@ def test_stack_argument_errors():
     assert _stack(x=None) == ocq.ERR_INVALID_ARG
     assert _stack(nws=1000) == ocq.ERR_BUFFER_TOO_SMALL
     assert "workspace" in ocq.last_error()
+
+
+def test_calibration_matches_oracle():
+    d = I.make_inputs(384, 640, 40, x_outliers=True, w_std=0.03, seed=9)
+    for alpha in (0.0, 0.35, 0.5, 1.0):
+        s_lib = ocq.calibrate_smoothing(d["x_bits"], d["w_gate"], d["w_up"], alpha)
+        s_ref = O.calibrate_smoothing(d["x_bits"], d["w_gate"], d["w_up"], alpha)
+        assert np.array_equal(s_lib, s_ref), alpha
+
+
+@pytest.mark.parametrize("prec", [0, 1, 2])
+def test_smoothed_packer_matches_oracle(prec):
+    d = I.make_inputs(256, 512, 32, x_outliers=True, w_std=0.02, seed=prec + 4)
+    s = O.calibrate_smoothing(d["x_bits"], d["w_gate"], d["w_up"], 0.5)
+    blob = ocq.pack_weights_host(d["w_gate"], d["w_up"], d["w_down"], prec, smooth=s)
+    ref = O.pack_block(d["w_gate"], d["w_up"], d["w_down"], prec, smooth=s)
+    for which, key in enumerate(("gate", "up", "down")):
+        codes, scales, ts = ocq.unpack_weights_host(blob, which, 256, 512, prec)
+        r = ref[key]
+        if prec == O.PREC_FP4:
+            assert np.array_equal(codes, r[0]) and np.array_equal(scales, r[1]) and np.float32(ts) == r[2], key
+        elif prec == O.PREC_FP8_DOWN_BF16 and key == "down":
+            assert np.array_equal(codes, r), key
+        else:
+            assert np.array_equal(codes, r[0]) and np.array_equal(scales, r[1]), key
+    _, xmul, _ = ocq.unpack_weights_host(blob, 3, 256, 512, prec)
+    assert np.array_equal(xmul, ref["xmul"])
+    plain = ocq.pack_weights_host(d["w_gate"], d["w_up"], d["w_down"], prec)
+    assert np.all(ocq.unpack_weights_host(plain, 3, 256, 512, prec)[1] == 1.0)
+
+
+def test_smoothing_argument_errors():
+    L = ocq.lib()
+    w = np.zeros((512, 256), np.float32)
+    x = np.zeros((4, 256), np.uint16)
+    s = np.ones(256, np.float32)
+    out = np.zeros(ocq.packed_bytes(256, 512, 0), np.uint8)
+    assert L.ocq_calibrate_smoothing_host(x.ctypes.data, 4, 256, w.ctypes.data, w.ctypes.data, 512, 1.5,
+                                          s.ctypes.data) == ocq.ERR_INVALID_ARG
+    assert L.ocq_calibrate_smoothing_host(x.ctypes.data, 0, 256, w.ctypes.data, w.ctypes.data, 512, 0.5,
+                                          s.ctypes.data) == ocq.ERR_INVALID_ARG
+    bad = s.copy()
+    bad[7] = 0.0
+    assert L.ocq_pack_weights_smoothed_host(w.ctypes.data, w.ctypes.data, w.T.copy().ctypes.data, bad.ctypes.data,
+                                            256, 512, 0, out.ctypes.data, out.nbytes) == ocq.ERR_INVALID_ARG
+    bad[7] = np.inf
+    assert L.ocq_pack_weights_smoothed_host(w.ctypes.data, w.ctypes.data, w.T.copy().ctypes.data, bad.ctypes.data,
+                                            256, 512, 0, out.ctypes.data, out.nbytes) == ocq.ERR_INVALID_ARG

@@ -86,6 +86,24 @@ def test_small_shapes(hidden, inter, M, prec):
     compare(g, r, prec, what="%dx%d M=%d prec=%d" % (hidden, inter, M, prec))
 
 
+# blobs packed with activation-aware smoothing (factors calibrated on a
+# separate draw with the same outlier channels): x is multiplied per channel
+# before its quantization; the small shapes, the LDS-tiled kernels (420 rows)
+# and the plain decode workload's shape
+@pytest.mark.parametrize("prec", [0, 1, 2])
+@pytest.mark.parametrize("hidden,inter,M", [(256, 512, 37), (256, 768, 420), (2048, 6144, 16)])
+def test_smoothed_blobs(hidden, inter, M, prec):
+    print("case smoothed hidden=%d inter=%d M=%d prec=%d" % (hidden, inter, M, prec), flush=True)
+    d = I.make_inputs(hidden, inter, M, x_outliers=True, w_std=0.02, seed=hidden + M + prec)
+    xc = np.random.default_rng(M + 1).standard_normal((64, hidden), dtype=np.float32)
+    xc[:, d["outliers"]] *= np.float32(20.0)
+    sm = O.calibrate_smoothing(I.to_bf16_bits(xc), d["w_gate"], d["w_up"], 0.5)
+    blob = ocq.pack_weights(d["w_gate"], d["w_up"], d["w_down"], prec, smooth=sm)
+    g, _ = run_gpu(d, prec, blob=blob)
+    r = O.forward(d["x_bits"], O.pack_block(d["w_gate"], d["w_up"], d["w_down"], prec, smooth=sm))
+    compare(g, r, prec, what="smoothed %dx%d M=%d prec=%d" % (hidden, inter, M, prec))
+
+
 _PACK_CACHE = {}
 
 

@@ -313,6 +313,49 @@ __device__ __forceinline__ void ks_mainloop_roll(const LanePtrs& p, int kidx, in
   }
 }
 
+// ---------------------------------------------------------------- gate/up epilogue
+
+// Epilogue of one 16x16 gate/up tile pair for one m-tile: v = accumulated tile (gate
+// in lanes r < 8, up in lanes r + 8 of each 16-lane row, rows 4 gq + i),
+// m_base = first row of the m-tile, n = column of h.  One DPP exchange gives
+// gate lane r the up values of rows 0, 2 and up lane r + 8 the gate values of
+// rows 1, 3, so every lane evaluates two of the four h values: value e is row
+// 4 gq + 2 e (gate lanes) or 4 gq + 2 e + 1 (up lanes).  Each 16-lane group
+// then stores two adjacent rows of the tile's 8 columns: 64 contiguous bytes
+// of the [tile][row][8] h32 block.  amax[e] accumulates |h| of value e.
+// SKIP_PAD: rows >= M (padding, never read back) store no h32.
+template <bool BF16H, int T, bool SKIP_PAD = false>
+__device__ __forceinline__ void gateup_tile_epilogue(const GateUpArgs& g, const v4f v, const v4f xs,
+                                                     float cg, float cu, int m_base, int ng, int t,
+                                                     float (&amax)[2]) {
+  const int lane = threadIdx.x & 63, gq = lane >> 4, r = lane & 15;
+  const bool lo = r < 8;
+  const int c = r & 7, n = (ng * T + t) * 8 + c;
+  // gate lanes send G of rows 1, 3 and receive U of rows 0, 2
+  const float p0 = dpp<0x128>(lo ? v[1] : v[0]);
+  const float p1 = dpp<0x128>(lo ? v[3] : v[2]);
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    // row 2e (gate lanes) or 2e + 1 (up lanes): selects, not a lane-dependent
+    // array index, which would put xs and v in scratch memory
+    const int i = 2 * e + (lo ? 0 : 1);
+    const float vi = lo ? v[2 * e] : v[2 * e + 1];
+    const float xi = lo ? xs[2 * e] : xs[2 * e + 1];
+    const float gv = lo ? vi : (e ? p1 : p0);
+    const float uv = lo ? (e ? p1 : p0) : vi;
+    const float hv = silu(gv * xi * cg) * (uv * xi * cu);
+    const int m = m_base + 4 * gq + i;
+    if constexpr (BF16H) {
+      const uint16_t hb = (uint16_t)bf16_bits(hv);
+      g.hb[frag_off16(m, n, g.I / 128)] = hb;
+      if (g.tap_hb && m < g.M) g.tap_hb[(size_t)m * g.I + n] = hb;
+    } else {
+      if (!SKIP_PAD || m < g.M) g.h32[((size_t)(ng * T + t) * g.Mpad + m) * 8 + c] = hv;
+      amax[e] = fmaxf(amax[e], fabsf(hv));
+    }
+  }
+}
+
 // LDS partial tiles [wave][pair][lane], 16 B each (one ds_write_b128 per
 // tile); returns after a workgroup barrier
 template <int MT, int T>

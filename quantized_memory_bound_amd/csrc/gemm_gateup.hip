@@ -46,46 +46,6 @@ __device__ __forceinline__ void load_epi(EpiScales<Q, T>& e, const GateUpArgs& g
   }
 }
 
-// Epilogue of one 16x16 tile pair for one m-tile: v = accumulated tile (gate
-// in lanes r < 8, up in lanes r + 8 of each 16-lane row, rows 4 gq + i),
-// m_base = first row of the m-tile, n = column of h.  One DPP exchange gives
-// gate lane r the up values of rows 0, 2 and up lane r + 8 the gate values of
-// rows 1, 3, so every lane evaluates two of the four h values: value e is row
-// 4 gq + 2 e (gate lanes) or 4 gq + 2 e + 1 (up lanes).  Each 16-lane group
-// then stores two adjacent rows of the tile's 8 columns: 64 contiguous bytes
-// of the [tile][row][8] h32 block.  amax[e] accumulates |h| of value e.
-template <bool BF16H, int T>
-__device__ __forceinline__ void gateup_tile_epilogue(const GateUpArgs& g, const v4f v, const v4f xs,
-                                                     float cg, float cu, int m_base, int ng, int t,
-                                                     float (&amax)[2]) {
-  const int lane = threadIdx.x & 63, gq = lane >> 4, r = lane & 15;
-  const bool lo = r < 8;
-  const int c = r & 7, n = (ng * T + t) * 8 + c;
-  // gate lanes send G of rows 1, 3 and receive U of rows 0, 2
-  const float p0 = dpp<0x128>(lo ? v[1] : v[0]);
-  const float p1 = dpp<0x128>(lo ? v[3] : v[2]);
-#pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    // row 2e (gate lanes) or 2e + 1 (up lanes): selects, not a lane-dependent
-    // array index, which would put xs and v in scratch memory
-    const int i = 2 * e + (lo ? 0 : 1);
-    const float vi = lo ? v[2 * e] : v[2 * e + 1];
-    const float xi = lo ? xs[2 * e] : xs[2 * e + 1];
-    const float gv = lo ? vi : (e ? p1 : p0);
-    const float uv = lo ? (e ? p1 : p0) : vi;
-    const float hv = silu(gv * xi * cg) * (uv * xi * cu);
-    const int m = m_base + 4 * gq + i;
-    if constexpr (BF16H) {
-      const uint16_t hb = (uint16_t)bf16_bits(hv);
-      g.hb[frag_off16(m, n, g.I / 128)] = hb;
-      if (g.tap_hb && m < g.M) g.tap_hb[(size_t)m * g.I + n] = hb;
-    } else {
-      g.h32[((size_t)(ng * T + t) * g.Mpad + m) * 8 + c] = hv;
-      amax[e] = fmaxf(amax[e], fabsf(hv));
-    }
-  }
-}
-
 // workgroup -> (m-block, column group); groups shared by several m-blocks are
 // numbered 8 apart (one XCD under round-robin placement) when possible
 __device__ __forceinline__ void gateup_block(const GateUpArgs& g, int ngroups, int& mb, int& ng) {
@@ -126,13 +86,62 @@ __global__ __launch_bounds__(64 * MS * KS) void ks_gateup(GateUpArgs g) {
   // latency is hidden behind it (after it for the loop with padding chunks,
   // which has no registers to spare)
   constexpr int NW = MS * KS, Q = (MT + NW - 1) / NW;
+  constexpr bool SPLIT = MS == 1 && MT * T <= NW;   // one (m-tile, tile) pair per wave
   EpiScales<Q, T> es;
   auto q_of = [&](int j) { return wave + NW * j < MT ? wave + NW * j : wave; };
-  if constexpr (D != -1) load_epi<BF, Q, T>(es, g, row0, ng * T, q_of);
+  if constexpr (D != -1 && !SPLIT) load_epi<BF, Q, T>(es, g, row0, ng * T, q_of);
+  // SPLIT: this wave's pair (m-tile sq, tile st) and its scales
+  const int sq = SPLIT && wave < MT * T ? wave / T : 0, st = SPLIT && wave < MT * T ? wave % T : 0;
+  v4f sxs = v4f{0.f, 0.f, 0.f, 0.f};
+  float scg = 0.f, scu = 0.f;
+  if constexpr (SPLIT) {
+    if (wave < MT * T) {
+      if constexpr (BF == kB_FP4_F16) {
+        scg = g.tscales[0];
+        scu = g.tscales[1];
+      } else {
+        scg = g.wscales[(ng * T + st) * 8 + (lane & 7)];
+        scu = g.wscales[g.I + (ng * T + st) * 8 + (lane & 7)];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sxs[i] = g.sx[row0 + sq * 16 + 4 * (lane >> 4) + i];
+    }
+  }
   if constexpr (D == -1) ks_mainloop_roll<BF, MTW, T, KS, false>(lp, kidx, 0, C, acc);
   else if constexpr (D < -1) ks_mainloop_roll<BF, MTW, T, KS, true, -D>(lp, kidx, 0, C, acc);
   else ks_mainloop<BF, MTW, T, KS, D>(lp, kidx, 0, C, acc);
 
+  if constexpr (SPLIT) {
+    // Few (m-tile, tile) pairs: all partial tiles go through LDS at once
+    // ([wave][m-tile][tile][lane]) and wave i finishes pair i, writing its
+    // rows' maxima over that tile's 8 columns (I / 8 partials per row).
+    const int I8 = g.I / 8;
+#pragma unroll
+    for (int j = 0; j < MT; ++j)
+#pragma unroll
+      for (int t = 0; t < T; ++t) red4[((wave * MT + j) * T + t) * 64 + lane] = acc[j][t];
+    lds_barrier();
+    if (wave < MT * T) {
+      const int q = sq, t = st;
+      v4f v = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) v += red4[((ks * MT + q) * T + t) * 64 + lane];
+      const int n0 = ng * T + t;
+      float am[2] = {0.f, 0.f};
+      // padding rows (>= M) are never read back: their h is not stored
+      gateup_tile_epilogue<BF16H, 1, true>(g, v, sxs, scg, scu, row0 + q * 16, n0, 0, am);
+      if constexpr (!BF16H) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) am[e] = max8(am[e]);
+        if ((lane & 7) == 0) {
+          const int m = row0 + q * 16 + 4 * (lane >> 4) + ((lane & 8) ? 1 : 0);
+#pragma unroll
+          for (int e = 0; e < 2; ++e) g.amax_part[(size_t)(m + 2 * e) * I8 + n0] = am[e];
+        }
+      }
+    }
+    return;
+  }
   // Epilogue, one wave per m-tile (rows are owned by exactly one wave, so the
   // row maxima need no cross-wave combination).  The partial tiles go through
   // LDS one weight tile t at a time ([wave][m-tile][lane] 16 B each, NW * MTW
@@ -187,7 +196,7 @@ template <int BF, bool BF16H, int MT, int T, int MS, int KS, int D>
 hipError_t launch_ks(const GateUpArgs& g, int grid, hipStream_t st, const LaunchEvents& ev) {
   constexpr int MTW = (MT + MS - 1) / MS;
   auto fn = ks_gateup<BF, MT, T, MS, KS, D, BF16H>;
-  const size_t lds = (size_t)(T > 1 ? 2 : 1) * MS * KS * MTW * 64 * sizeof(v4f);
+  const size_t lds = (size_t)(MS == 1 && MT * T <= MS * KS ? T : (T > 1 ? 2 : 1)) * MS * KS * MTW * 64 * sizeof(v4f);
   static bool attr = false;   // idempotent; a race only repeats the call
   if (!attr) {
     hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

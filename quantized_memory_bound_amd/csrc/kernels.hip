@@ -164,8 +164,21 @@ __global__ __launch_bounds__(kThreads) void k_requant(const float* __restrict__ 
   const int k = (xb * kThreads + threadIdx.x) * 4;
   const bool has = k < I;
   const v4f v = has ? *(const v4f*)(h32 + ((size_t)(k / 8) * Mpad + m) * 8 + k % 8) : v4f{0.f, 0.f, 0.f, 0.f};
+  // up to 8 partials per thread requested together
   float a = 0.0f;
-  for (int g = threadIdx.x; g < ngroups; g += kThreads) a = fmaxf(a, amax_part[(size_t)m * ngroups + g]);
+  const float* ap = amax_part + (size_t)m * ngroups;
+  if (ngroups <= kThreads) {
+    if (threadIdx.x < ngroups) a = ap[threadIdx.x];
+  } else for (int g0 = 0; g0 < ngroups; g0 += 8 * kThreads) {
+    float t[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int g = g0 + u * kThreads + threadIdx.x;
+      t[u] = g < ngroups ? ap[g] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) a = fmaxf(a, t[u]);
+  }
   a = wave_max(a);
   if (lane == 0) s_max[wave] = a;
   __syncthreads();
@@ -233,7 +246,7 @@ int launch_forward(const Plan& p, const FwdArgs& a) {
   if (!bf16_down) {
     hipLaunchKernelGGL(k_requant, dim3(tile_row_grid(p.Mpad / 16, (p.inter + 1023) / 1024)), dim3(kThreads), 0, st,
                        h32, amax_part,
-                       p.ngroups1, p.M, p.Mpad, p.inter, hq, sh, (uint8_t*)a.taps.h_out,
+                       p.namax, p.M, p.Mpad, p.inter, hq, sh, (uint8_t*)a.taps.h_out,
                        (float*)a.taps.h_scales);
     e = hipGetLastError();
     if (e != hipSuccess) return (int)e;

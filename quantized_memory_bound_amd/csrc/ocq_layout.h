@@ -127,12 +127,21 @@ struct Plan {
   // down kernel: n_mb2 m-blocks of MT2 m-tiles x ngroups2 groups of T2 tiles,
   // every workgroup over the whole input range
   int MT2, n_mb2, T2, ngroups2;
-  // LDS-tiled kernels selected (gate/up, down); then ngroups1 counts the
-  // partial row maxima per row (workgroups x wave columns)
+  // LDS-tiled kernels selected (gate/up, down)
   int lg1, lg2;
+  // partial maxima of |h| per row written by the gate/up kernel: one per
+  // workgroup, per wave column (LDS-tiled kernel) or per tile (epilogue
+  // split over the waves, see epi_split)
+  int namax;
   // workspace offsets (xq, hq, hb are fragment-ordered operand buffers of Mpad rows)
   size_t off_xq, off_sx, off_amax, off_h32, off_hq, off_hb, off_sh, total;
 };
+
+// Gate/up epilogue with one (m-tile, tile) pair per wave: when a workgroup of
+// eight K-split waves holds at most eight such pairs, each wave finishes one
+// of them (and writes its own partial row maxima) instead of one wave
+// finishing all of them in turn.
+inline bool epi_split(int MT, int T) { return MT * T <= 8; }
 
 inline int pick_mt(int M) {
   int need = (M + 15) / 16;
@@ -185,6 +194,7 @@ inline Plan make_plan(int M, int hidden, int inter, int prec) {
     if (nt1 % t == 0 && nt1 / t >= 192) { p.T1 = t; break; }
   }
   p.ngroups1 = nt1 / p.T1;
+  p.namax = epi_split(p.MT, p.T1) ? nt1 : p.ngroups1;
   pick_down(p);
   const bool many = M >= kLgMinRows;
   p.lg1 = many && (prec == kFP8 || prec == kFP8DownBF16) && nt1 % kLgRT1 == 0 && hidden >= 256;
@@ -192,7 +202,8 @@ inline Plan make_plan(int M, int hidden, int inter, int prec) {
     p.MT = kLgRM;
     p.n_mblocks = (M + 16 * kLgRM - 1) / (16 * kLgRM);
     p.T1 = kLgRT1;
-    p.ngroups1 = nt1 / kLgRT1 * kLgWT1;
+    p.ngroups1 = nt1 / kLgRT1;
+    p.namax = p.ngroups1 * kLgWT1;
   }
   p.lg2 = many && prec == kFP8DownBF16 && (hidden / 16) % kLgRT2 == 0 && inter >= 256;
   if (p.lg2) {
@@ -208,7 +219,7 @@ inline Plan make_plan(int M, int hidden, int inter, int prec) {
   size_t o = 0;
   p.off_xq = o;   o = align_up(o + Mp * hidden * (p.lg1 ? 2 : 1));   // E4M3 codes, or their fp16 values
   p.off_sx = o;   o = align_up(o + Mp * 4);
-  p.off_amax = o; o = align_up(o + (size_t)p.ngroups1 * Mp * 4);   // per-workgroup row maxima of |h|
+  p.off_amax = o; o = align_up(o + (size_t)p.namax * Mp * 4);   // partial row maxima of |h|
   p.off_h32 = o;  o = align_up(o + (prec == kFP8DownBF16 ? 0 : Mp * inter * 4));   // [inter / 8][Mpad][8]
   p.off_hq = o;   o = align_up(o + (prec == kFP8DownBF16 ? 0 : Mp * inter));
   p.off_hb = o;   o = align_up(o + (prec == kFP8DownBF16 ? Mp * inter * 2 : 0));

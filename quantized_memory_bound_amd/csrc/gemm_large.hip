@@ -416,10 +416,11 @@ hipError_t lg_launch(void (*fn)(Arg), int grid, const Arg& arg, hipStream_t st, 
 // gate/up: 13 m-tiles x 12 tiles per workgroup; 2 x 4 waves of 7 m-tiles x 3
 // tiles, one weight unit position per stage (64 inputs), three stages (120 KB)
 using GUL = Lg<kB_FP8_F16, true, kLgRM, kLgRT1, 2, kLgWT1, 1, 1, 3>;
-// down: 13 m-tiles x 4 tiles per workgroup; 2 x 2 waves of 7 m-tiles x 2 tiles,
-// each pair of K-waves splitting the two unit positions of a stage (64
-// inputs), four stages (144 KB)
-using GDL = Lg<kB_BF16, true, kLgRM, kLgRT2, 2, 2, 2, 2, 4>;
+// down: 7 m-tiles x 8 tiles per workgroup (112 rows x 128 columns: more
+// multiply-adds per staged byte than 208 x 64); 1 x 4 waves of 7 m-tiles x 2
+// tiles, each pair of K-waves splitting the two unit positions of a stage (64
+// inputs), four stages (120 KB)
+using GDL = Lg<kB_BF16, true, kLgRM2, kLgRT2, 1, 4, 2, 2, 4>;
 
 }  // namespace
 

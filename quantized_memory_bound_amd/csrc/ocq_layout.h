@@ -111,12 +111,12 @@ inline BlobLayout blob_layout(int hidden, int inter, int prec) {
 constexpr int kMTChoices[] = {1, 2, 4, 7, 13};
 constexpr int kMTMax = 13;
 
-// LDS-tiled kernels for many rows (both projections' m-blocks are kLgRM
-// m-tiles); chosen from kLgMinRows rows on
-constexpr int kLgRM = 13;        // m-tiles per workgroup
+// LDS-tiled kernels for many rows; chosen from kLgMinRows rows on
+constexpr int kLgRM = 13;        // gate/up: m-tiles per workgroup
 constexpr int kLgRT1 = 12;       // gate/up: interleaved tiles per workgroup
 constexpr int kLgWT1 = 4;        // gate/up: wave columns (partial row maxima per workgroup)
-constexpr int kLgRT2 = 4;        // down: output tiles per workgroup
+constexpr int kLgRT2 = 8;        // down: output tiles per workgroup
+constexpr int kLgRM2 = 7;        // down: m-tiles per workgroup
 constexpr int kLgMinRows = 384;
 
 struct Plan {
@@ -207,9 +207,9 @@ inline Plan make_plan(int M, int hidden, int inter, int prec) {
   }
   p.lg2 = many && prec == kFP8DownBF16 && (hidden / 16) % kLgRT2 == 0 && inter >= 256;
   if (p.lg2) {
-    p.MT2 = kLgRM;
+    p.MT2 = kLgRM2;
     p.T2 = kLgRT2;
-    p.n_mb2 = (M + 16 * kLgRM - 1) / (16 * kLgRM);
+    p.n_mb2 = (M + 16 * kLgRM2 - 1) / (16 * kLgRM2);
     p.ngroups2 = hidden / 16 / kLgRT2;
   }
   const int rows1 = p.n_mblocks * 16 * p.MT, rows2 = p.n_mb2 * 16 * p.MT2;

@@ -200,6 +200,26 @@ def test_deterministic_and_zero_rows(prec):
     compare(g1, r, prec, what="zero rows prec=%d" % prec)
 
 
+# the block is row-wise: the first 13 rows of a 208-row call (13 m-tiles per
+# workgroup) against a 13-row call on the same rows (one m-tile per
+# workgroup), and a 13-row call against a 16-row call (the same blocking, so
+# padding rows must not leak into real ones: bit-exact)
+@pytest.mark.parametrize("prec", [0, 1, 2])
+def test_row_independence(prec):
+    print("case row independence prec=%d" % prec, flush=True)
+    d = I.make_inputs(512, 1024, 208, x_outliers=True, seed=21)
+    blob = ocq.pack_weights(d["w_gate"], d["w_up"], d["w_down"], prec)
+    g208, _ = run_gpu(d, prec, blob=blob)
+    g13, _ = run_gpu(d, prec, blob=blob, x_bits=d["x_bits"][:13])
+    g16, _ = run_gpu(d, prec, blob=blob, x_bits=d["x_bits"][:16])
+    assert np.array_equal(g13["xq"], g208["xq"][:13]) and np.array_equal(g13["sx"], g208["sx"][:13])
+    assert np.array_equal(g13["y"], g16["y"][:13]), "rows 13..15 changed rows 0..12"
+    r = O.block_reference(d["x_bits"][:13], d["w_gate"], d["w_up"], d["w_down"], prec)
+    compare(g13, r, prec, what="M=13 prec=%d" % prec)
+    compare(g208, r, prec, rows=slice(0, 13), what="M=208 rows 0..12 prec=%d" % prec)
+    check_y(g208["y"][:13], g13["y"], "y of rows 0..12, M=208 against M=13")
+
+
 # row counts at the edges of the kernel choice (383 and 384 rows: the last
 # skinny shape and the first LDS-tiled one) and the largest M the ABI takes
 # (8192 rows: 40 m-blocks of 208 in the LDS-tiled kernels); the oracle runs on

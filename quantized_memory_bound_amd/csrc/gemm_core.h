@@ -343,7 +343,8 @@ __device__ __forceinline__ void gateup_tile_epilogue(const GateUpArgs& g, const 
     const float xi = lo ? xs[2 * e] : xs[2 * e + 1];
     const float gv = lo ? vi : (e ? p1 : p0);
     const float uv = lo ? (e ? p1 : p0) : vi;
-    const float hv = silu(gv * xi * cg) * (uv * xi * cu);
+    const float ga = gv * xi * cg;
+    const float hv = (BF16H ? silu(ga) : silu_rcp(ga)) * (uv * xi * cu);
     const int m = m_base + 4 * gq + i;
     if constexpr (BF16H) {
       const uint16_t hb = (uint16_t)bf16_bits(hv);

@@ -335,7 +335,8 @@ __global__ __launch_bounds__(G::THREADS) void lg_gateup(GateUpArgs g) {
         const float xi = lo ? xs[2 * e] : xs[2 * e + 1];
         const float gv = lo ? vi : (e ? p1 : p0);
         const float uv = lo ? (e ? p1 : p0) : vi;
-        const float hv = silu(gv * xi * cg[t]) * (uv * xi * cu[t]);
+        const float ga = gv * xi * cg[t];
+        const float hv = (BF16H ? silu(ga) : silu_rcp(ga)) * (uv * xi * cu[t]);
         const int m = m_base + i;
         if constexpr (BF16H) {
           const uint16_t hb = (uint16_t)bf16_bits(hv);

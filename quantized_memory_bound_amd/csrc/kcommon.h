@@ -140,6 +140,12 @@ __device__ __forceinline__ void e4m3x2_scales(uint32_t two, v2h& s0, v2h& s1) {
 // e^-g overflowing to +inf gives -0 for very negative g.
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 
+// SiLU through the hardware reciprocal (about one unit in the last place):
+// for h that is requantized to E4M3, whose 3-bit mantissa makes such a
+// difference change a code only right next to a rounding midpoint.  The bf16
+// h of a BF16 down projection (8-bit mantissa) keeps the exact division.
+__device__ __forceinline__ float silu_rcp(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
+
 // Cross-lane moves inside 16-lane rows through DPP (no LDS round trip).
 // CTRL: 0x128 row_ror:8 (lane r <- r ^ 8), 0xB1 quad_perm [1,0,3,2] (r ^ 1),
 // 0x4E quad_perm [2,3,0,1] (r ^ 2), 0x141 row_half_mirror (r <- 7 - r in

@@ -101,6 +101,42 @@ __device__ __forceinline__ uint32_t enc_e4m3(float v) {
   return sign | c;
 }
 
+// Eight E4M3 codes of fl32(v[j] / s) for s > 0 with rcp = fl32(1 / s), two
+// dwords in element order: the same codes as enc_e4m3(v[j] / s).
+//   * q = v rcp is within 2.5 units in the last place of fl32(v / s) (two
+//     roundings of relative size 2^-24 each), so both round to the same E4M3
+//     code unless a decision boundary lies that close: in the normal range a
+//     midpoint has low 20 mantissa bits 0x80000 (tested with a window of
+//     +-3 units); in the subnormal range (|q| < 2^-6, grid 2^-9) a midpoint
+//     is an odd multiple of 2^-10, i.e. fract(|q| 2^9) = 1/2 (tested with a
+//     window of 2^-19, more than 2.5 units there).  If any of the eight is
+//     that close, all eight take the exact quotient (one branch, rarely taken).
+//   * Clamped to +-448, the hardware conversion (nearest even, sign kept for
+//     zero) gives the saturating code; checked equal to enc_e4m3 on every
+//     midpoint +-3 units, the subnormals, both zeros and random values.
+__device__ __forceinline__ v2u e4m3x8_quot(const float (&v)[8], float s, float rcp) {
+  float q[8];
+  bool near = false;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    q[j] = v[j] * rcp;
+    const float t = fabsf(q[j]) * 512.0f;
+    near |= (t < 8.0f) & (fabsf(__builtin_amdgcn_fractf(t) - 0.5f) < 0x1p-19f);
+    near |= (__float_as_uint(q[j]) & 0xFFFFFu) - 0x7FFFDu <= 6u;
+  }
+  if (near) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) q[j] = v[j] / s;
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) q[j] = __builtin_amdgcn_fmed3f(q[j], -448.0f, 448.0f);
+  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], lo, true);
+  int hi = __builtin_amdgcn_cvt_pk_fp8_f32(q[4], q[5], 0, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(q[6], q[7], hi, true);
+  return v2u{(uint32_t)lo, (uint32_t)hi};
+}
+
 __device__ __forceinline__ uint32_t bf16_bits(float v) {   // round to nearest even (finite v)
   const uint32_t u = __float_as_uint(v);
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;

@@ -99,6 +99,7 @@ __global__ __launch_bounds__(kThreads) void k_xquant(const uint16_t* __restrict_
   __syncthreads();
   amax = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
   const float s = amax / 448.0f;
+  const float rcp = s > 0.0f ? 1.0f / s : 0.0f;
   for (int base = 0; base < H; base += kThreads * 8 * kReg) {
     if (base > 0 || H > kThreads * 8 * kReg) {      // reload unless the whole row is still in registers
 #pragma unroll
@@ -114,14 +115,16 @@ __global__ __launch_bounds__(kThreads) void k_xquant(const uint16_t* __restrict_
       uint32_t out[2] = {0u, 0u};
       if (s > 0.0f) {
         const v4f m0 = *(const v4f*)(xmul + k), m1 = *(const v4f*)(xmul + k + 4);
+        float p[8];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const uint32_t w = (uint32_t)v[j][q];
-          const float ma = q < 2 ? m0[2 * q] : m1[2 * q - 4], mb = q < 2 ? m0[2 * q + 1] : m1[2 * q - 3];
-          const uint32_t c0 = enc_e4m3(__uint_as_float(w << 16) * ma / s);
-          const uint32_t c1 = enc_e4m3(__uint_as_float(w & 0xFFFF0000u) * mb / s);
-          out[q >> 1] |= (c0 | (c1 << 8)) << (16 * (q & 1));
+          p[2 * q] = __uint_as_float(w << 16) * (q < 2 ? m0[2 * q] : m1[2 * q - 4]);
+          p[2 * q + 1] = __uint_as_float(w & 0xFFFF0000u) * (q < 2 ? m0[2 * q + 1] : m1[2 * q - 3]);
         }
+        const v2u c = e4m3x8_quot(p, s, rcp);
+        out[0] = c[0];
+        out[1] = c[1];
       }
       if (f16) *(v8h*)((uint16_t*)xq + frag_off16(m, k, C)) = e4m3x8_to_f16(out[0], out[1]);
       else *(v2u*)(xq + frag_off8(m, k, C)) = v2u{out[0], out[1]};
@@ -137,12 +140,14 @@ __global__ __launch_bounds__(kThreads) void k_xquant(const uint16_t* __restrict_
 // ---------------------------------------------------------------- k_requant
 
 // amax_part[m][g] holds the |h| maximum of row m over the columns of gate/up
-// workgroup g; every block first reduces the row's ngroups partial maxima.
+// partial g; every block first reduces the row's ngroups partial maxima.
 // Rows M..Mpad-1 (padding, possibly beyond the gate/up m-blocks) get zero
-// codes and scale 0 without reading h.
-// Codes go to the fragment-ordered operand buffer of the down projection (4
-// consecutive inputs = 4 contiguous bytes there).  tap_q / tap_s (nullable)
-// receive the plain [M][I] codes and [M] scales.
+// codes and scale 0 without reading h.  Each thread quantizes 8 consecutive
+// columns (one 32-byte piece of an 8-column h32 tile) into 8 contiguous bytes
+// of the fragment-ordered operand buffer of the down projection.  tap_q /
+// tap_s (nullable) receive the plain [M][I] codes and [M] scales.
+constexpr int kRqCols = 8 * kThreads;   // columns of a row per workgroup
+
 __global__ __launch_bounds__(kThreads) void k_requant(const float* __restrict__ h32,
                                                       const float* __restrict__ amax_part, int ngroups, int M,
                                                       int Mpad, int I, uint8_t* __restrict__ hq,
@@ -152,18 +157,21 @@ __global__ __launch_bounds__(kThreads) void k_requant(const float* __restrict__ 
   int m, xb;
   if (!tile_row_of(blockIdx.x, Mpad / 16, m, xb)) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int k = xb * kRqCols + threadIdx.x * 8;
+  const bool has = k < I;
   if (m >= M) {
     if (xb == 0 && threadIdx.x == 0) sh[m] = 0.0f;
-    const int k = (xb * kThreads + threadIdx.x) * 4;
-    if (k < I) *(uint32_t*)(hq + frag_off8(m, k, I / 128)) = 0u;
+    if (has) *(v2u*)(hq + frag_off8(m, k, I / 128)) = v2u{0u, 0u};
     return;
   }
-  // this thread's 4 values of h are requested before the row maximum, so the
-  // two loads are in flight together.  h32 holds each 8-column tile of h as
-  // one [Mpad][8] block; 4 consecutive columns (k % 4 == 0) lie in one tile.
-  const int k = (xb * kThreads + threadIdx.x) * 4;
-  const bool has = k < I;
-  const v4f v = has ? *(const v4f*)(h32 + ((size_t)(k / 8) * Mpad + m) * 8 + k % 8) : v4f{0.f, 0.f, 0.f, 0.f};
+  // the thread's 8 values of h are requested before the row maximum, so the
+  // loads are in flight together (h32: each 8-column tile is a [Mpad][8] block)
+  v4f v0 = v4f{0.f, 0.f, 0.f, 0.f}, v1 = v0;
+  if (has) {
+    const float* src = h32 + ((size_t)(k / 8) * Mpad + m) * 8;
+    v0 = *(const v4f*)src;
+    v1 = *(const v4f*)(src + 4);
+  }
   // up to 8 partials per thread requested together
   float a = 0.0f;
   const float* ap = amax_part + (size_t)m * ngroups;
@@ -189,13 +197,13 @@ __global__ __launch_bounds__(kThreads) void k_requant(const float* __restrict__ 
     if (tap_s) tap_s[m] = s;
   }
   if (!has) return;
-  uint32_t out = 0u;
+  v2u out = v2u{0u, 0u};
   if (s > 0.0f) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) out |= enc_e4m3(v[j] / s) << (8 * j);
+    const float p[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+    out = e4m3x8_quot(p, s, 1.0f / s);
   }
-  *(uint32_t*)(hq + frag_off8(m, k, I / 128)) = out;
-  if (tap_q) *(uint32_t*)(tap_q + (size_t)m * I + k) = out;
+  *(v2u*)(hq + frag_off8(m, k, I / 128)) = out;
+  if (tap_q) *(v2u*)(tap_q + (size_t)m * I + k) = out;
 }
 
 }  // namespace
@@ -244,7 +252,8 @@ int launch_forward(const Plan& p, const FwdArgs& a) {
   if (e != hipSuccess) return (int)e;
 
   if (!bf16_down) {
-    hipLaunchKernelGGL(k_requant, dim3(tile_row_grid(p.Mpad / 16, (p.inter + 1023) / 1024)), dim3(kThreads), 0, st,
+    hipLaunchKernelGGL(k_requant, dim3(tile_row_grid(p.Mpad / 16, (p.inter + kRqCols - 1) / kRqCols)),
+                       dim3(kThreads), 0, st,
                        h32, amax_part,
                        p.namax, p.M, p.Mpad, p.inter, hq, sh, (uint8_t*)a.taps.h_out,
                        (float*)a.taps.h_scales);

@@ -220,6 +220,23 @@ def test_row_independence(prec):
     check_y(g208["y"][:13], g13["y"], "y of rows 0..12, M=208 against M=13")
 
 
+# one workspace for a sequence of calls: different rows each time, and a call
+# that takes the LDS-tiled kernels in between
+def test_workspace_reuse():
+    print("case workspace reuse", flush=True)
+    H, Iw, prec = 256, 768, 0
+    d = I.make_inputs(H, Iw, 420, x_outliers=True, seed=5)
+    blob = ocq.pack_weights(d["w_gate"], d["w_up"], d["w_down"], prec)
+    nws = max(ocq.workspace_bytes(m, H, Iw, prec) for m in (13, 16, 420))
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    for rows in (slice(0, 16), slice(16, 32), slice(0, 420), slice(100, 116), slice(200, 213), slice(0, 16)):
+        xb = np.ascontiguousarray(d["x_bits"][rows])
+        y = ocq.mlp_forward(blob, _to_dev_bf16(xb), H, Iw, prec, workspace=ws)
+        torch.cuda.synchronize()
+        r = O.block_reference(xb, d["w_gate"], d["w_up"], d["w_down"], prec)
+        check_y(y.view(torch.int16).cpu().numpy().view(np.uint16), r["y"], "rows %s" % rows)
+
+
 # row counts at the edges of the kernel choice (383 and 384 rows: the last
 # skinny shape and the first LDS-tiled one) and the largest M the ABI takes
 # (8192 rows: 40 m-blocks of 208 in the LDS-tiled kernels); the oracle runs on

@@ -219,7 +219,10 @@ hipError_t go(const GateUpArgs& g, int grid, hipStream_t st, const LaunchEvents&
   constexpr int KS = 8 / MS;
   constexpr int MTW = (MT + MS - 1) / MS;
   const int C = g.H / kChunk;
-  if constexpr (MTW <= 4) return launch_ks<BF, BF16H, MT, T, MS, KS, 2>(g, grid, st, ev);
+  // six NVFP4 tiles of 2-4 m-tiles: one chunk in flight per wave (two
+  // would not fit the registers of two waves per SIMD)
+  if constexpr (T == 6) return launch_ks<BF, BF16H, MT, T, MS, KS, 1>(g, grid, st, ev);
+  else if constexpr (MTW <= 4) return launch_ks<BF, BF16H, MT, T, MS, KS, 2>(g, grid, st, ev);
   else if (C == 4 * KS) return launch_ks<BF, BF16H, MT, T, MS, KS, -4>(g, grid, st, ev);
   else if (C == 8 * KS) return launch_ks<BF, BF16H, MT, T, MS, KS, -8>(g, grid, st, ev);
   else return launch_ks<BF, BF16H, MT, T, MS, KS, -1>(g, grid, st, ev);
@@ -231,6 +234,7 @@ hipError_t go_t(const GateUpArgs& g, int T, int grid, hipStream_t st, const Laun
     case 1: return go<BF, BF16H, MT, 1>(g, grid, st, ev);
     case 2: return go<BF, BF16H, MT, 2>(g, grid, st, ev);
     case 3: return go<BF, BF16H, MT, 3>(g, grid, st, ev);
+    case 6: if constexpr (BF == kB_FP4_F16 && (MT == 2 || MT == 4)) return go<BF, BF16H, MT, 6>(g, grid, st, ev);
   }
   return hipErrorInvalidValue;
 }

@@ -187,11 +187,13 @@ inline Plan make_plan(int M, int hidden, int inter, int prec) {
   int rows_per_block = 16 * p.MT;
   p.n_mblocks = (M + rows_per_block - 1) / rows_per_block;
   // gate/up: tiles of 8 gate + 8 up columns; 3 tiles per workgroup when that
-  // still gives >= 192 workgroups (one per CU at the configured sizes)
+  // still gives >= 192 workgroups (one per CU at the configured sizes); 6 for
+  // NVFP4 with 2-4 m-tiles, whose workgroups hold one per CU (512 workgroups of
+  // 3 tiles would run in two rounds)
   int nt1 = inter / 8;
   p.T1 = 1;
-  for (int t : {3, 2}) {
-    if (nt1 % t == 0 && nt1 / t >= 192) { p.T1 = t; break; }
+  for (int t : {6, 3, 2}) {
+    if (nt1 % t == 0 && nt1 / t >= 192 && (t < 6 || (prec == kFP4 && (p.MT == 2 || p.MT == 4)))) { p.T1 = t; break; }
   }
   p.ngroups1 = nt1 / p.T1;
   p.namax = epi_split(p.MT, p.T1) ? nt1 : p.ngroups1;

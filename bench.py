@@ -146,8 +146,8 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build measures one GPU; the block is row-independent and shards as data "
-              "parallel over requests with no exchange (see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py: measures one GPU only; the block is row-independent and shards as data "
+              "parallel over requests with no exchange between GPUs. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -113,9 +113,10 @@ __global__ __launch_bounds__(64 * MS * KS) void ks_gateup(GateUpArgs g) {
 
   if constexpr (SPLIT) {
     // Few (m-tile, tile) pairs: all partial tiles go through LDS at once
-    // ([wave][m-tile][tile][lane]) and wave i finishes pair i, writing its
-    // rows' maxima over that tile's 8 columns (I / 8 partials per row).
-    const int I8 = g.I / 8;
+    // ([wave][m-tile][tile][lane]) and wave i finishes pair i; the T waves of
+    // an m-tile then combine their rows' maxima in LDS, and the first of them
+    // writes one partial per row for the workgroup.
+    __shared__ float s_am[8][16];
 #pragma unroll
     for (int j = 0; j < MT; ++j)
 #pragma unroll
@@ -133,11 +134,21 @@ __global__ __launch_bounds__(64 * MS * KS) void ks_gateup(GateUpArgs g) {
       if constexpr (!BF16H) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) am[e] = max8(am[e]);
-        if ((lane & 7) == 0) {
-          const int m = row0 + q * 16 + 4 * (lane >> 4) + ((lane & 8) ? 1 : 0);
+        if ((lane & 7) == 0) {   // lane 16 gq (rows 0, 2) and 16 gq + 8 (rows 1, 3) of 4 gq ..
+          const int r = 4 * (lane >> 4) + ((lane & 8) ? 1 : 0);
 #pragma unroll
-          for (int e = 0; e < 2; ++e) g.amax_part[(size_t)(m + 2 * e) * I8 + n0] = am[e];
+          for (int e = 0; e < 2; ++e) s_am[wave][r + 2 * e] = am[e];
         }
+      }
+    }
+    if constexpr (!BF16H) {
+      lds_barrier();
+      if (wave < MT * T && st == 0 && lane < 16) {
+        float a = s_am[wave][lane];
+#pragma unroll
+        for (int t = 1; t < T; ++t) a = fmaxf(a, s_am[wave + t][lane]);
+        const int m = row0 + sq * 16 + lane;
+        if (m < g.M) g.amax_part[(size_t)m * ((g.I / 8) / T) + ng] = a;
       }
     }
     return;

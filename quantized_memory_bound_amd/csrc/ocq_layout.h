@@ -130,18 +130,11 @@ struct Plan {
   // LDS-tiled kernels selected (gate/up, down)
   int lg1, lg2;
   // partial maxima of |h| per row written by the gate/up kernel: one per
-  // workgroup, per wave column (LDS-tiled kernel) or per tile (epilogue
-  // split over the waves, see epi_split)
+  // workgroup (skinny kernels) or per wave column (LDS-tiled kernel)
   int namax;
   // workspace offsets (xq, hq, hb are fragment-ordered operand buffers of Mpad rows)
   size_t off_xq, off_sx, off_amax, off_h32, off_hq, off_hb, off_sh, total;
 };
-
-// Gate/up epilogue with one (m-tile, tile) pair per wave: when a workgroup of
-// eight K-split waves holds at most eight such pairs, each wave finishes one
-// of them (and writes its own partial row maxima) instead of one wave
-// finishing all of them in turn.
-inline bool epi_split(int MT, int T) { return MT * T <= 8; }
 
 inline int pick_mt(int M) {
   int need = (M + 15) / 16;
@@ -196,7 +189,7 @@ inline Plan make_plan(int M, int hidden, int inter, int prec) {
     if (nt1 % t == 0 && nt1 / t >= 192 && (t < 6 || (prec == kFP4 && (p.MT == 2 || p.MT == 4)))) { p.T1 = t; break; }
   }
   p.ngroups1 = nt1 / p.T1;
-  p.namax = epi_split(p.MT, p.T1) ? nt1 : p.ngroups1;
+  p.namax = p.ngroups1;
   pick_down(p);
   const bool many = M >= kLgMinRows;
   p.lg1 = many && (prec == kFP8 || prec == kFP8DownBF16) && nt1 % kLgRT1 == 0 && hidden >= 256;

@@ -201,6 +201,213 @@ __global__ __launch_bounds__(64 * MS * KS) void ks_gateup(GateUpArgs g) {
   }
 }
 
+// ---------------------------------------------------------------- 13 m-tiles, weights through LDS
+//
+// For one 208-row m-block of E4M3 weights the skinny kernel's waves stall on
+// the weight stream: a wave's loads complete in issue order, so the
+// activations it needs next wait behind the weights it requested earlier.
+// Here the roles are split.  Four producer waves (one per SIMD) stream the
+// workgroup's weight tiles into an LDS ring with direct-to-LDS loads, in
+// stages of 4 chunks, and publish each stage with a workgroup barrier after
+// their own loads of it have landed.  Eight consumer waves load only
+// activations (one chunk ahead, in registers), read the weights of a chunk
+// from LDS and run the MFMAs: wave (ms, kidx) holds m-tiles 0-3 (ms = 0) or
+// 1 + 3 ms .. 3 + 3 ms and the chunks kidx, kidx + 2, ...  Every barrier is
+// passed by all twelve waves in the same order: one per stage, one after the
+// main loop, one per weight tile in the epilogue.
+constexpr int kPcConsumers = 8, kPcProducers = 4, kPcSlots = 4;
+
+template <int T, int NS>
+struct Pc {
+  static constexpr int C = 4 * NS;                     // chunks of 128 inputs
+  static constexpr int NK = C / 2;                     // chunks per consumer wave
+  static constexpr int UPS = 8 * T;                    // weight units (1 KB) per stage
+  static constexpr int PPW = UPS / kPcProducers;       // loads per producer wave and stage
+  static constexpr int NSLOT = NS < kPcSlots ? NS : kPcSlots;
+  static constexpr int SLOT = UPS * 1024;
+  static constexpr int RED = kPcConsumers * 4 * 1024;  // epilogue partials of one weight tile
+  static constexpr int LDS = NSLOT * SLOT > 2 * RED ? NSLOT * SLOT : 2 * RED;
+  static_assert(UPS % kPcProducers == 0 && (NSLOT - 1) * PPW < 64, "loads per producer");
+  static_assert(LDS <= 160 * 1024, "LDS of one CU");
+};
+
+template <int T, int NS, bool BF16H>
+__device__ __forceinline__ void pc_producer(const GateUpArgs& g, uint8_t* lds, int ng, int p) {
+  using P = Pc<T, NS>;
+  const int lane = threadIdx.x & 63;
+  const size_t wt = (size_t)P::C * Fmt<kB_FP8_F16>::kGlobal;
+  const uint8_t* w = g.wcodes + (size_t)ng * T * wt + lane * 16;
+  auto issue = [&](int s) {
+    uint8_t* slot = lds + (s % P::NSLOT) * P::SLOT;
+#pragma unroll
+    for (int q = 0; q < P::PPW; ++q) {
+      const int x = p + q * kPcProducers;
+      const int cc = x / (2 * T), t = (x >> 1) % T, u = x & 1;
+      const uint8_t* src = w + t * wt + (size_t)(4 * s + cc) * Fmt<kB_FP8_F16>::kGlobal + u * 1024;
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(slot + x * 1024), 16, 0, 0);
+    }
+  };
+#pragma unroll
+  for (int s = 0; s < P::NSLOT; ++s) issue(s);
+  int hi = P::NSLOT;   // stages issued
+  for (int s = 0; s < NS; ++s) {
+    // stages s .. hi - 1 are outstanding: wait for stage s only
+    switch (hi - 1 - s) {
+      case 0: wait_vm<0>(); break;
+      case 1: wait_vm<P::PPW>(); break;
+      case 2: wait_vm<2 * P::PPW>(); break;
+      default: wait_vm<3 * P::PPW>(); break;
+    }
+    lds_barrier();
+    // after barrier s every consumer has finished stage s - 1: refill its slot
+    if (s >= 1 && hi < NS) issue(hi++);
+  }
+  lds_barrier();   // after the main loop
+#pragma unroll
+  for (int t = 0; t < T; ++t) lds_barrier();   // epilogue tiles
+}
+
+template <int NV, int T, int NS, bool BF16H>
+__device__ __forceinline__ void pc_consumer(const GateUpArgs& g, uint8_t* lds, int row0, int ng, int wave, int mt0) {
+  using P = Pc<T, NS>;
+  constexpr int MT = 13, Q = 2;
+  const int lane = threadIdx.x & 63, kidx = wave & 1;
+  const size_t a_mt = (size_t)P::C * AGeom<kB_FP8_F16>::kBlk;
+  const uint8_t* abase = g.xq + (size_t)(row0 / 16 + mt0) * a_mt + lane * 16;
+  const uint8_t* lbase = lds + lane * 16;
+  auto a_ld = [&](int j, int c, int u) {
+    return *(const v4i*)(abase + j * a_mt + (size_t)c * AGeom<kB_FP8_F16>::kBlk + u * 1024);
+  };
+  auto b_rd = [&](int c, int t, int u) {
+    return *(const v4i*)(lbase + ((c >> 2) % P::NSLOT) * P::SLOT + ((((c & 3) * T) + t) * 2 + u) * 1024);
+  };
+  // epilogue: this wave finishes m-tiles q = wave and wave + 8 (if < 13);
+  // their scales are requested before the main loop
+  EpiScales<Q, T> es;
+  auto q_of = [&](int j) { return wave + kPcConsumers * j < MT ? wave + kPcConsumers * j : wave; };
+  load_epi<kB_FP8_F16, Q, T>(es, g, row0, ng * T, q_of);
+
+  v4f acc[NV][T];
+#pragma unroll
+  for (int j = 0; j < NV; ++j)
+#pragma unroll
+    for (int t = 0; t < T; ++t) acc[j][t] = v4f{0.f, 0.f, 0.f, 0.f};
+  v4i a[NV][2];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    a[j][0] = a_ld(j, kidx, 0);
+    a[j][1] = a_ld(j, kidx, 1);
+  }
+  v4i b[T][2];
+#pragma unroll
+  for (int k = 0; k < P::NK; ++k) {
+    const int c = kidx + 2 * k;
+    if (k % 2 == 0) {   // stage k / 2 published
+      lds_barrier();
+#pragma unroll
+      for (int t = 0; t < T; ++t) b[t][0] = b_rd(c, t, 0);
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t) b[t][1] = b_rd(c, t, 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v8h bv[T];
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const v4i& w = b[t][i >> 1];
+        bv[t] = e4m3x8_to_f16((uint32_t)w[2 * (i & 1)], (uint32_t)w[2 * (i & 1) + 1]);
+      }
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const v4i& w = a[j][i >> 1];
+        const v8h av = e4m3x8_to_f16((uint32_t)w[2 * (i & 1)], (uint32_t)w[2 * (i & 1) + 1]);
+#pragma unroll
+        for (int t = 0; t < T; ++t) acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv[t], acc[j][t], 0, 0, 0);
+      }
+      if ((i == 1 || i == 3) && k + 1 < P::NK) {
+        // unit i / 2 of the activations is free: load the next chunk's
+        const int u = i >> 1;
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < NV; ++j) a[j][u] = a_ld(j, c + 2, u);
+        // weights of the next chunk, when it is in the same stage
+        if (i == 1 && k % 2 == 0) {
+#pragma unroll
+          for (int t = 0; t < T; ++t) b[t][0] = b_rd(c + 2, t, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+
+  // Epilogue, one weight tile at a time: partial tiles to LDS
+  // ([wave][m-tile][lane], two regions used alternately), then the wave that
+  // owns m-tile q sums its two K halves (wave 2 ms, then 2 ms + 1).
+  lds_barrier();   // every consumer is done with the weights; the ring is reused
+  float amax[Q][2];
+#pragma unroll
+  for (int jq = 0; jq < Q; ++jq) amax[jq][0] = amax[jq][1] = 0.f;
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    v4f* red = (v4f*)(lds + (t & 1) * P::RED);
+#pragma unroll
+    for (int j = 0; j < NV; ++j) red[(wave * 4 + j) * 64 + lane] = acc[j][t];
+    lds_barrier();
+#pragma unroll
+    for (int jq = 0; jq < Q; ++jq) {
+      const int q = wave + kPcConsumers * jq;
+      if (q < MT) {
+        const int msq = q < 4 ? 0 : (q - 1) / 3, jj = q < 4 ? q : (q - 1) % 3;
+        const v4f v = red[((2 * msq) * 4 + jj) * 64 + lane] + red[((2 * msq + 1) * 4 + jj) * 64 + lane];
+        gateup_tile_epilogue<BF16H, T>(g, v, es.xs[jq], es.cg[t], es.cu[t], row0 + q * 16, ng, t, amax[jq]);
+      }
+    }
+  }
+  if constexpr (!BF16H) {
+    const int ngroups = (g.I / 8) / T;
+#pragma unroll
+    for (int jq = 0; jq < Q; ++jq) {
+      const int q = wave + kPcConsumers * jq;
+      if (q < MT) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) amax[jq][e] = max8(amax[jq][e]);
+        if ((lane & 7) == 0) {      // lane 16 gq (rows 0, 2) and 16 gq + 8 (rows 1, 3)
+          const int m = row0 + q * 16 + 4 * (lane >> 4) + ((lane & 8) ? 1 : 0);
+#pragma unroll
+          for (int e = 0; e < 2; ++e) g.amax_part[(size_t)(m + 2 * e) * ngroups + ng] = amax[jq][e];
+        }
+      }
+    }
+  }
+}
+
+template <int T, int NS, bool BF16H>
+__global__ __launch_bounds__(64 * (kPcConsumers + kPcProducers)) void pc_gateup(GateUpArgs g) {
+  extern __shared__ v4f pc_lds[];
+  uint8_t* lds = (uint8_t*)pc_lds;
+  int mb, ng;
+  gateup_block(g, (g.I / 8) / T, mb, ng);
+  const int row0 = mb * 13 * 16;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (wave >= kPcConsumers) pc_producer<T, NS, BF16H>(g, lds, ng, wave - kPcConsumers);
+  else if (wave < 2) pc_consumer<4, T, NS, BF16H>(g, lds, row0, ng, wave, 0);
+  else pc_consumer<3, T, NS, BF16H>(g, lds, row0, ng, wave, 1 + 3 * (wave >> 1));
+}
+
+template <int T, int NS, bool BF16H>
+hipError_t launch_pc(const GateUpArgs& g, int grid, hipStream_t st, const LaunchEvents& ev) {
+  auto fn = pc_gateup<T, NS, BF16H>;
+  constexpr size_t lds = Pc<T, NS>::LDS;
+  static bool attr = false;   // idempotent; a race only repeats the call
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  launch_kernel(fn, dim3(grid), dim3(64 * (kPcConsumers + kPcProducers)), lds, st, ev, g);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- dispatch
 
 template <int BF, bool BF16H, int MT, int T, int MS, int KS, int D>
@@ -232,6 +439,10 @@ hipError_t go(const GateUpArgs& g, int grid, hipStream_t st, const LaunchEvents&
   const int C = g.H / kChunk;
   // six NVFP4 tiles of 2-4 m-tiles: one chunk in flight per wave (two
   // would not fit the registers of two waves per SIMD)
+  if constexpr (BF == kB_FP8_F16 && MT == 13) {
+    if (C == 16) return launch_pc<T, 4, BF16H>(g, grid, st, ev);
+    if (C == 32) return launch_pc<T, 8, BF16H>(g, grid, st, ev);
+  }
   if constexpr (T == 6) return launch_ks<BF, BF16H, MT, T, MS, KS, 1>(g, grid, st, ev);
   else if constexpr (MTW <= 4) return launch_ks<BF, BF16H, MT, T, MS, KS, 2>(g, grid, st, ev);
   else if (C == 4 * KS) return launch_ks<BF, BF16H, MT, T, MS, KS, -4>(g, grid, st, ev);

@@ -33,16 +33,6 @@
 namespace ocq {
 namespace {
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-// s_waitcnt for vector-memory count <= N only (gfx9 encoding: vmcnt in bits
-// 3:0 and 15:14; expcnt 6:4 and lgkmcnt 11:8 left at their maxima)
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
 // Geometry of one LDS-tiled kernel.  BF: weight format (kB_FP8_F16: E4M3
 // codes, two MFMA sub-steps per unit; kB_BF16: one).  A16: the activations
 // are 16-bit values in fragment order (one unit per sub-step: AU units per

@@ -204,32 +204,40 @@ __global__ __launch_bounds__(64 * MS * KS) void ks_gateup(GateUpArgs g) {
 // ---------------------------------------------------------------- 13 m-tiles, weights through LDS
 //
 // For one 208-row m-block of E4M3 weights the skinny kernel's waves stall on
-// the weight stream: a wave's loads complete in issue order, so the
-// activations it needs next wait behind the weights it requested earlier.
-// Here the roles are split.  Four producer waves (one per SIMD) stream the
-// workgroup's weight tiles into an LDS ring with direct-to-LDS loads, in
-// stages of 4 chunks, and publish each stage with a workgroup barrier after
-// their own loads of it have landed.  Eight consumer waves load only
-// activations (one chunk ahead, in registers), read the weights of a chunk
-// from LDS and run the MFMAs: wave (ms, kidx) holds m-tiles 0-3 (ms = 0) or
+// the weight stream (a wave's loads complete in issue order, so the
+// activations it needs next wait behind the weights it requested earlier),
+// and each of its two wave rows converts the same weights to fp16.  Here the
+// roles are split.  Four producer waves (one per SIMD) load the workgroup's
+// weight tiles in stages of 4 chunks, one stage ahead, convert
+// each E4M3 unit once to fp16 and write it to a two-slot LDS ring; a
+// workgroup barrier publishes each stage.  Eight consumer waves load only
+// activations (one chunk ahead, in registers), read fp16 weights from LDS
+// and run the MFMAs: wave (ms, kidx) holds m-tiles 0-3 (ms = 0) or
 // 1 + 3 ms .. 3 + 3 ms and the chunks kidx, kidx + 2, ...  Every barrier is
 // passed by all twelve waves in the same order: one per stage, one after the
 // main loop, one per weight tile in the epilogue.
-constexpr int kPcConsumers = 8, kPcProducers = 4, kPcSlots = 4;
+constexpr int kPcConsumers = 8, kPcProducers = 4;
 
 template <int T, int NS>
 struct Pc {
   static constexpr int C = 4 * NS;                     // chunks of 128 inputs
   static constexpr int NK = C / 2;                     // chunks per consumer wave
-  static constexpr int UPS = 8 * T;                    // weight units (1 KB) per stage
+  static constexpr int UPS = 8 * T;                    // E4M3 weight units (1 KB) per stage
   static constexpr int PPW = UPS / kPcProducers;       // loads per producer wave and stage
-  static constexpr int NSLOT = NS < kPcSlots ? NS : kPcSlots;
-  static constexpr int SLOT = UPS * 1024;
+  static constexpr int PW = 1;                         // stages loaded ahead of the one being converted
+  static constexpr int W = PW + 1;                     // register buffers of a producer (stages)
+  static constexpr int SLOT = 2 * UPS * 1024;          // fp16 units of a stage: [chunk][tile][sub-step]
   static constexpr int RED = kPcConsumers * 4 * 1024;  // epilogue partials of one weight tile
-  static constexpr int LDS = NSLOT * SLOT > 2 * RED ? NSLOT * SLOT : 2 * RED;
-  static_assert(UPS % kPcProducers == 0 && (NSLOT - 1) * PPW < 64, "loads per producer");
+  static constexpr int LDS = 2 * SLOT > 2 * RED ? 2 * SLOT : 2 * RED;
+  static_assert(UPS % kPcProducers == 0 && W * PPW < 64, "loads per producer");
   static_assert(LDS <= 160 * 1024, "LDS of one CU");
 };
+
+// fp16 unit of (chunk c, tile t, sub-step i) in the ring (lane part excluded)
+template <int T, int NS>
+__device__ __forceinline__ int pc_f16_unit(int c, int t, int i) {
+  return ((c >> 2) & 1) * Pc<T, NS>::SLOT + ((((c & 3) * T) + t) * 4 + i) * 1024;
+}
 
 template <int T, int NS, bool BF16H>
 __device__ __forceinline__ void pc_producer(const GateUpArgs& g, uint8_t* lds, int ng, int p) {
@@ -237,30 +245,38 @@ __device__ __forceinline__ void pc_producer(const GateUpArgs& g, uint8_t* lds, i
   const int lane = threadIdx.x & 63;
   const size_t wt = (size_t)P::C * Fmt<kB_FP8_F16>::kGlobal;
   const uint8_t* w = g.wcodes + (size_t)ng * T * wt + lane * 16;
-  auto issue = [&](int s) {
-    uint8_t* slot = lds + (s % P::NSLOT) * P::SLOT;
+  // unit x of a stage: chunk x / 2T of the stage, tile (x / 2) % T, unit x % 2
+  v4i r[P::W][P::PPW];
+  auto load = [&](v4i (&d)[P::PPW], int s) {
 #pragma unroll
     for (int q = 0; q < P::PPW; ++q) {
       const int x = p + q * kPcProducers;
       const int cc = x / (2 * T), t = (x >> 1) % T, u = x & 1;
-      const uint8_t* src = w + t * wt + (size_t)(4 * s + cc) * Fmt<kB_FP8_F16>::kGlobal + u * 1024;
-      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(slot + x * 1024), 16, 0, 0);
+      d[q] = *(const v4i*)(w + t * wt + (size_t)(4 * s + cc) * Fmt<kB_FP8_F16>::kGlobal + u * 1024);
     }
   };
+  // stage 0 alone first: requested together with later stages it would
+  // land only once most of them had (the memory system does not serve a
+  // burst in issue order), and every consumer waits for it
+  load(r[0], 0);
 #pragma unroll
-  for (int s = 0; s < P::NSLOT; ++s) issue(s);
-  int hi = P::NSLOT;   // stages issued
   for (int s = 0; s < NS; ++s) {
-    // stages s .. hi - 1 are outstanding: wait for stage s only
-    switch (hi - 1 - s) {
-      case 0: wait_vm<0>(); break;
-      case 1: wait_vm<P::PPW>(); break;
-      case 2: wait_vm<2 * P::PPW>(); break;
-      default: wait_vm<3 * P::PPW>(); break;
+    // slot s % 2 held stage s - 2, which every consumer finished before
+    // passing barrier s - 1
+    uint8_t* slot = lds + (s & 1) * P::SLOT + lane * 16;
+#pragma unroll
+    for (int q = 0; q < P::PPW; ++q) {
+      const int x = p + q * kPcProducers;
+      const int cc = x / (2 * T), t = (x >> 1) % T, u = x & 1;
+      const v4i& v = r[s % P::W][q];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        *(v8h*)(slot + (((cc * T) + t) * 4 + 2 * u + h) * 1024) = e4m3x8_to_f16((uint32_t)v[2 * h], (uint32_t)v[2 * h + 1]);
     }
-    lds_barrier();
-    // after barrier s every consumer has finished stage s - 1: refill its slot
-    if (s >= 1 && hi < NS) issue(hi++);
+#pragma unroll
+    for (int n = s + 1; n <= s + P::PW; ++n)
+      if (n < NS && (s == 0 || n == s + P::PW)) load(r[n % P::W], n);
+    lds_barrier();   // stage s published
   }
   lds_barrier();   // after the main loop
 #pragma unroll
@@ -278,8 +294,9 @@ __device__ __forceinline__ void pc_consumer(const GateUpArgs& g, uint8_t* lds, i
   auto a_ld = [&](int j, int c, int u) {
     return *(const v4i*)(abase + j * a_mt + (size_t)c * AGeom<kB_FP8_F16>::kBlk + u * 1024);
   };
-  auto b_rd = [&](int c, int t, int u) {
-    return *(const v4i*)(lbase + ((c >> 2) % P::NSLOT) * P::SLOT + ((((c & 3) * T) + t) * 2 + u) * 1024);
+  auto b_rd = [&](v8h (&d)[T], int c, int i) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) d[t] = *(const v8h*)(lbase + pc_f16_unit<T, NS>(c, t, i));
   };
   // epilogue: this wave finishes m-tiles q = wave and wave + 8 (if < 13);
   // their scales are requested before the main loop
@@ -298,31 +315,28 @@ __device__ __forceinline__ void pc_consumer(const GateUpArgs& g, uint8_t* lds, i
     a[j][0] = a_ld(j, kidx, 0);
     a[j][1] = a_ld(j, kidx, 1);
   }
-  v4i b[T][2];
+  // fp16 weights of two sub-steps: the next one is read while the current
+  // one's MFMAs run
+  v8h bq[2][T];
 #pragma unroll
   for (int k = 0; k < P::NK; ++k) {
     const int c = kidx + 2 * k;
     if (k % 2 == 0) {   // stage k / 2 published
       lds_barrier();
-#pragma unroll
-      for (int t = 0; t < T; ++t) b[t][0] = b_rd(c, t, 0);
+      b_rd(bq[0], c, 0);
     }
 #pragma unroll
-    for (int t = 0; t < T; ++t) b[t][1] = b_rd(c, t, 1);
-#pragma unroll
     for (int i = 0; i < 4; ++i) {
-      v8h bv[T];
-#pragma unroll
-      for (int t = 0; t < T; ++t) {
-        const v4i& w = b[t][i >> 1];
-        bv[t] = e4m3x8_to_f16((uint32_t)w[2 * (i & 1)], (uint32_t)w[2 * (i & 1) + 1]);
-      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (i < 3) b_rd(bq[(i + 1) & 1], c, i + 1);
+      else if (k % 2 == 0) b_rd(bq[0], c + 2, 0);   // next chunk, same stage
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < NV; ++j) {
         const v4i& w = a[j][i >> 1];
         const v8h av = e4m3x8_to_f16((uint32_t)w[2 * (i & 1)], (uint32_t)w[2 * (i & 1) + 1]);
 #pragma unroll
-        for (int t = 0; t < T; ++t) acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv[t], acc[j][t], 0, 0, 0);
+        for (int t = 0; t < T; ++t) acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bq[i & 1][t], acc[j][t], 0, 0, 0);
       }
       if ((i == 1 || i == 3) && k + 1 < P::NK) {
         // unit i / 2 of the activations is free: load the next chunk's
@@ -330,11 +344,6 @@ __device__ __forceinline__ void pc_consumer(const GateUpArgs& g, uint8_t* lds, i
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < NV; ++j) a[j][u] = a_ld(j, c + 2, u);
-        // weights of the next chunk, when it is in the same stage
-        if (i == 1 && k % 2 == 0) {
-#pragma unroll
-          for (int t = 0; t < T; ++t) b[t][0] = b_rd(c + 2, t, 0);
-        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }

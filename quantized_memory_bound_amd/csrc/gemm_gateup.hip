@@ -208,7 +208,7 @@ __global__ __launch_bounds__(64 * MS * KS) void ks_gateup(GateUpArgs g) {
 // activations it needs next wait behind the weights it requested earlier),
 // and each of its two wave rows converts the same weights to fp16.  Here the
 // roles are split.  Four producer waves (one per SIMD) load the workgroup's
-// weight tiles in stages of 4 chunks, one stage ahead, convert
+// weight tiles in stages of 2 chunks, one stage ahead, convert
 // each E4M3 unit once to fp16 and write it to a two-slot LDS ring; a
 // workgroup barrier publishes each stage.  Eight consumer waves load only
 // activations (one chunk ahead, in registers), read fp16 weights from LDS
@@ -218,11 +218,13 @@ __global__ __launch_bounds__(64 * MS * KS) void ks_gateup(GateUpArgs g) {
 // main loop, one per weight tile in the epilogue.
 constexpr int kPcConsumers = 8, kPcProducers = 4;
 
-template <int T, int NS>
+template <int T_, int C_>
 struct Pc {
-  static constexpr int C = 4 * NS;                     // chunks of 128 inputs
+  static constexpr int C = C_, T = T_;                 // chunks of 128 inputs, weight tiles
+  static constexpr int CPS = 2;                        // chunks per stage (one per consumer wave)
+  static constexpr int NS = C / CPS;                   // stages
   static constexpr int NK = C / 2;                     // chunks per consumer wave
-  static constexpr int UPS = 8 * T;                    // E4M3 weight units (1 KB) per stage
+  static constexpr int UPS = 2 * CPS * T;              // E4M3 weight units (1 KB) per stage
   static constexpr int PPW = UPS / kPcProducers;       // loads per producer wave and stage
   static constexpr int PW = 1;                         // stages loaded ahead of the one being converted
   static constexpr int W = PW + 1;                     // register buffers of a producer (stages)
@@ -230,18 +232,19 @@ struct Pc {
   static constexpr int RED = kPcConsumers * 4 * 1024;  // epilogue partials of one weight tile
   static constexpr int LDS = 2 * SLOT > 2 * RED ? 2 * SLOT : 2 * RED;
   static_assert(UPS % kPcProducers == 0 && W * PPW < 64, "loads per producer");
+  static_assert(CPS % 2 == 0 && C % CPS == 0, "stages of whole chunk pairs");
   static_assert(LDS <= 160 * 1024, "LDS of one CU");
 };
 
 // fp16 unit of (chunk c, tile t, sub-step i) in the ring (lane part excluded)
-template <int T, int NS>
+template <class P>
 __device__ __forceinline__ int pc_f16_unit(int c, int t, int i) {
-  return ((c >> 2) & 1) * Pc<T, NS>::SLOT + ((((c & 3) * T) + t) * 4 + i) * 1024;
+  return ((c / P::CPS) & 1) * P::SLOT + ((((c % P::CPS) * P::T) + t) * 4 + i) * 1024;
 }
 
-template <int T, int NS, bool BF16H>
+template <int T, int C, bool BF16H>
 __device__ __forceinline__ void pc_producer(const GateUpArgs& g, uint8_t* lds, int ng, int p) {
-  using P = Pc<T, NS>;
+  using P = Pc<T, C>;
   const int lane = threadIdx.x & 63;
   const size_t wt = (size_t)P::C * Fmt<kB_FP8_F16>::kGlobal;
   const uint8_t* w = g.wcodes + (size_t)ng * T * wt + lane * 16;
@@ -252,7 +255,7 @@ __device__ __forceinline__ void pc_producer(const GateUpArgs& g, uint8_t* lds, i
     for (int q = 0; q < P::PPW; ++q) {
       const int x = p + q * kPcProducers;
       const int cc = x / (2 * T), t = (x >> 1) % T, u = x & 1;
-      d[q] = *(const v4i*)(w + t * wt + (size_t)(4 * s + cc) * Fmt<kB_FP8_F16>::kGlobal + u * 1024);
+      d[q] = *(const v4i*)(w + t * wt + (size_t)(P::CPS * s + cc) * Fmt<kB_FP8_F16>::kGlobal + u * 1024);
     }
   };
   // stage 0 alone first: requested together with later stages it would
@@ -260,7 +263,7 @@ __device__ __forceinline__ void pc_producer(const GateUpArgs& g, uint8_t* lds, i
   // burst in issue order), and every consumer waits for it
   load(r[0], 0);
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
+  for (int s = 0; s < P::NS; ++s) {
     // slot s % 2 held stage s - 2, which every consumer finished before
     // passing barrier s - 1
     uint8_t* slot = lds + (s & 1) * P::SLOT + lane * 16;
@@ -275,7 +278,7 @@ __device__ __forceinline__ void pc_producer(const GateUpArgs& g, uint8_t* lds, i
     }
 #pragma unroll
     for (int n = s + 1; n <= s + P::PW; ++n)
-      if (n < NS && (s == 0 || n == s + P::PW)) load(r[n % P::W], n);
+      if (n < P::NS && (s == 0 || n == s + P::PW)) load(r[n % P::W], n);
     lds_barrier();   // stage s published
   }
   lds_barrier();   // after the main loop
@@ -283,9 +286,9 @@ __device__ __forceinline__ void pc_producer(const GateUpArgs& g, uint8_t* lds, i
   for (int t = 0; t < T; ++t) lds_barrier();   // epilogue tiles
 }
 
-template <int NV, int T, int NS, bool BF16H>
+template <int NV, int T, int C, bool BF16H>
 __device__ __forceinline__ void pc_consumer(const GateUpArgs& g, uint8_t* lds, int row0, int ng, int wave, int mt0) {
-  using P = Pc<T, NS>;
+  using P = Pc<T, C>;
   constexpr int MT = 13, Q = 2;
   const int lane = threadIdx.x & 63, kidx = wave & 1;
   const size_t a_mt = (size_t)P::C * AGeom<kB_FP8_F16>::kBlk;
@@ -296,7 +299,7 @@ __device__ __forceinline__ void pc_consumer(const GateUpArgs& g, uint8_t* lds, i
   };
   auto b_rd = [&](v8h (&d)[T], int c, int i) {
 #pragma unroll
-    for (int t = 0; t < T; ++t) d[t] = *(const v8h*)(lbase + pc_f16_unit<T, NS>(c, t, i));
+    for (int t = 0; t < T; ++t) d[t] = *(const v8h*)(lbase + pc_f16_unit<P>(c, t, i));
   };
   // epilogue: this wave finishes m-tiles q = wave and wave + 8 (if < 13);
   // their scales are requested before the main loop
@@ -321,7 +324,8 @@ __device__ __forceinline__ void pc_consumer(const GateUpArgs& g, uint8_t* lds, i
 #pragma unroll
   for (int k = 0; k < P::NK; ++k) {
     const int c = kidx + 2 * k;
-    if (k % 2 == 0) {   // stage k / 2 published
+    constexpr int KPS = P::CPS / 2;   // chunks per consumer wave and stage
+    if (k % KPS == 0) {   // stage k / KPS published
       lds_barrier();
       b_rd(bq[0], c, 0);
     }
@@ -329,7 +333,7 @@ __device__ __forceinline__ void pc_consumer(const GateUpArgs& g, uint8_t* lds, i
     for (int i = 0; i < 4; ++i) {
       __builtin_amdgcn_sched_barrier(0);
       if (i < 3) b_rd(bq[(i + 1) & 1], c, i + 1);
-      else if (k % 2 == 0) b_rd(bq[0], c + 2, 0);   // next chunk, same stage
+      else if ((k + 1) % KPS != 0) b_rd(bq[0], c + 2, 0);   // next chunk, same stage
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < NV; ++j) {
@@ -390,7 +394,7 @@ __device__ __forceinline__ void pc_consumer(const GateUpArgs& g, uint8_t* lds, i
   }
 }
 
-template <int T, int NS, bool BF16H>
+template <int T, int C, bool BF16H>
 __global__ __launch_bounds__(64 * (kPcConsumers + kPcProducers)) void pc_gateup(GateUpArgs g) {
   extern __shared__ v4f pc_lds[];
   uint8_t* lds = (uint8_t*)pc_lds;
@@ -398,15 +402,15 @@ __global__ __launch_bounds__(64 * (kPcConsumers + kPcProducers)) void pc_gateup(
   gateup_block(g, (g.I / 8) / T, mb, ng);
   const int row0 = mb * 13 * 16;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (wave >= kPcConsumers) pc_producer<T, NS, BF16H>(g, lds, ng, wave - kPcConsumers);
-  else if (wave < 2) pc_consumer<4, T, NS, BF16H>(g, lds, row0, ng, wave, 0);
-  else pc_consumer<3, T, NS, BF16H>(g, lds, row0, ng, wave, 1 + 3 * (wave >> 1));
+  if (wave >= kPcConsumers) pc_producer<T, C, BF16H>(g, lds, ng, wave - kPcConsumers);
+  else if (wave < 2) pc_consumer<4, T, C, BF16H>(g, lds, row0, ng, wave, 0);
+  else pc_consumer<3, T, C, BF16H>(g, lds, row0, ng, wave, 1 + 3 * (wave >> 1));
 }
 
-template <int T, int NS, bool BF16H>
+template <int T, int C, bool BF16H>
 hipError_t launch_pc(const GateUpArgs& g, int grid, hipStream_t st, const LaunchEvents& ev) {
-  auto fn = pc_gateup<T, NS, BF16H>;
-  constexpr size_t lds = Pc<T, NS>::LDS;
+  auto fn = pc_gateup<T, C, BF16H>;
+  constexpr size_t lds = Pc<T, C>::LDS;
   static bool attr = false;   // idempotent; a race only repeats the call
   if (!attr) {
     hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -449,8 +453,8 @@ hipError_t go(const GateUpArgs& g, int grid, hipStream_t st, const LaunchEvents&
   // six NVFP4 tiles of 2-4 m-tiles: one chunk in flight per wave (two
   // would not fit the registers of two waves per SIMD)
   if constexpr (BF == kB_FP8_F16 && MT == 13) {
-    if (C == 16) return launch_pc<T, 4, BF16H>(g, grid, st, ev);
-    if (C == 32) return launch_pc<T, 8, BF16H>(g, grid, st, ev);
+    if (C == 16) return launch_pc<T, 16, BF16H>(g, grid, st, ev);
+    if (C == 32) return launch_pc<T, 32, BF16H>(g, grid, st, ev);
   }
   if constexpr (T == 6) return launch_ks<BF, BF16H, MT, T, MS, KS, 1>(g, grid, st, ev);
   else if constexpr (MTW <= 4) return launch_ks<BF, BF16H, MT, T, MS, KS, 2>(g, grid, st, ev);

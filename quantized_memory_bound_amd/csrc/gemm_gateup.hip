@@ -218,20 +218,22 @@ __global__ __launch_bounds__(64 * MS * KS) void ks_gateup(GateUpArgs g) {
 // main loop, one per weight tile in the epilogue.
 constexpr int kPcConsumers = 8, kPcProducers = 4;
 
-template <int T_, int C_>
+template <int BF_, int T_, int C_>
 struct Pc {
-  static constexpr int C = C_, T = T_;                 // chunks of 128 inputs, weight tiles
+  static constexpr int BF = BF_, C = C_, T = T_;       // weight format, chunks of 128 inputs, weight tiles
   static constexpr int CPS = 2;                        // chunks per stage (one per consumer wave)
   static constexpr int NS = C / CPS;                   // stages
   static constexpr int NK = C / 2;                     // chunks per consumer wave
-  static constexpr int UPS = 2 * CPS * T;              // E4M3 weight units (1 KB) per stage
-  static constexpr int PPW = UPS / kPcProducers;       // loads per producer wave and stage
+  static constexpr int UB = Fmt<BF>::kUnits;           // weight units (1 KB) per tile and chunk
+  static constexpr int US = CPS * T * UB;              // weight units per stage
+  static constexpr int PPW = (US + kPcProducers - 1) / kPcProducers;   // loads per producer wave and stage
   static constexpr int PW = 1;                         // stages loaded ahead of the one being converted
   static constexpr int W = PW + 1;                     // register buffers of a producer (stages)
-  static constexpr int SLOT = 2 * UPS * 1024;          // fp16 units of a stage: [chunk][tile][sub-step]
+  static constexpr int SLOT = CPS * T * 4 * 1024;      // fp16 units of a stage: [chunk][tile][sub-step]
   static constexpr int RED = kPcConsumers * 4 * 1024;  // epilogue partials of one weight tile
   static constexpr int LDS = 2 * SLOT > 2 * RED ? 2 * SLOT : 2 * RED;
-  static_assert(UPS % kPcProducers == 0 && W * PPW < 64, "loads per producer");
+  static_assert(BF == kB_FP8_F16 || BF == kB_FP4_F16, "E4M3 or NVFP4 weights");
+  static_assert(W * PPW < 64 && PPW * kPcProducers - US <= kPcProducers, "loads per producer");
   static_assert(CPS % 2 == 0 && C % CPS == 0, "stages of whole chunk pairs");
   static_assert(LDS <= 160 * 1024, "LDS of one CU");
 };
@@ -242,26 +244,37 @@ __device__ __forceinline__ int pc_f16_unit(int c, int t, int i) {
   return ((c / P::CPS) & 1) * P::SLOT + ((((c % P::CPS) * P::T) + t) * 4 + i) * 1024;
 }
 
-template <int T, int C, bool BF16H>
+template <int BF, int T, int C, bool BF16H>
 __device__ __forceinline__ void pc_producer(const GateUpArgs& g, uint8_t* lds, int ng, int p) {
-  using P = Pc<T, C>;
+  using P = Pc<BF, T, C>;
   const int lane = threadIdx.x & 63;
-  const size_t wt = (size_t)P::C * Fmt<kB_FP8_F16>::kGlobal;
+  const size_t wt = (size_t)C * Fmt<BF>::kGlobal, bt = (size_t)((C + 7) / 8) * 1024;
   const uint8_t* w = g.wcodes + (size_t)ng * T * wt + lane * 16;
-  // unit x of a stage: chunk x / 2T of the stage, tile (x / 2) % T, unit x % 2
+  const uint8_t* wb = g.wbscales + (size_t)ng * T * bt + lane * 16;
+  // unit x of a stage: chunk x / (T UB) of the stage, tile (x / UB) % T,
+  // unit x % UB of the tile's chunk; NVFP4 units also take the lane's two
+  // E4M3 block scales (inputs 0-15 and 16-31 of each 32-input sub-step pair)
   v4i r[P::W][P::PPW];
-  auto load = [&](v4i (&d)[P::PPW], int s) {
+  uint32_t rs[P::W][P::PPW];
+  // Every load is unconditional (a unit past the stage's last reloads one
+  // that exists and is not written): a load under a branch would make the
+  // compiler wait for every outstanding load where the branches join, so
+  // stage s + 1 would have landed before stage s is published.
+  auto load = [&](int b, int s) {
 #pragma unroll
     for (int q = 0; q < P::PPW; ++q) {
-      const int x = p + q * kPcProducers;
-      const int cc = x / (2 * T), t = (x >> 1) % T, u = x & 1;
-      d[q] = *(const v4i*)(w + t * wt + (size_t)(P::CPS * s + cc) * Fmt<kB_FP8_F16>::kGlobal + u * 1024);
+      const int x0 = p + q * kPcProducers;
+      const int x = P::US % kPcProducers == 0 || x0 < P::US ? x0 : x0 - kPcProducers;
+      const int cc = x / (T * P::UB), t = (x / P::UB) % T, u = x % P::UB, c = P::CPS * s + cc;
+      r[b][q] = *(const v4i*)(w + t * wt + (size_t)c * Fmt<BF>::kGlobal + u * 1024);
+      if constexpr (BF == kB_FP4_F16)
+        rs[b][q] = *(const uint16_t*)(wb + t * bt + (size_t)(c >> 3) * 1024 + 2 * (c & 7));
     }
   };
   // stage 0 alone first: requested together with later stages it would
   // land only once most of them had (the memory system does not serve a
   // burst in issue order), and every consumer waits for it
-  load(r[0], 0);
+  load(0, 0);
 #pragma unroll
   for (int s = 0; s < P::NS; ++s) {
     // slot s % 2 held stage s - 2, which every consumer finished before
@@ -270,15 +283,25 @@ __device__ __forceinline__ void pc_producer(const GateUpArgs& g, uint8_t* lds, i
 #pragma unroll
     for (int q = 0; q < P::PPW; ++q) {
       const int x = p + q * kPcProducers;
-      const int cc = x / (2 * T), t = (x >> 1) % T, u = x & 1;
-      const v4i& v = r[s % P::W][q];
+      if (P::US % kPcProducers == 0 || x < P::US) {
+        const int cc = x / (T * P::UB), t = (x / P::UB) % T, u = x % P::UB;
+        const v4i& v = r[s % P::W][q];
+        uint8_t* dst = slot + ((cc * T) + t) * 4 * 1024;
+        if constexpr (BF == kB_FP8_F16) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-        *(v8h*)(slot + (((cc * T) + t) * 4 + 2 * u + h) * 1024) = e4m3x8_to_f16((uint32_t)v[2 * h], (uint32_t)v[2 * h + 1]);
+          for (int h = 0; h < 2; ++h)
+            *(v8h*)(dst + (2 * u + h) * 1024) = e4m3x8_to_f16((uint32_t)v[2 * h], (uint32_t)v[2 * h + 1]);
+        } else {
+          v2h s0, s1;
+          e4m3x2_scales(rs[s % P::W][q], s0, s1);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) *(v8h*)(dst + i * 1024) = e2m1x8_to_f16((uint32_t)v[i], i < 2 ? s0 : s1);
+        }
+      }
     }
 #pragma unroll
     for (int n = s + 1; n <= s + P::PW; ++n)
-      if (n < P::NS && (s == 0 || n == s + P::PW)) load(r[n % P::W], n);
+      if (n < P::NS && (s == 0 || n == s + P::PW)) load(n % P::W, n);
     lds_barrier();   // stage s published
   }
   lds_barrier();   // after the main loop
@@ -286,9 +309,9 @@ __device__ __forceinline__ void pc_producer(const GateUpArgs& g, uint8_t* lds, i
   for (int t = 0; t < T; ++t) lds_barrier();   // epilogue tiles
 }
 
-template <int NV, int T, int C, bool BF16H>
+template <int BF, int NV, int T, int C, bool BF16H>
 __device__ __forceinline__ void pc_consumer(const GateUpArgs& g, uint8_t* lds, int row0, int ng, int wave, int mt0) {
-  using P = Pc<T, C>;
+  using P = Pc<BF, T, C>;
   constexpr int MT = 13, Q = 2;
   const int lane = threadIdx.x & 63, kidx = wave & 1;
   const size_t a_mt = (size_t)P::C * AGeom<kB_FP8_F16>::kBlk;
@@ -305,7 +328,7 @@ __device__ __forceinline__ void pc_consumer(const GateUpArgs& g, uint8_t* lds, i
   // their scales are requested before the main loop
   EpiScales<Q, T> es;
   auto q_of = [&](int j) { return wave + kPcConsumers * j < MT ? wave + kPcConsumers * j : wave; };
-  load_epi<kB_FP8_F16, Q, T>(es, g, row0, ng * T, q_of);
+  load_epi<BF, Q, T>(es, g, row0, ng * T, q_of);
 
   v4f acc[NV][T];
 #pragma unroll
@@ -394,7 +417,7 @@ __device__ __forceinline__ void pc_consumer(const GateUpArgs& g, uint8_t* lds, i
   }
 }
 
-template <int T, int C, bool BF16H>
+template <int BF, int T, int C, bool BF16H>
 __global__ __launch_bounds__(64 * (kPcConsumers + kPcProducers)) void pc_gateup(GateUpArgs g) {
   extern __shared__ v4f pc_lds[];
   uint8_t* lds = (uint8_t*)pc_lds;
@@ -402,15 +425,15 @@ __global__ __launch_bounds__(64 * (kPcConsumers + kPcProducers)) void pc_gateup(
   gateup_block(g, (g.I / 8) / T, mb, ng);
   const int row0 = mb * 13 * 16;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (wave >= kPcConsumers) pc_producer<T, C, BF16H>(g, lds, ng, wave - kPcConsumers);
-  else if (wave < 2) pc_consumer<4, T, C, BF16H>(g, lds, row0, ng, wave, 0);
-  else pc_consumer<3, T, C, BF16H>(g, lds, row0, ng, wave, 1 + 3 * (wave >> 1));
+  if (wave >= kPcConsumers) pc_producer<BF, T, C, BF16H>(g, lds, ng, wave - kPcConsumers);
+  else if (wave < 2) pc_consumer<BF, 4, T, C, BF16H>(g, lds, row0, ng, wave, 0);
+  else pc_consumer<BF, 3, T, C, BF16H>(g, lds, row0, ng, wave, 1 + 3 * (wave >> 1));
 }
 
-template <int T, int C, bool BF16H>
+template <int BF, int T, int C, bool BF16H>
 hipError_t launch_pc(const GateUpArgs& g, int grid, hipStream_t st, const LaunchEvents& ev) {
-  auto fn = pc_gateup<T, C, BF16H>;
-  constexpr size_t lds = Pc<T, C>::LDS;
+  auto fn = pc_gateup<BF, T, C, BF16H>;
+  constexpr size_t lds = Pc<BF, T, C>::LDS;
   static bool attr = false;   // idempotent; a race only repeats the call
   if (!attr) {
     hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -452,9 +475,9 @@ hipError_t go(const GateUpArgs& g, int grid, hipStream_t st, const LaunchEvents&
   const int C = g.H / kChunk;
   // six NVFP4 tiles of 2-4 m-tiles: one chunk in flight per wave (two
   // would not fit the registers of two waves per SIMD)
-  if constexpr (BF == kB_FP8_F16 && MT == 13) {
-    if (C == 16) return launch_pc<T, 16, BF16H>(g, grid, st, ev);
-    if (C == 32) return launch_pc<T, 32, BF16H>(g, grid, st, ev);
+  if constexpr ((BF == kB_FP8_F16 || BF == kB_FP4_F16) && MT == 13 && T <= 3) {
+    if (C == 16) return launch_pc<BF, T, 16, BF16H>(g, grid, st, ev);
+    if (C == 32) return launch_pc<BF, T, 32, BF16H>(g, grid, st, ev);
   }
   if constexpr (T == 6) return launch_ks<BF, BF16H, MT, T, MS, KS, 1>(g, grid, st, ev);
   else if constexpr (MTW <= 4) return launch_ks<BF, BF16H, MT, T, MS, KS, 2>(g, grid, st, ev);

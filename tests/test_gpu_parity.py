@@ -220,6 +220,19 @@ def test_row_independence(prec):
     check_y(g208["y"][:13], g13["y"], "y of rows 0..12, M=208 against M=13")
 
 
+# 13-m-tile gate/up with producer waves (H = 2048 or 4096, 113..383 rows):
+# every format, one and two m-blocks, padded rows, 1, 2 and 3 weight tiles
+# per workgroup (I = 1024, 3200, 6144), bf16 h for a BF16 down projection
+@pytest.mark.parametrize("hidden,inter,M,prec", [(2048, 1024, 300, 0), (2048, 3200, 250, 1), (4096, 6144, 208, 0),
+                                                 (4096, 3200, 150, 2), (2048, 6144, 120, 1), (2048, 1024, 383, 2)])
+def test_gateup_weight_producers(hidden, inter, M, prec):
+    print("case producers hidden=%d inter=%d M=%d prec=%d" % (hidden, inter, M, prec), flush=True)
+    d = I.make_inputs(hidden, inter, M, x_outliers=True, w_std=0.02, seed=hidden + inter + M + prec)
+    g, _ = run_gpu(d, prec)
+    r = O.block_reference(d["x_bits"], d["w_gate"], d["w_up"], d["w_down"], prec)
+    compare(g, r, prec, what="producers %dx%d M=%d prec=%d" % (hidden, inter, M, prec))
+
+
 # one workspace for a sequence of calls: different rows each time, and a call
 # that takes the LDS-tiled kernels in between
 def test_workspace_reuse():

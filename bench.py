@@ -24,6 +24,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -84,13 +85,25 @@ class HipEvents:
         self.h.hipEventDestroy(e)
 
 
-def kernel_source_digest():
-    """Digest of the gate/up kernel's sources: the counters in profiles/ are
-    reported only while these files are unchanged."""
+def _code_only(text):
+    """Source text without comments and blank lines (whitespace normalised)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    lines = (re.sub(r"//.*", "", l).split() for l in text.splitlines())
+    return "\n".join(" ".join(l) for l in lines if l)
+
+
+def kernel_source_digest(read=None):
+    """Digest of the gate/up kernel's code (comments and blank lines ignored):
+    the counters in profiles/ are reported only while it is unchanged.
+    read(name) -> text overrides where the sources come from."""
     h = hashlib.sha256()
     for name in ("gemm_gateup.hip", "gemm_core.h", "kcommon.h"):
-        with open(os.path.join(ROOT, "quantized_memory_bound_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        if read is not None:
+            text = read(name)
+        else:
+            with open(os.path.join(ROOT, "quantized_memory_bound_amd", "csrc", name)) as f:
+                text = f.read()
+        h.update(_code_only(text).encode())
     return h.hexdigest()[:16]
 
 

@@ -203,14 +203,14 @@ __global__ __launch_bounds__(64 * MS * KS) void ks_gateup(GateUpArgs g) {
 
 // ---------------------------------------------------------------- 13 m-tiles, weights through LDS
 //
-// For one 208-row m-block of E4M3 weights the skinny kernel's waves stall on
-// the weight stream (a wave's loads complete in issue order, so the
-// activations it needs next wait behind the weights it requested earlier),
-// and each of its two wave rows converts the same weights to fp16.  Here the
-// roles are split.  Four producer waves (one per SIMD) load the workgroup's
-// weight tiles in stages of 2 chunks, one stage ahead, convert
-// each E4M3 unit once to fp16 and write it to a two-slot LDS ring; a
-// workgroup barrier publishes each stage.  Eight consumer waves load only
+// For one 208-row m-block the skinny kernel's waves stall on the weight
+// stream (a wave's loads complete in issue order, so the activations it
+// needs next wait behind the weights it requested earlier), and each of its
+// two wave rows converts the same weights to fp16.  Here the roles are split.
+// Four producer waves (one per SIMD) load the workgroup's weight tiles (E4M3,
+// or E2M1 with their E4M3 block scales) in stages of 2 chunks, one stage
+// ahead, convert each unit once to fp16 and write it to a two-slot LDS ring;
+// a workgroup barrier publishes each stage.  Eight consumer waves load only
 // activations (one chunk ahead, in registers), read fp16 weights from LDS
 // and run the MFMAs: wave (ms, kidx) holds m-tiles 0-3 (ms = 0) or
 // 1 + 3 ms .. 3 + 3 ms and the chunks kidx, kidx + 2, ...  Every barrier is

@@ -89,12 +89,8 @@ template <int BF, int MT, int T, int NW, int D>
 hipError_t go_d(const DownArgs& d, int grid, hipStream_t st) {
   auto fn = ks_down<BF, MT, T, NW, D>;
   const size_t lds = (size_t)NW * MT * T * 256 * sizeof(float);
-  static bool attr = false;   // idempotent; a race only repeats the call
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  if (hipError_t e = allow_lds((const void*)fn, lds, lds_set); e != hipSuccess) return e;
   hipLaunchKernelGGL(fn, dim3(grid), dim3(64 * NW), lds, st, d);
   return hipGetLastError();
 }

@@ -434,12 +434,8 @@ template <int BF, int T, int C, bool BF16H>
 hipError_t launch_pc(const GateUpArgs& g, int grid, hipStream_t st, const LaunchEvents& ev) {
   auto fn = pc_gateup<BF, T, C, BF16H>;
   constexpr size_t lds = Pc<BF, T, C>::LDS;
-  static bool attr = false;   // idempotent; a race only repeats the call
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  if (hipError_t e = allow_lds((const void*)fn, lds, lds_set); e != hipSuccess) return e;
   launch_kernel(fn, dim3(grid), dim3(64 * (kPcConsumers + kPcProducers)), lds, st, ev, g);
   return hipGetLastError();
 }
@@ -451,12 +447,8 @@ hipError_t launch_ks(const GateUpArgs& g, int grid, hipStream_t st, const Launch
   constexpr int MTW = (MT + MS - 1) / MS;
   auto fn = ks_gateup<BF, MT, T, MS, KS, D, BF16H>;
   const size_t lds = (size_t)(MS == 1 && MT * T <= MS * KS ? T : (T > 1 ? 2 : 1)) * MS * KS * MTW * 64 * sizeof(v4f);
-  static bool attr = false;   // idempotent; a race only repeats the call
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  if (hipError_t e = allow_lds((const void*)fn, lds, lds_set); e != hipSuccess) return e;
   launch_kernel(fn, dim3(grid), dim3(64 * MS * KS), lds, st, ev, g);
   return hipGetLastError();
 }

@@ -393,13 +393,9 @@ __global__ __launch_bounds__(G::THREADS) void lg_down_bf16(DownArgs d) {
 }
 
 template <class G, class Arg>
-hipError_t lg_launch(void (*fn)(Arg), int grid, const Arg& arg, hipStream_t st, bool& attr,
+hipError_t lg_launch(void (*fn)(Arg), int grid, const Arg& arg, hipStream_t st, std::atomic<uint64_t>& lds_set,
                      const LaunchEvents& ev = LaunchEvents{}) {
-  if (!attr) {   // idempotent; a race only repeats the call
-    hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+  if (hipError_t e = allow_lds((const void*)fn, G::LDS, lds_set); e != hipSuccess) return e;
   launch_kernel(fn, dim3(grid), dim3(G::THREADS), G::LDS, st, ev, arg);
   return hipGetLastError();
 }
@@ -419,18 +415,18 @@ hipError_t launch_gateup_large(const Plan& p, const GateUpArgs& g, hipStream_t s
   if ((p.inter / 8) % GUL::RT || p.hidden % kChunk) return hipErrorInvalidValue;
   const int grid = p.n_mblocks * ((p.inter / 8) / GUL::RT);
   if (p.prec == kFP8DownBF16) {
-    static bool attr = false;
-    return lg_launch<GUL>(lg_gateup<GUL, true>, grid, g, st, attr, ev);
+    static std::atomic<uint64_t> lds_set{0};
+    return lg_launch<GUL>(lg_gateup<GUL, true>, grid, g, st, lds_set, ev);
   }
-  static bool attr = false;
-  return lg_launch<GUL>(lg_gateup<GUL, false>, grid, g, st, attr, ev);
+  static std::atomic<uint64_t> lds_set{0};
+  return lg_launch<GUL>(lg_gateup<GUL, false>, grid, g, st, lds_set, ev);
 }
 
 hipError_t launch_down_large(const Plan& p, const DownArgs& d, hipStream_t st) {
   if ((p.hidden / 16) % GDL::RT || p.inter % kChunk || p.prec != kFP8DownBF16) return hipErrorInvalidValue;
   const int grid = p.n_mb2 * ((p.hidden / 16) / GDL::RT);
-  static bool attr = false;
-  return lg_launch<GDL>(lg_down_bf16<GDL>, grid, d, st, attr);
+  static std::atomic<uint64_t> lds_set{0};
+  return lg_launch<GDL>(lg_down_bf16<GDL>, grid, d, st, lds_set);
 }
 
 }  // namespace ocq

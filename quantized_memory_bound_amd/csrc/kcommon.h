@@ -3,6 +3,7 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstddef>
 #include <cstdint>
 
@@ -72,6 +73,21 @@ inline void launch_kernel(K fn, dim3 grid, dim3 block, size_t lds, hipStream_t s
                           Args... args) {
   if (ev.start || ev.end) hipExtLaunchKernelGGL(fn, grid, block, (uint32_t)lds, st, ev.start, ev.end, 0, args...);
   else hipLaunchKernelGGL(fn, grid, block, lds, st, args...);
+}
+
+// A kernel that uses more than 64 KB of dynamic LDS must be allowed it on
+// each device it runs on (the attribute belongs to the device's copy of the
+// kernel).  `done` holds one bit per device ordinal (< 64) on which it has
+// been set; two threads racing only repeat the call.
+inline hipError_t allow_lds(const void* fn, size_t bytes, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev >= 0 && dev < 64 ? (uint64_t)1 << dev : 0;
+  if (bit && (done.load(std::memory_order_relaxed) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_relaxed);
+  return e;
 }
 
 hipError_t launch_gateup(const Plan& p, const GateUpArgs& g, hipStream_t st, const LaunchEvents& ev);

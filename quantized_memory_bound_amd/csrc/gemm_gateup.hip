@@ -215,7 +215,7 @@ __global__ __launch_bounds__(64 * MS * KS) void ks_gateup(GateUpArgs g) {
 // and run the MFMAs: wave (ms, kidx) holds m-tiles 0-3 (ms = 0) or
 // 1 + 3 ms .. 3 + 3 ms and the chunks kidx, kidx + 2, ...  Every barrier is
 // passed by all twelve waves in the same order: one per stage, one after the
-// main loop, one per weight tile in the epilogue.
+// main loop, one after the partial tiles are stored.
 constexpr int kPcConsumers = 8, kPcProducers = 4;
 
 template <int BF_, int T_, int C_>
@@ -230,8 +230,8 @@ struct Pc {
   static constexpr int PW = 1;                         // stages loaded ahead of the one being converted
   static constexpr int W = PW + 1;                     // register buffers of a producer (stages)
   static constexpr int SLOT = CPS * T * 4 * 1024;      // fp16 units of a stage: [chunk][tile][sub-step]
-  static constexpr int RED = kPcConsumers * 4 * 1024;  // epilogue partials of one weight tile
-  static constexpr int LDS = 2 * SLOT > 2 * RED ? 2 * SLOT : 2 * RED;
+  static constexpr int RED = kPcConsumers * 4 * 1024;  // epilogue partials of one weight tile (all T stored at once)
+  static constexpr int LDS = 2 * SLOT > T * RED ? 2 * SLOT : T * RED;
   static_assert(BF == kB_FP8_F16 || BF == kB_FP4_F16, "E4M3 or NVFP4 weights");
   static_assert(W * PPW < 64 && PPW * kPcProducers - US <= kPcProducers, "loads per producer");
   static_assert(CPS % 2 == 0 && C % CPS == 0, "stages of whole chunk pairs");
@@ -305,8 +305,7 @@ __device__ __forceinline__ void pc_producer(const GateUpArgs& g, uint8_t* lds, i
     lds_barrier();   // stage s published
   }
   lds_barrier();   // after the main loop
-#pragma unroll
-  for (int t = 0; t < T; ++t) lds_barrier();   // epilogue tiles
+  lds_barrier();   // partial tiles stored
 }
 
 template <int BF, int NV, int T, int C, bool BF16H>
@@ -376,25 +375,27 @@ __device__ __forceinline__ void pc_consumer(const GateUpArgs& g, uint8_t* lds, i
     }
   }
 
-  // Epilogue, one weight tile at a time: partial tiles to LDS
-  // ([wave][m-tile][lane], two regions used alternately), then the wave that
-  // owns m-tile q sums its two K halves (wave 2 ms, then 2 ms + 1).
+  // Epilogue: every partial tile to LDS at once ([wave][m-tile][tile][lane],
+  // one barrier), then the wave that owns m-tile q sums its two K halves
+  // (wave 2 ms, then 2 ms + 1) tile by tile.
   lds_barrier();   // every consumer is done with the weights; the ring is reused
   float amax[Q][2];
 #pragma unroll
   for (int jq = 0; jq < Q; ++jq) amax[jq][0] = amax[jq][1] = 0.f;
+  v4f* red = (v4f*)lds;   // [wave][m-tile slot][tile][lane]
 #pragma unroll
-  for (int t = 0; t < T; ++t) {
-    v4f* red = (v4f*)(lds + (t & 1) * P::RED);
+  for (int j = 0; j < NV; ++j)
 #pragma unroll
-    for (int j = 0; j < NV; ++j) red[(wave * 4 + j) * 64 + lane] = acc[j][t];
-    lds_barrier();
+    for (int t = 0; t < T; ++t) red[((wave * 4 + j) * T + t) * 64 + lane] = acc[j][t];
+  lds_barrier();
 #pragma unroll
-    for (int jq = 0; jq < Q; ++jq) {
-      const int q = wave + kPcConsumers * jq;
-      if (q < MT) {
-        const int msq = q < 4 ? 0 : (q - 1) / 3, jj = q < 4 ? q : (q - 1) % 3;
-        const v4f v = red[((2 * msq) * 4 + jj) * 64 + lane] + red[((2 * msq + 1) * 4 + jj) * 64 + lane];
+  for (int jq = 0; jq < Q; ++jq) {
+    const int q = wave + kPcConsumers * jq;
+    if (q < MT) {
+      const int msq = q < 4 ? 0 : (q - 1) / 3, jj = q < 4 ? q : (q - 1) % 3;
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const v4f v = red[(((2 * msq) * 4 + jj) * T + t) * 64 + lane] + red[(((2 * msq + 1) * 4 + jj) * T + t) * 64 + lane];
         gateup_tile_epilogue<BF16H, T>(g, v, es.xs[jq], es.cg[t], es.cu[t], row0 + q * 16, ng, t, amax[jq]);
       }
     }

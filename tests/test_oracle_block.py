@@ -267,3 +267,49 @@ def test_code_sums_exact_vs_rationals():
         for j in range(4):
             exact = sum(Fraction(float(F.E4M3[a[i, k]])) * Fraction(float(F.E4M3[b[j, k]])) for k in range(40))
             assert Fraction(float(got[i, j])) == exact
+
+
+# ------------------------------------------------------------------ permutation invariances
+#
+# Relabelling channels must relabel the results and nothing else.  Hidden
+# channels (x columns, gate/up weight columns, down weight rows) permute the
+# x codes and the columns of y and leave h unchanged; intermediate channels
+# (gate/up weight rows, down weight columns) permute h and its codes and
+# leave y unchanged.  The code-domain sums are exact (E4M3 and E2M1 products
+# in fp64), so the equalities are bit-exact.  NVFP4 permutes whole 16-input
+# blocks, which keeps every block scale's inputs together.  A swapped or
+# transposed operand, or a scale or maximum taken along the wrong axis,
+# breaks these.
+
+def _block_perm(rng, n, block):
+    return (rng.permutation(n // block)[:, None] * block + np.arange(block)[None, :]).reshape(-1)
+
+
+@pytest.mark.parametrize("prec", [O.PREC_FP8, O.PREC_FP8_DOWN_BF16, O.PREC_FP4])
+def test_hidden_channel_permutation(prec):
+    d = I.make_inputs(256, 384, 11, x_outliers=True, w_std=0.02, seed=31 + prec)
+    rng = np.random.default_rng(5)
+    p = _block_perm(rng, 256, 16 if prec == O.PREC_FP4 else 1)
+    a = O.block_reference(d["x_bits"], d["w_gate"], d["w_up"], d["w_down"], prec)
+    b = O.block_reference(np.ascontiguousarray(d["x_bits"][:, p]), np.ascontiguousarray(d["w_gate"][:, p]),
+                          np.ascontiguousarray(d["w_up"][:, p]), np.ascontiguousarray(d["w_down"][p, :]), prec)
+    assert np.array_equal(b["xq"], a["xq"][:, p]) and np.array_equal(b["sx"], a["sx"])
+    for key in ("hb",) if prec == O.PREC_FP8_DOWN_BF16 else ("hq", "sh"):
+        assert np.array_equal(b[key], a[key]), key
+    assert np.array_equal(b["y"], a["y"][:, p])
+
+
+@pytest.mark.parametrize("prec", [O.PREC_FP8, O.PREC_FP8_DOWN_BF16, O.PREC_FP4])
+def test_intermediate_channel_permutation(prec):
+    d = I.make_inputs(256, 384, 11, x_outliers=True, w_std=0.02, seed=37 + prec)
+    rng = np.random.default_rng(6)
+    p = _block_perm(rng, 384, 16 if prec == O.PREC_FP4 else 1)
+    a = O.block_reference(d["x_bits"], d["w_gate"], d["w_up"], d["w_down"], prec)
+    b = O.block_reference(d["x_bits"], np.ascontiguousarray(d["w_gate"][p, :]), np.ascontiguousarray(d["w_up"][p, :]),
+                          np.ascontiguousarray(d["w_down"][:, p]), prec)
+    assert np.array_equal(b["xq"], a["xq"]) and np.array_equal(b["sx"], a["sx"])
+    if prec == O.PREC_FP8_DOWN_BF16:
+        assert np.array_equal(b["hb"], a["hb"][:, p])
+    else:
+        assert np.array_equal(b["hq"], a["hq"][:, p]) and np.array_equal(b["sh"], a["sh"])
+    assert np.array_equal(b["y"], a["y"])

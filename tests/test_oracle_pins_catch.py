@@ -1,0 +1,51 @@
+"""The channel-permutation pins must fail for plausible oracle mistakes.
+
+Each case loads a fresh copy of oracle/mlp.py with one mistake planted in its
+source text (never in the real module), runs the two permutation pins of
+test_oracle_block.py against the copy in all three modes, and requires at
+least one of them to fail."""
+
+import types
+
+import pytest
+
+import test_oracle_block as T
+from oracle import mlp as O
+
+SRC_PATH = O.__file__
+PLANTS = {
+    # per-row scales taken along the wrong axis (columns)
+    "scale_axis": ("amax = np.max(np.abs(a32), axis=1) if a32.shape[1] else np.zeros(a32.shape[0], np.float32)",
+                   "amax = (np.max(np.abs(a32), axis=0)[:a32.shape[0]] if a32.shape[0] <= a32.shape[1] "
+                   "else np.max(np.abs(a32), axis=1)) if a32.shape[1] else np.zeros(a32.shape[0], np.float32)"),
+    # output-channel scales applied to the wrong columns
+    "column_scales": ("return acc * a_scale.astype(np.float64)[:, None] * w_packed[1].astype(np.float64)[None, :]",
+                      "return acc * a_scale.astype(np.float64)[:, None] * np.sort(w_packed[1]).astype(np.float64)[None, :]"),
+    # the down projection's inputs paired with the wrong weight columns
+    "down_input_order": ('Y = _projection(dec_e4m3(hq), sh, packed["down"], "fp4" if prec == PREC_FP4 else "fp8")',
+                         'Y = _projection(dec_e4m3(hq)[:, ::-1].copy(), sh, packed["down"], '
+                         '"fp4" if prec == PREC_FP4 else "fp8")'),
+}
+
+
+def _planted(old, new):
+    src = open(SRC_PATH).read()
+    assert src.count(old) == 1, "the planted line is no longer in the oracle"
+    mod = types.ModuleType("oracle.mlp_planted")
+    mod.__file__ = SRC_PATH
+    mod.__package__ = "oracle"   # the oracle's relative imports
+    exec(compile(src.replace(old, new), SRC_PATH, "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(PLANTS))
+def test_permutation_pins_catch(name, monkeypatch):
+    monkeypatch.setattr(T, "O", _planted(*PLANTS[name]))
+    caught = 0
+    for prec in (O.PREC_FP8, O.PREC_FP8_DOWN_BF16, O.PREC_FP4):
+        for pin in (T.test_hidden_channel_permutation, T.test_intermediate_channel_permutation):
+            try:
+                pin(prec)
+            except (AssertionError, ValueError, IndexError):
+                caught += 1
+    assert caught > 0, "planted mistake %s passes every permutation pin" % name

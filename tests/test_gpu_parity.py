@@ -235,14 +235,20 @@ def test_gateup_weight_producers(hidden, inter, M, prec):
 
 # one workspace for a sequence of calls: different rows each time, and a call
 # that takes the LDS-tiled kernels in between
-def test_workspace_reuse():
-    print("case workspace reuse", flush=True)
-    H, Iw, prec = 256, 768, 0
-    d = I.make_inputs(H, Iw, 420, x_outliers=True, seed=5)
+# (H = 2048: the 13-m-tile gate/up with weight producers, one and two
+# m-blocks, between skinny calls)
+@pytest.mark.parametrize("H,Iw,prec,n,seq", [
+    (256, 768, 0, 420, ((0, 16), (16, 32), (0, 420), (100, 116), (200, 213), (0, 16))),
+    (2048, 1024, 0, 300, ((0, 208), (0, 16), (0, 300), (100, 113), (40, 248), (0, 13))),
+    (2048, 1024, 2, 300, ((0, 300), (7, 20), (0, 208), (0, 52)))])
+def test_workspace_reuse(H, Iw, prec, n, seq):
+    print("case workspace reuse H=%d prec=%d" % (H, prec), flush=True)
+    d = I.make_inputs(H, Iw, n, x_outliers=True, seed=5)
     blob = ocq.pack_weights(d["w_gate"], d["w_up"], d["w_down"], prec)
-    nws = max(ocq.workspace_bytes(m, H, Iw, prec) for m in (13, 16, 420))
+    nws = max(ocq.workspace_bytes(b - a, H, Iw, prec) for a, b in seq)
     ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
-    for rows in (slice(0, 16), slice(16, 32), slice(0, 420), slice(100, 116), slice(200, 213), slice(0, 16)):
+    for a, b in seq:
+        rows = slice(a, b)
         xb = np.ascontiguousarray(d["x_bits"][rows])
         y = ocq.mlp_forward(blob, _to_dev_bf16(xb), H, Iw, prec, workspace=ws)
         torch.cuda.synchronize()

@@ -29,9 +29,12 @@ What is computed, step by step, and the passage each step follows:
 
 Readings where the pages are silent (all listed with the design notes):
   * scale = fl32(amax / 448); zero amax -> scale 0 and all codes +0.
-  * every quantization decision (a code) is taken on the binary32 quotient
-    value/scale, i.e. on what an fp32 kernel holds; in particular h is
-    rounded to binary32 before its amax, scale and codes are formed.
+  * the weights and x are binary32 values (bf16 x, fp32 weights); their codes
+    are decided on the binary32 quotient fl32(value / scale), the true
+    float32 division both the packer and the x quantization perform.
+  * h is the exact (fp64) SiLU(G) * U: its row maximum, its scale and its
+    codes E4M3(h / sh) are taken from the fp64 values with no binary32
+    rounding in between, and bf16(h) is rounded directly from fp64.
   * scales apply after the integer-code sums (exact algebra for per-row and
     per-column scales); NVFP4 block scales apply inside the sum.
   * in the BF16-down mode h enters the down projection as bf16(h) with no
@@ -63,14 +66,18 @@ def _f32(a):
 
 
 def quantize_rows_e4m3(a):
-    """Per-row absmax E4M3 quantization.
+    """Per-row absmax E4M3 quantization of binary32 values (weights per
+    output channel, x per token).
 
-    a: 2-D array.  The values are first taken as binary32 (a no-op for fp32
-    weights and bf16 activations; the fp32 rounding of h for the
-    intermediate).  Returns (codes uint8 [R, C], scales float32 [R]) with
-    scale = fl32(amax / 448) and codes = E4M3(fl32(value / scale)).
+    a: 2-D array whose values are all exactly representable in binary32
+    (fp32 weights; bf16 activations, possibly times a float32 multiplier).
+    Returns (codes uint8 [R, C], scales float32 [R]) with
+    scale = fl32(amax / 448) and codes = E4M3(fl32(value / scale)): the
+    quotient is the correctly rounded float32 division of two float32 values.
     """
-    a32 = _f32(a)
+    a64 = np.asarray(a, dtype=np.float64)
+    a32 = a64.astype(np.float32)
+    assert np.array_equal(a32.astype(np.float64), a64, equal_nan=True), "values must be binary32"
     amax = np.max(np.abs(a32), axis=1) if a32.shape[1] else np.zeros(a32.shape[0], np.float32)
     scale = _f32(amax.astype(np.float64) / 448.0)
     codes = np.zeros(a32.shape, dtype=np.uint8)
@@ -78,6 +85,24 @@ def quantize_rows_e4m3(a):
     if np.any(nz):
         quot = _f32(a32[nz].astype(np.float64) / scale[nz, None].astype(np.float64))
         codes[nz] = enc_e4m3(quot)
+    return codes, scale
+
+
+def quantize_h_e4m3(h):
+    """Per-token E4M3 requantization of the intermediate h (fp64 values).
+
+    sh = fl32(max_n |h| / 448) (the scale is stored as float32); codes =
+    E4M3(h / sh) with the quotient taken in fp64 from the fp64 h, so no
+    binary32 rounding of h or of the quotient comes between the exact
+    intermediate and its code.  A zero row gets sh = 0 and codes +0.
+    """
+    h = np.asarray(h, dtype=np.float64)
+    amax = np.max(np.abs(h), axis=1) if h.shape[1] else np.zeros(h.shape[0])
+    scale = _f32(amax / 448.0)
+    codes = np.zeros(h.shape, dtype=np.uint8)
+    nz = scale > 0
+    if np.any(nz):
+        codes[nz] = enc_e4m3(h[nz] / scale[nz, None].astype(np.float64))
     return codes, scale
 
 
@@ -264,11 +289,11 @@ def forward(x_bits, packed):
 
     out = {"xq": xq, "sx": sx, "h": h}
     if prec == PREC_FP8_DOWN_BF16:
-        hb = rne_bf16(_f32(h).astype(np.float64))
+        hb = rne_bf16(h)
         Y = bf16_to_f64(hb) @ bf16_to_f64(packed["down"]).T
         out["hb"] = hb
     else:
-        hq, sh = quantize_rows_e4m3(h)
+        hq, sh = quantize_h_e4m3(h)
         Y = _projection(dec_e4m3(hq), sh, packed["down"], "fp4" if prec == PREC_FP4 else "fp8")
         out["hq"] = hq
         out["sh"] = sh

@@ -47,6 +47,16 @@ def _torch_e4m3_values(codes):
     return torch.from_numpy(np.asarray(codes, np.uint8)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
 
 
+def _agree_up_to_binary32_ties(got, ref, exact):
+    """got: values the oracle decided from the exact values `exact`; ref: a
+    library's decision on their float32 rounding.  They may differ only
+    where that rounding moved a value onto or across a midpoint, so a
+    differing entry of got must be at least as near to the exact value."""
+    diff = got != ref
+    assert np.all(np.abs(got[diff] - exact[diff]) <= np.abs(ref[diff] - exact[diff]))
+    assert np.mean(diff) <= 1e-3
+
+
 def _silu_torch(g):
     return torch.nn.functional.silu(torch.from_numpy(g)).numpy()
 
@@ -81,11 +91,13 @@ def test_lossless_fp8_block_equals_textbook_mlp(seed):
     U = d["x"] @ d["wu"].astype(np.float64).T
     h = _silu_torch(G) * U
     np.testing.assert_allclose(out["h"], h, rtol=1e-13, atol=0)
-    # requant: scale = fl32(amax/448) and codes by torch's own E4M3 cast
-    h32 = out["h"].astype(np.float32)
-    sh = (np.max(np.abs(h32), axis=1) / np.float32(448)).astype(np.float32)
+    # requant of the exact h: scale = fl32(amax/448); codes by torch's own E4M3
+    # cast, which rounds through float32 and may differ only where that
+    # rounding decides a near-tie (there the oracle's code must be the nearer)
+    sh = (np.max(np.abs(h), axis=1) / 448.0).astype(np.float32)
     assert np.array_equal(out["sh"], sh)
-    assert np.array_equal(out["hq"], _torch_e4m3_codes(h32 / sh[:, None]))
+    q = h / sh[:, None].astype(np.float64)
+    _agree_up_to_binary32_ties(F.dec_e4m3(out["hq"]), _torch_e4m3_values(_torch_e4m3_codes(q)), q)
     # down: textbook (dequantized h) W_d^T, W_d exact on its grid
     Y = (_torch_e4m3_values(out["hq"]) * sh[:, None].astype(np.float64)) @ wd.T
     np.testing.assert_allclose(out["Y"], Y, rtol=1e-13, atol=1e-300)
@@ -104,9 +116,10 @@ def test_lossless_bf16_down_equals_textbook(seed):
     U = d["x"] @ d["wu"].astype(np.float64).T
     h = _silu_torch(G) * U
     np.testing.assert_allclose(out["h"], h, rtol=1e-13)
-    hb = torch.from_numpy(out["h"].astype(np.float32)).to(torch.bfloat16)
-    assert np.array_equal(out["hb"], hb.view(torch.int16).numpy().view(np.uint16))
-    Y = hb.to(torch.float64).numpy() @ wd.astype(np.float64).T
+    # bf16(h) rounded once from the exact h; torch rounds through float32
+    hb_t = torch.from_numpy(h.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    _agree_up_to_binary32_ties(F.bf16_to_f64(out["hb"]), hb_t, h)
+    Y = F.bf16_to_f64(out["hb"]) @ wd.astype(np.float64).T
     np.testing.assert_allclose(out["Y"], Y, rtol=1e-13, atol=1e-300)
 
 
@@ -313,3 +326,83 @@ def test_intermediate_channel_permutation(prec):
     else:
         assert np.array_equal(b["hq"], a["hq"][:, p]) and np.array_equal(b["sh"], a["sh"])
     assert np.array_equal(b["y"], a["y"])
+
+
+# ------------------------------------------------------------------ h requantization from fp64
+
+def test_h_requant_decides_on_fp64_values(golden):
+    """The requantization of h takes its codes from the exact fp64 h (hand-
+    derived cases 2^-40 off an E4M3 midpoint, where a binary32 rounding of h
+    would land on the tie and round to the even code instead)."""
+    from conftest import parse_num
+    rows = golden("h_requant_fp64_cases.txt")
+    vals = np.array([parse_num(v) for v, _, _ in rows])
+    want = np.array([int(c, 16) for _, c, _ in rows], dtype=np.uint8)
+    assert np.all(vals.astype(np.float32).astype(np.float64) != vals)     # none is a binary32 value
+    h = np.concatenate([[448.0], vals])[None, :]
+    codes, sh = O.quantize_h_e4m3(h)
+    assert sh[0] == np.float32(1.0)
+    assert codes[0, 0] == 0x7E
+    for (v, _, why), got, exp in zip(rows, codes[0, 1:], want):
+        assert got == exp, "%s: got %#x want %#x (%s)" % (v, got, exp, why)
+
+
+def test_h_requant_scale_rule_and_zero_row():
+    # the row maximum is taken on fp64 |h| and the scale stored as float32;
+    # a zero row (and a row of -0) gets scale 0 and +0 codes
+    h = np.array([[0.0, -0.0, 0.0], [3.0, -7.0, 1.0], [-0.0, -0.0, -0.0]])
+    codes, sh = O.quantize_h_e4m3(h)
+    assert sh[0] == 0 and sh[2] == 0 and np.all(codes[[0, 2]] == 0)
+    assert sh[1] == np.float32(7.0 / 448.0)
+    assert codes[1, 1] == 0xFE                          # -amax -> -448 (exact saturation)
+    q = np.array([3.0, 1.0]) / np.float64(sh[1])
+    assert np.array_equal(codes[1, [0, 2]], F.enc_e4m3(q))
+
+
+def test_bf16_h_rounds_fp64_directly():
+    # bf16(h) in the BF16-down mode is one rounding of the fp64 h: a value
+    # 2^-40 above the 1 / 1+2^-7 midpoint goes up; a binary32 rounding first
+    # would make it the tie, which goes to the even 1.0
+    v = np.array([1.0 + 2.0 ** -8 + 2.0 ** -40, 1.0 + 2.0 ** -8])
+    assert np.array_equal(F.rne_bf16(v), np.array([0x3F81, 0x3F80], dtype=np.uint16))
+    assert np.array_equal(F.rne_bf16(v.astype(np.float32).astype(np.float64)),
+                          np.array([0x3F80, 0x3F80], dtype=np.uint16))
+
+
+def _tie_block():
+    """A 5-input, 3-intermediate block built by hand so that h lands 2^-34
+    (relative) past a bf16 and an E4M3 midpoint.  Every x row and weight
+    row holds a 448, so every scale is 1 and every code is its value.
+
+      x codes       [448, 256, 16, 2^-9, 0]
+      gate rows     [0, 256, 16, 2^-9, 448]  -> G0 = 65536 + 256 + 2^-18
+                    [0, 256, 256, 2^-9, 448] -> G1 = 65536 + 4096 + 2^-18
+                    [256, 0, 0, 0, 448]      -> G2 = 448 * 256 = 114688
+      up rows       [0, 0, 2^-4, 0, 448]     -> U = 16 * 2^-4 = 1 (all three)
+    G >= 40, so SiLU(G) = G exactly in fp64, and h = G.
+    """
+    x = np.array([[448.0, 256.0, 16.0, 2.0 ** -9, 0.0]])
+    wg = np.array([[0, 256, 16, 2.0 ** -9, 448], [0, 256, 256, 2.0 ** -9, 448], [256, 0, 0, 0, 448]], np.float32)
+    wu = np.tile(np.array([[0, 0, 2.0 ** -4, 0, 448]], np.float32), (3, 1))
+    wd = np.eye(5, 3, dtype=np.float32)
+    return _bf16_bits_exact(x), wg, wu, wd
+
+
+def test_tie_block_bf16_h():
+    # h0 = 2^16 (1 + 2^-8 + 2^-34): just above the bf16 midpoint of 65536
+    # (0x4780) and 66048 (0x4781) -> 0x4781; its float32 rounding (65792) is
+    # the tie itself, which would go to the even 0x4780
+    x_bits, wg, wu, wd = _tie_block()
+    out = O.block_reference(x_bits, wg, wu, wd, O.PREC_FP8_DOWN_BF16)
+    assert out["h"][0, 0] == 65792.0 + 2.0 ** -18
+    assert list(out["hb"][0]) == [0x4781, 0x4788, 0x47E0]
+
+
+def test_tie_block_e4m3_h():
+    # sh = fl32(114688 / 448) = 256; h1 / sh = 272 + 2^-26, just above the
+    # E4M3 midpoint of 256 (0x78) and 288 (0x79) -> 0x79 (float32 would tie
+    # to the even 0x78); h0 / sh = 257 + 2^-26 -> 256 (0x78); h2 / sh = 448
+    x_bits, wg, wu, wd = _tie_block()
+    out = O.block_reference(x_bits, wg, wu, wd, O.PREC_FP8)
+    assert out["sh"][0] == np.float32(256.0)
+    assert list(out["hq"][0]) == [0x78, 0x79, 0x7E]

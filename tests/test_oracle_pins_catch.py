@@ -1,9 +1,10 @@
-"""The channel-permutation pins must fail for plausible oracle mistakes.
+"""The oracle's pins must fail for plausible oracle mistakes.
 
 Each case loads a fresh copy of oracle/mlp.py with one mistake planted in its
-source text (never in the real module), runs the two permutation pins of
-test_oracle_block.py against the copy in all three modes, and requires at
-least one of them to fail."""
+source text (never in the real module), runs pins of test_oracle_block.py
+against the copy (the two channel-permutation pins in all three modes, or the
+hand-built tie-block pins of the h requantization), and requires at least one
+of them to fail."""
 
 import types
 
@@ -36,6 +37,31 @@ def _planted(old, new):
     mod.__package__ = "oracle"   # the oracle's relative imports
     exec(compile(src.replace(old, new), SRC_PATH, "exec"), mod.__dict__)
     return mod
+
+
+# h rounded to binary32 before its decisions (the requantization or the
+# bf16 rounding of the BF16-down mode): caught by the hand-built tie block
+H_PLANTS = {
+    "h_codes_via_binary32": ("codes[nz] = enc_e4m3(h[nz] / scale[nz, None].astype(np.float64))",
+                             "codes[nz] = enc_e4m3((h[nz] / scale[nz, None].astype(np.float64))"
+                             ".astype(np.float32).astype(np.float64))"),
+    "h_amax_via_binary32": ("amax = np.max(np.abs(h), axis=1) if h.shape[1] else np.zeros(h.shape[0])",
+                            "h = h.astype(np.float32).astype(np.float64); "
+                            "amax = np.max(np.abs(h), axis=1) if h.shape[1] else np.zeros(h.shape[0])"),
+    "hb_via_binary32": ("hb = rne_bf16(h)", "hb = rne_bf16(h.astype(np.float32).astype(np.float64))"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(H_PLANTS))
+def test_tie_block_pins_catch(name, monkeypatch):
+    monkeypatch.setattr(T, "O", _planted(*H_PLANTS[name]))
+    caught = 0
+    for pin in (T.test_tie_block_bf16_h, T.test_tie_block_e4m3_h):
+        try:
+            pin()
+        except AssertionError:
+            caught += 1
+    assert caught > 0, "planted mistake %s passes the tie-block pins" % name
 
 
 @pytest.mark.parametrize("name", sorted(PLANTS))

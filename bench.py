@@ -140,6 +140,92 @@ def cpu_baseline(inp, prec, M, seconds):
     return dt, reps, threads
 
 
+def capture_steps(torch, step, n):
+    """A HIP graph of steps 0 .. n-1 (None for n = 0), captured on a side stream."""
+    if n == 0:
+        return None
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+        for i in range(n):
+            step(i)
+    return g
+
+
+def roofline(nbytes, flops, prec, seconds, traffic):
+    """Roofline object of the gate/up kernel.  Binding bound (the larger of
+    the two times): HBM at 8 TB/s for the algorithmic bytes, or the matrix
+    cores at the peak of the contraction's own type -- E4M3 x E4M3 (FP8,
+    5 PFLOP/s) for the E4M3 weights; NVFP4 on its exact dequantized path at
+    the fp16 rate (2.5 PFLOP/s).  frac is against the binding bound; the other
+    fractions are given beside it, including the f16 peak of the instruction
+    the kernel runs (its E4M3 operands are converted exactly to fp16)."""
+    mfma_peak = MFMA_F16_PEAK_TFLOPS if prec == 2 else MFMA_FP8_PEAK_TFLOPS
+    t_hbm = nbytes / (HBM_PEAK_GBPS * 1e9)
+    t_mfma = flops / (mfma_peak * 1e12)
+    gbps = nbytes / seconds / 1e9
+    tflops = flops / seconds / 1e12
+    if t_mfma > t_hbm:
+        r = {"bound": "mfma", "achieved": round(tflops, 2), "peak": mfma_peak, "unit": "TFLOP/s",
+             "frac": round(tflops / mfma_peak, 4)}
+    else:
+        r = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+             "frac": round(gbps / HBM_PEAK_GBPS, 4)}
+    r["traffic"] = traffic
+    r["alg_bytes_per_launch"] = nbytes
+    r["alg_flops_per_launch"] = flops
+    r["frac_hbm"] = round(gbps / HBM_PEAK_GBPS, 4)
+    r["frac_mfma_fp8"] = round(tflops / MFMA_FP8_PEAK_TFLOPS, 4)
+    r["frac_mfma_f16"] = round(tflops / MFMA_F16_PEAK_TFLOPS, 4)
+    return r
+
+
+def stream_ceiling(torch, ocq, nbytes, dev, reps=64):
+    """GB/s of the library's plain streaming-read kernel reading nbytes per
+    launch (rounded to 16 B), launches replayed from a graph over a 1 GiB
+    buffer so no read hits the 256 MB last-level cache."""
+    n = max(16, nbytes // 16 * 16)
+    span = max(1 << 30, 4 * n)
+    buf = torch.ones(span, dtype=torch.uint8, device=dev)
+    out = torch.empty(2048, dtype=torch.int32, device=dev)
+    nslot = span // n
+    step = lambda i: ocq.diag_stream_read(buf[(i % nslot) * n:(i % nslot + 1) * n], out, 2048)
+    g = capture_steps(torch, step, reps)
+    g.replay()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    sec = t0.elapsed_time(t1) * 1e-3 / reps
+    del buf
+    return n / sec / 1e9
+
+
+def launch_floor(torch, ocq, reps=200):
+    """Seconds per launch of an empty kernel, replayed from a graph."""
+    g = capture_steps(torch, lambda i: ocq.diag_empty(), reps)
+    g.replay()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) * 1e-3 / reps
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -201,22 +287,20 @@ def main():
 
     # --- timed region: K steps, HIP events on the stream the kernels run on
     if args.mode == "graph":
-        # one captured graph holds R consecutive steps (one per weight copy)
-        cs = torch.cuda.Stream()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=cs):
-            for i in range(R):
-                step(i)
-        for _ in range(2):
-            graph.replay()
+        # one captured graph holds R consecutive steps (one per weight copy),
+        # a second one the K mod R steps left over, so exactly K steps run
+        full, rest = capture_steps(torch, step, R), capture_steps(torch, step, K % R)
+        for g in (full, rest):
+            if g is not None:
+                g.replay()
         torch.cuda.synchronize()
-        n_rep = -(-K // R)
-        K = n_rep * R
         t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t_start.record()
-        for _ in range(n_rep):
-            graph.replay()
+        for _ in range(K // R):
+            full.replay()
+        if rest is not None:
+            rest.replay()
         t_end.record()
         torch.cuda.synchronize()
     else:
@@ -260,31 +344,23 @@ def main():
     roof = None
     if gu_ms:
         gbytes, gflops = gateup_alg(M, H, Iw, prec)
-        t_hbm = gbytes / (HBM_PEAK_GBPS * 1e9)
-        t_mfma = gflops / (MFMA_F16_PEAK_TFLOPS * 1e12)
         traffic = read_traffic(args.workload if args.M is None else "%s_M%d" % (args.workload, M),
                                kernel_source_digest())
-        if t_mfma > t_hbm:
-            ach = gflops / (gu_ms * 1e-3) / 1e12
-            roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(ach / MFMA_F16_PEAK_TFLOPS, 4), "traffic": traffic}
-        else:
-            ach = gbytes / (gu_ms * 1e-3) / 1e9
-            roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                    "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": traffic}
-        roof["kernel"] = "k_gateup (gate/up GEMM + SiLU*up + per-token amax)"
+        roof = roofline(gbytes, gflops, prec, gu_ms * 1e-3, traffic)
+        roof["kernel"] = "gate/up GEMM + SiLU*up + per-token amax"
         roof["us_per_launch"] = round(gu_ms * 1e3, 3)
         roof["timing"] = gu_how
-        roof["alg_bytes_per_launch"] = gbytes
-        roof["alg_flops_per_launch"] = gflops
-        roof["hbm_frac_at_this_duration"] = round(gbytes / (gu_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
+        ceil = stream_ceiling(torch, ocq, gbytes, dev)
+        roof["stream_ceiling_GBps"] = round(ceil, 1)
+        roof["frac_of_stream_ceiling"] = round(gbytes / (gu_ms * 1e-3) / 1e9 / ceil, 4)
+        roof["launch_floor_us"] = round(launch_floor(torch, ocq) * 1e6, 3)
 
     cpu = None
     if not args.no_cpu_baseline:
         dt, reps, threads = cpu_baseline(inp, prec, M, args.cpu_seconds)
         cpu = {"value": round(ab / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
                "sample": "whole block, all %d rows, weights pre-packed, %d repetitions (%.2f s each)" % (M, reps, dt),
-               "tokens_per_s": round(M / dt, 1), "us_per_block": round(dt * 1e6, 1)}
+               "tokens_per_s": round(M / dt, 1), "us_per_block": round(dt * 1e6, 1), "cpu_model": cpu_model()}
 
     prec_name = {0: "fp8_e4m3", 1: "fp8_e4m3 gate/up + bf16 down", 2: "nvfp4 (e2m1 + e4m3 block scales)"}[prec]
     out = {
@@ -342,20 +418,18 @@ def run_stack(args):
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    cs = torch.cuda.Stream()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=cs):
-        for i in range(R):
-            step(i)
-    for _ in range(2):
-        graph.replay()
+    K = args.steps
+    full, rest = capture_steps(torch, step, R), capture_steps(torch, step, K % R)
+    for g in (full, rest):
+        if g is not None:
+            g.replay()
     torch.cuda.synchronize()
-    n_rep = max(1, -(-args.steps // R))
-    K = n_rep * R
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record()
-    for _ in range(n_rep):
-        graph.replay()
+    for _ in range(K // R):
+        full.replay()
+    if rest is not None:
+        rest.replay()
     t1.record()
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / K
@@ -378,7 +452,7 @@ def run_stack(args):
         threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
         cpu = {"value": round(ab / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
                "sample": "whole stack, all %d rows, weights pre-packed, %d repetitions (%.2f s each)" % (M, reps, dt),
-               "tokens_per_s": round(M / dt, 1)}
+               "tokens_per_s": round(M / dt, 1), "cpu_model": cpu_model()}
     names = {0: "fp8", 1: "fp8+bf16down", 2: "nvfp4"}
     out = {
         "metric": "achieved HBM GB/s (% of peak) + verified tokens/s per MLP stack (" + str(len(modes)) + " blocks)",

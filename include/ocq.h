@@ -211,6 +211,34 @@ ocq_status ocq_check_blob(const void* packed_dev, size_t packed_bytes, int hidde
  * stay valid while the hook is set. */
 ocq_status ocq_set_stage_events(void* const* events, int count);
 
+/* Measurement helpers (not part of the block; used by the benchmark and the
+ * tests to state what the block's timings and arithmetic are measured
+ * against).  All are asynchronous on `stream` and return OCQ_OK,
+ * OCQ_ERR_INVALID_ARG (bad size or pointer, checked before any launch) or
+ * OCQ_ERR_DEVICE (launch failure).
+ *
+ * ocq_diag_stream_read: read `bytes` bytes (a multiple of 16, > 0) of the
+ *   16-byte-aligned device buffer src_dev with 16-byte loads, `blocks`
+ *   workgroups of 256 lanes (1 <= blocks <= 65536), each writing one uint32
+ *   to out_dev[block] so the loads are kept: the practical HBM read ceiling
+ *   for one launch of that many bytes (the block streams its weights the
+ *   same way: "Why decoding dominates latency" in the post, weights read on
+ *   every step).
+ * ocq_diag_empty: one empty kernel (the fixed cost of a launch).
+ * ocq_diag_mfma_dot: c[m][n] = sum_k dec(a[m][k]) dec(b[n][k]) over E4M3
+ *   codes (a: uint8 [M][K], b: uint8 [N][K], c: float [M][N], row-major,
+ *   device, 16-byte aligned; M, N multiples of 16, K a multiple of 128,
+ *   M, N, K <= 65536) through one matrix-core instruction form, with the
+ *   block's fragment order and per-chunk instruction sequence:
+ *     form 0: operands converted exactly to fp16, MFMA 16x16x32 f16 (fp32 sums)
+ *     form 1: MFMA 16x16x128 f8f6f4 on the E4M3 codes (unit scales)
+ *     form 2: MFMA 16x16x32 fp8 x fp8 on the E4M3 codes
+ *   so that each form's sums can be compared against exact ones. */
+ocq_status ocq_diag_stream_read(const void* src_dev, size_t bytes, void* out_dev, int blocks, void* stream);
+ocq_status ocq_diag_empty(void* stream);
+ocq_status ocq_diag_mfma_dot(int form, const void* a_dev, const void* b_dev, int M, int N, int K, float* c_dev,
+                             void* stream);
+
 /* Message for the last failure on this thread ("" if none). */
 const char* ocq_last_error(void);
 

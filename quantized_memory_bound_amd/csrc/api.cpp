@@ -179,6 +179,33 @@ ocq_status ocq_mlp_forward(const void* packed_dev, size_t packed_bytes, const vo
   return OCQ_OK;
 }
 
+ocq_status ocq_diag_stream_read(const void* src_dev, size_t bytes, void* out_dev, int blocks, void* stream) {
+  g_err.clear();
+  if (!src_dev || !out_dev || !aligned16(src_dev)) return set_error(OCQ_ERR_INVALID_ARG, "null or misaligned pointer");
+  if (bytes == 0 || bytes % 16 || blocks < 1 || blocks > 65536)
+    return set_error(OCQ_ERR_INVALID_ARG, "bytes must be a positive multiple of 16, blocks in [1, 65536]");
+  int rc = diag_stream_read(src_dev, bytes, out_dev, blocks, stream);
+  return rc ? set_hip_error((hipError_t)rc, "kernel launch") : OCQ_OK;
+}
+
+ocq_status ocq_diag_empty(void* stream) {
+  g_err.clear();
+  int rc = diag_empty(stream);
+  return rc ? set_hip_error((hipError_t)rc, "kernel launch") : OCQ_OK;
+}
+
+ocq_status ocq_diag_mfma_dot(int form, const void* a_dev, const void* b_dev, int M, int N, int K, float* c_dev,
+                             void* stream) {
+  g_err.clear();
+  if (form < 0 || form > 2) return set_error(OCQ_ERR_INVALID_ARG, "form must be 0, 1 or 2");
+  if (M < 16 || N < 16 || K < 128 || M % 16 || N % 16 || K % 128 || M > 65536 || N > 65536 || K > 65536)
+    return set_error(OCQ_ERR_INVALID_ARG, "M, N multiples of 16 and K a multiple of 128, each <= 65536");
+  if (!a_dev || !b_dev || !c_dev || !aligned16(a_dev) || !aligned16(b_dev) || !aligned16(c_dev))
+    return set_error(OCQ_ERR_INVALID_ARG, "null or misaligned pointer");
+  int rc = diag_mfma_dot(form, (const uint8_t*)a_dev, (const uint8_t*)b_dev, M, N, K, c_dev, stream);
+  return rc ? set_hip_error((hipError_t)rc, "kernel launch") : OCQ_OK;
+}
+
 static size_t stack_ws(int M, int hidden, int inter, const int* modes, int L, size_t* act_off) {
   size_t w = 0;
   for (int l = 0; l < L; ++l) {

@@ -93,9 +93,7 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<BF, MT, T>& r, const LanePt
 // B operand of tile t, sub-step i, from raw registers
 template <int BF, int MT, int T>
 __device__ __forceinline__ auto b_from_regs(const ChunkRegs<BF, MT, T>& r, int t, int i) {
-  if constexpr (BF == kB_FP8) {
-    return cat(r.b[t][0], r.b[t][1]);
-  } else if constexpr (BF == kB_FP8_F16) {
+  if constexpr (BF == kB_FP8_F16) {
     const v4i& w = r.b[t][i >> 1];
     return e4m3x8_to_f16((uint32_t)w[2 * (i & 1)], (uint32_t)w[2 * (i & 1) + 1]);
   } else if constexpr (BF == kB_BF16) {
@@ -109,37 +107,26 @@ __device__ __forceinline__ auto b_from_regs(const ChunkRegs<BF, MT, T>& r, int t
 
 // acc[j][t] += A[j] x B[t] over one chunk (all NMT m-tiles; padding tiles
 // hold duplicate data and are discarded by the caller)
+// (MFMA 16x16x32 f16 on exact fp16 conversions of E4M3 / E2M1 operands, or
+// 16x16x32 bf16; four sub-steps of 32 inputs per chunk)
 template <int BF, int NMT, int T, class BGet>
 __device__ __forceinline__ void compute_chunk(v4f (&acc)[NMT][T], const AFrag<BF> (&a)[NMT], int, BGet bget) {
-  if constexpr (BF == kB_FP8) {
-    v8i b[T];
 #pragma unroll
-    for (int t = 0; t < T; ++t) b[t] = bget(t, 0);
+  for (int i = 0; i < 4; ++i) {
+    decltype(bget(0, 0)) b[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) b[t] = bget(t, i);
 #pragma unroll
     for (int j = 0; j < NMT; ++j) {
-      const v8i av = cat(a[j].q[0], a[j].q[1]);
+      if constexpr (BF == kB_BF16) {
+        const v8bf av = __builtin_bit_cast(v8bf, a[j].q[i]);
 #pragma unroll
-      for (int t = 0; t < T; ++t)
-        acc[j][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, b[t], acc[j][t], 0, 0, 0, 0, 0, 0);
-    }
-  } else {
+        for (int t = 0; t < T; ++t) acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b[t], acc[j][t], 0, 0, 0);
+      } else {
+        const v4i& w = a[j].q[i >> 1];
+        const v8h av = e4m3x8_to_f16((uint32_t)w[2 * (i & 1)], (uint32_t)w[2 * (i & 1) + 1]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      decltype(bget(0, 0)) b[T];
-#pragma unroll
-      for (int t = 0; t < T; ++t) b[t] = bget(t, i);
-#pragma unroll
-      for (int j = 0; j < NMT; ++j) {
-        if constexpr (BF == kB_BF16) {
-          const v8bf av = __builtin_bit_cast(v8bf, a[j].q[i]);
-#pragma unroll
-          for (int t = 0; t < T; ++t) acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b[t], acc[j][t], 0, 0, 0);
-        } else {
-          const v4i& w = a[j].q[i >> 1];
-          const v8h av = e4m3x8_to_f16((uint32_t)w[2 * (i & 1)], (uint32_t)w[2 * (i & 1) + 1]);
-#pragma unroll
-          for (int t = 0; t < T; ++t) acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, b[t], acc[j][t], 0, 0, 0);
-        }
+        for (int t = 0; t < T; ++t) acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, b[t], acc[j][t], 0, 0, 0);
       }
     }
   }

@@ -2,7 +2,11 @@
 //
 // A is the requantized h (E4M3 codes, FP8 and NVFP4 modes) or bf16(h) (BF16
 // mode, a layer kept at higher precision: "OCRia 推理栈：单卡 B200 提速近 10 倍",
-// section "Reducing the data moved: workload-aware quantization").
+// section "Reducing the data moved: workload-aware quantization").  E4M3 and
+// NVFP4 operands are converted exactly to fp16 in registers and summed by the
+// f16 matrix cores in fp32: the E4M3 matrix-core forms sum their products
+// with an error up to about 2^-15 of the sum of their magnitudes, which the
+// exact-integer case of the pages' definition does not allow.
 //
 // One workgroup owns MT m-tiles x T output tiles over the whole input range;
 // its NW waves take the 128-input chunks round-robin (every load of a wave is
@@ -19,7 +23,7 @@ namespace {
 
 template <int BF>
 __device__ __forceinline__ float col_scale(const DownArgs& d, int j) {
-  if constexpr (BF == kB_FP8) return d.wscales[j];
+  if constexpr (BF == kB_FP8_F16) return d.wscales[j];
   else if constexpr (BF == kB_FP4_F16) return d.tscale[0];
   else return 1.0f;
 }
@@ -97,22 +101,18 @@ hipError_t go_d(const DownArgs& d, int grid, hipStream_t st) {
 
 // Eight waves (two per SIMD) unless one chunk's operands need more than 64
 // registers, then four; the prefetch depth is what fits in about 160 (eight
-// waves; 128 when the weights are converted in registers) or 320 (four waves)
-// registers, at most 3, preferring a depth that divides the per-wave chunk
-// count (no zero-weight padding iterations).  E4M3 x E4M3 takes one chunk in
-// flight: its operands are used as loaded, and with 36 loads of 1 KB in
-// flight per wave (depth 3) the 208-row down projection took 11.0 us against
-// 10.6 us (loads that many CUs share arrive more slowly the more of them
-// are queued).  A workgroup of one 16 x 16 E4M3 tile (few rows: 128
-// workgroups for 2048 outputs) runs sixteen waves with every chunk in flight
-// at once (decode down projection 5.1 -> 4.9 us).
+// waves; 128 when the operands are converted to fp16 in registers) or 320
+// (four waves) registers, at most 3, preferring a depth that divides the
+// per-wave chunk count (no zero-weight padding iterations).  A workgroup of
+// one 16 x 16 E4M3 tile (few rows: 128 workgroups for 2048 outputs) runs
+// sixteen waves with every chunk in flight at once.
 template <int BF, int MT, int T>
 hipError_t go(const DownArgs& d, int grid, hipStream_t st) {
   constexpr int CV = chunk_vgprs<BF, MT, T>();
-  constexpr bool ONE = BF == kB_FP8 && MT * T == 1;
+  constexpr bool ONE = BF == kB_FP8_F16 && MT * T == 1;
   constexpr int NW = CV > 64 ? 4 : (ONE ? 16 : 8);
-  constexpr int BUDGET = NW == 4 ? 320 : (BF == kB_FP4_F16 ? 128 : 160);
-  constexpr int DMAX = ONE ? 3 : (BF == kB_FP8 ? 1 : (BUDGET / CV >= 3 ? 3 : (BUDGET / CV >= 2 ? 2 : 1)));
+  constexpr int BUDGET = NW == 4 ? 320 : (BF == kB_BF16 ? 160 : 128);
+  constexpr int DMAX = ONE ? 3 : (BUDGET / CV >= 3 ? 3 : (BUDGET / CV >= 2 ? 2 : 1));
   const int nk = (d.I / kChunk + NW - 1) / NW;
   if constexpr (DMAX >= 3) {
     if (nk % 3 == 0 || nk % 2 != 0) return go_d<BF, MT, T, NW, 3>(d, grid, st);
@@ -148,7 +148,7 @@ hipError_t go_mt(const DownArgs& d, int MT, int T, int grid, hipStream_t st) {
 hipError_t launch_down(const Plan& p, const DownArgs& d, hipStream_t st) {
   if (p.lg2) return launch_down_large(p, d, st);
   const int grid = p.n_mb2 * p.ngroups2;
-  if (p.prec == kFP8) return go_mt<kB_FP8>(d, p.MT2, p.T2, grid, st);
+  if (p.prec == kFP8) return go_mt<kB_FP8_F16>(d, p.MT2, p.T2, grid, st);
   if (p.prec == kFP8DownBF16) return go_mt<kB_BF16>(d, p.MT2, p.T2, grid, st);
   return go_mt<kB_FP4_F16>(d, p.MT2, p.T2, grid, st);
 }

@@ -244,7 +244,6 @@ __device__ __forceinline__ v8i cat(v4i lo, v4i hi) {
 // Weight tiles are 16 output rows; a chunk is 128 inputs.  Per format: bytes of
 // one tile-chunk in the blob, and the matrix-core instruction used.
 enum BFmt {
-  kB_FP8 = 0,       // E4M3 codes, MFMA 16x16x128 f8f6f4 (one per chunk)
   kB_FP8_F16 = 1,   // E4M3 codes converted to fp16, MFMA 16x16x32 f16 (four per chunk)
   kB_BF16 = 2,      // bf16, MFMA 16x16x32 bf16 (four per chunk)
   kB_FP4_F16 = 3    // NVFP4 codes x block scale converted to fp16, MFMA 16x16x32 f16
@@ -253,7 +252,6 @@ enum BFmt {
 template <int BF> struct Fmt;
 // kA16: the activation operand is bf16 (BF16 down projection) rather than
 // E4M3 codes (converted to fp16 in registers for the f16 formats).
-template <> struct Fmt<kB_FP8> { static constexpr int kGlobal = 2048, kUnits = 2, kLds = 2048; static constexpr bool kA16 = false; };
 template <> struct Fmt<kB_FP8_F16> { static constexpr int kGlobal = 2048, kUnits = 2, kLds = 4096; static constexpr bool kA16 = false; };
 template <> struct Fmt<kB_BF16> { static constexpr int kGlobal = 4096, kUnits = 4, kLds = 4096; static constexpr bool kA16 = true; };
 template <> struct Fmt<kB_FP4_F16> { static constexpr int kGlobal = 1024, kUnits = 1, kLds = 4096; static constexpr bool kA16 = false; };

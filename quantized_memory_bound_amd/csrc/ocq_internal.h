@@ -39,4 +39,9 @@ struct FwdArgs {
 // enqueue the kernels of one forward call (kernels.hip); returns 0 or a hipError_t value
 int launch_forward(const Plan& p, const FwdArgs& a);
 
+// measurement kernels (diag.hip); return 0 or a hipError_t value
+int diag_stream_read(const void* src, size_t bytes, void* out, int nblocks, void* stream);
+int diag_empty(void* stream);
+int diag_mfma_dot(int form, const uint8_t* a, const uint8_t* b, int M, int N, int K, float* c, void* stream);
+
 }  // namespace ocq

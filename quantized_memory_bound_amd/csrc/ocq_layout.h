@@ -152,7 +152,6 @@ inline void pick_down(Plan& p) {
   const int mtiles = (p.M + 15) / 16, ntiles = p.hidden / 16;
   const double ea = p.prec == kFP8DownBF16 ? 2.0 : 1.0;
   const double eb = p.prec == kFP8DownBF16 ? 2.0 : (p.prec == kFP4 ? 0.5 + 1.0 / 16 : 1.0);
-  const double mfma_rate = p.prec == kFP8 ? 2.0 : 1.0;   // fp8 matrix cores at twice the 16-bit rate
   double best = 1e30;
   for (int mt : {1, 2, 4}) {
     for (int t : {1, 2, 4}) {
@@ -161,7 +160,7 @@ inline void pick_down(Plan& p) {
       const double wgs = (double)nmb * ng;
       const double waves = wgs <= 256 ? 1.0 : (double)((nmb * ng + 255) / 256);
       const double l1 = (double)p.inter * 16.0 * (mt * ea + t * eb);           // bytes per workgroup
-      const double mm = (double)p.inter * 16.0 * 16.0 * mt * t / mfma_rate;   // 16-bit MACs per workgroup
+      const double mm = (double)p.inter * 16.0 * 16.0 * mt * t;   // 16-bit MACs per workgroup
       // per CU: ~150 GB/s through L1; ~4 TMAC/s of 16-bit matrix work (us)
       double cost = waves * (l1 / 150e3 + mm / 4e6);
       if (wgs < 128) cost *= 128.0 / wgs;                                    // too few CUs streaming

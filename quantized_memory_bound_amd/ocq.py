@@ -27,7 +27,8 @@ ERR_BAD_BLOB = -5
 EXPORTS = ("ocq_version", "ocq_packed_bytes", "ocq_pack_weights_host", "ocq_pack_weights",
            "ocq_unpack_weights_host", "ocq_workspace_bytes", "ocq_mlp_forward", "ocq_check_blob",
            "ocq_set_stage_events", "ocq_last_error", "ocq_stack_workspace_bytes", "ocq_mlp_stack_forward",
-           "ocq_calibrate_smoothing_host", "ocq_pack_weights_smoothed_host", "ocq_pack_weights_smoothed")
+           "ocq_calibrate_smoothing_host", "ocq_pack_weights_smoothed_host", "ocq_pack_weights_smoothed",
+           "ocq_diag_stream_read", "ocq_diag_empty", "ocq_diag_mfma_dot")
 
 
 class OcqError(RuntimeError):
@@ -77,6 +78,9 @@ def lib():
     L.ocq_stack_workspace_bytes.argtypes, L.ocq_stack_workspace_bytes.restype = [i, i, i, ip, i], sz
     L.ocq_mlp_stack_forward.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(sz), ip, i, vp, i, i, i, vp, vp, sz, vp]
     L.ocq_mlp_stack_forward.restype = i
+    L.ocq_diag_stream_read.argtypes, L.ocq_diag_stream_read.restype = [vp, sz, vp, i, vp], i
+    L.ocq_diag_empty.argtypes, L.ocq_diag_empty.restype = [vp], i
+    L.ocq_diag_mfma_dot.argtypes, L.ocq_diag_mfma_dot.restype = [i, vp, vp, i, i, i, vp, vp], i
     _lib = L
     return L
 
@@ -194,20 +198,61 @@ def check_blob(blob, hidden, inter, prec_mode, stream=None):
     _check(lib().ocq_check_blob(blob.data_ptr(), blob.numel(), hidden, inter, prec_mode, _stream_handle(stream)))
 
 
+def _need(t, name, dtype, device, shape=None, min_numel=None):
+    """Raise OcqError(ERR_INVALID_ARG) unless t is a contiguous tensor of this
+    dtype on this device (and shape / size): the C ABI takes raw pointers and
+    would read or write past a tensor of another layout."""
+    if t is None or not hasattr(t, "data_ptr"):
+        raise OcqError(ERR_INVALID_ARG, "%s must be a tensor" % name)
+    if t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise OcqError(ERR_INVALID_ARG, "%s has dtype %s" % (name, t.dtype))
+    if t.device != device:
+        raise OcqError(ERR_INVALID_ARG, "%s is on %s, not %s" % (name, t.device, device))
+    if not t.is_contiguous():
+        raise OcqError(ERR_INVALID_ARG, "%s must be contiguous" % name)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise OcqError(ERR_INVALID_ARG, "%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if min_numel is not None and t.numel() < min_numel:
+        raise OcqError(ERR_BUFFER_TOO_SMALL, "%s holds %d elements, needs %d" % (name, t.numel(), min_numel))
+
+
+def _check_x(x, hidden):
+    import torch
+    if not hasattr(x, "is_cuda") or not x.is_cuda:
+        raise OcqError(ERR_INVALID_ARG, "x must be a CUDA tensor")
+    if x.dim() != 2 or x.shape[1] != hidden:
+        raise OcqError(ERR_INVALID_ARG, "x must be [M, hidden=%d], got %s" % (hidden, tuple(x.shape)))
+    _need(x, "x", torch.bfloat16, x.device)
+
+
 def mlp_forward(blob, x, hidden, inter, prec_mode, y=None, workspace=None, taps=None, stream=None):
     """y = block(x) for x a bf16 [M, hidden] CUDA tensor; returns y (bf16 [M, hidden]).
 
-    taps: optional dict with any of x_codes, x_scales, h_out, h_scales tensors.
+    taps: optional dict with any of x_codes (uint8 [M, hidden]), x_scales
+    (float32 [M]), h_out (uint8 [M, inter]; int16 / uint16 bf16 bits in the
+    BF16-down mode) and h_scales (float32 [M]) tensors.  Every tensor must be
+    contiguous and on x's device; otherwise OcqError is raised before the call.
     """
     import torch
-    M = x.shape[0]
+    _check_x(x, hidden)
+    M, dev = x.shape[0], x.device
+    _need(blob, "blob", torch.uint8, dev, min_numel=packed_bytes(hidden, inter, prec_mode))
     if y is None:
-        y = torch.empty((M, hidden), dtype=torch.bfloat16, device=x.device)
+        y = torch.empty((M, hidden), dtype=torch.bfloat16, device=dev)
+    _need(y, "y", torch.bfloat16, dev, shape=(M, hidden))
     if workspace is None:
         workspace = torch.empty(max(1, workspace_bytes(M, hidden, inter, prec_mode)), dtype=torch.uint8,
-                                device=x.device)
+                                device=dev)
+    _need(workspace, "workspace", torch.uint8, dev)
     t = None
     if taps:
+        spec = {"x_codes": (torch.uint8, (M, hidden)), "x_scales": (torch.float32, (M,)),
+                "h_out": ((torch.int16, torch.uint16) if prec_mode == PREC_FP8_DOWN_BF16 else torch.uint8,
+                          (M, inter)),
+                "h_scales": (torch.float32, (M,))}
+        for k, (dt, shp) in spec.items():
+            if taps.get(k) is not None:
+                _need(taps[k], "taps[%s]" % k, dt, dev, shape=shp)
         t = Taps(*(taps[k].data_ptr() if taps.get(k) is not None else None
                    for k in ("x_codes", "x_scales", "h_out", "h_scales")))
     _check(lib().ocq_mlp_forward(blob.data_ptr(), blob.numel(), x.data_ptr(), M, hidden, inter, prec_mode,
@@ -230,12 +275,17 @@ def mlp_stack_forward(blobs, prec_modes, x, hidden, inter, y=None, workspace=Non
     import torch
     if len(blobs) != len(prec_modes):
         raise ValueError("one prec_mode per blob")
-    M = x.shape[0]
+    _check_x(x, hidden)
+    M, dev = x.shape[0], x.device
+    for l, (b, m) in enumerate(zip(blobs, prec_modes)):
+        _need(b, "blobs[%d]" % l, torch.uint8, dev, min_numel=packed_bytes(hidden, inter, m))
     if y is None:
-        y = torch.empty((M, hidden), dtype=torch.bfloat16, device=x.device)
+        y = torch.empty((M, hidden), dtype=torch.bfloat16, device=dev)
+    _need(y, "y", torch.bfloat16, dev, shape=(M, hidden))
     if workspace is None:
         workspace = torch.empty(max(1, stack_workspace_bytes(M, hidden, inter, prec_modes)), dtype=torch.uint8,
-                                device=x.device)
+                                device=dev)
+    _need(workspace, "workspace", torch.uint8, dev)
     n = len(blobs)
     ptrs = (ctypes.c_void_p * n)(*[b.data_ptr() for b in blobs])
     sizes = (ctypes.c_size_t * n)(*[b.numel() for b in blobs])
@@ -265,3 +315,34 @@ class QuantizedMLP:
     def __call__(self, x, y=None, taps=None, stream=None):
         return mlp_forward(self.blob, x, self.hidden, self.inter, self.prec_mode, y=y,
                            workspace=self.workspace(x.shape[0]), taps=taps, stream=stream)
+
+
+# ---------------------------------------------------------------- measurement helpers
+
+def diag_stream_read(src, out, blocks, stream=None):
+    """Read the whole uint8 CUDA tensor src with the library's streaming-read
+    kernel (out: int32 / uint8 CUDA tensor of >= 4 * blocks bytes)."""
+    import torch
+    _need(src, "src", torch.uint8, src.device)
+    if out.numel() * out.element_size() < 4 * blocks:
+        raise OcqError(ERR_BUFFER_TOO_SMALL, "out holds fewer than 4 * blocks bytes")
+    _check(lib().ocq_diag_stream_read(src.data_ptr(), src.numel(), out.data_ptr(), blocks, _stream_handle(stream)))
+
+
+def diag_empty(stream=None):
+    _check(lib().ocq_diag_empty(_stream_handle(stream)))
+
+
+def diag_mfma_dot(form, a_codes, b_codes, stream=None):
+    """c = dec(a) dec(b)^T (float32 [M, N]) over E4M3 code tensors a [M, K],
+    b [N, K] (uint8, CUDA) through matrix-core form 0 (f16), 1 (f8f6f4 K=128)
+    or 2 (fp8 K=32)."""
+    import torch
+    M, K = a_codes.shape
+    N = b_codes.shape[0]
+    _need(a_codes, "a", torch.uint8, a_codes.device)
+    _need(b_codes, "b", torch.uint8, a_codes.device, shape=(N, K))
+    c = torch.empty((M, N), dtype=torch.float32, device=a_codes.device)
+    _check(lib().ocq_diag_mfma_dot(form, a_codes.data_ptr(), b_codes.data_ptr(), M, N, K, c.data_ptr(),
+                                   _stream_handle(stream)))
+    return c

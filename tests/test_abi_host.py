@@ -226,3 +226,12 @@ def test_smoothing_argument_errors():
     bad[7] = np.inf
     assert L.ocq_pack_weights_smoothed_host(w.ctypes.data, w.ctypes.data, w.T.copy().ctypes.data, bad.ctypes.data,
                                             256, 512, 0, out.ctypes.data, out.nbytes) == ocq.ERR_INVALID_ARG
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    d = I.make_inputs(256, 512, 4, seed=2)
+    x = torch.from_numpy(d["x_bits"].view(np.int16)).view(torch.bfloat16)
+    with pytest.raises(ocq.OcqError) as e:
+        ocq.mlp_forward(torch.zeros(10, dtype=torch.uint8), x, 256, 512, 0)
+    assert e.value.status == ocq.ERR_INVALID_ARG

@@ -165,6 +165,24 @@ ocq_status ocq_mlp_forward(const void* packed_dev, size_t packed_bytes, const vo
                            void* workspace_dev, size_t workspace_bytes, const ocq_taps* taps,
                            void* stream);
 
+/* The same forward call for callers that cannot allocate device memory
+ * (code under HIP graph capture that may not call hipMalloc, tight serving
+ * loops, hosts that forbid allocation): no workspace argument.  The
+ * workspace is a fixed array of ocq_noalloc_scratch_bytes() bytes (32 MiB)
+ * in device memory that the library holds on each device it runs on until
+ * the process ends; the entry point itself allocates nothing.
+ * Arguments, results and errors are those of ocq_mlp_forward, plus
+ * OCQ_ERR_BUFFER_TOO_SMALL (before any launch) when
+ * ocq_workspace_bytes(M, hidden, inter, prec_mode) exceeds the array.
+ * Every call on one device shares that device's array: calls that overlap
+ * on one device (different streams, or different threads without ordering)
+ * race and give wrong results; calls ordered on one stream are safe.  The
+ * array keeps the last call's contents; no call depends on them. */
+size_t ocq_noalloc_scratch_bytes(void);
+ocq_status ocq_mlp_forward_noalloc(const void* packed_dev, size_t packed_bytes, const void* x_bf16_dev, int M,
+                                   int hidden, int inter, int prec_mode, void* y_bf16_dev, const ocq_taps* taps,
+                                   void* stream);
+
 /* A stack of L MLP blocks with a precision mode per layer (the pages'
  * mixed-precision scheme at model scale: each layer's weights in the
  * precision chosen for it, BF16 kept for sensitive layers; "OCRia 推理栈：单卡

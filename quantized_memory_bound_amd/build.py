@@ -18,7 +18,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libocq.so")
 
-SOURCES = ["api.cpp", "pack.cpp", "kernels.hip", "gemm_gateup.hip", "gemm_down.hip", "gemm_large.hip", "diag.hip"]
+SOURCES = ["api.cpp", "pack.cpp", "kernels.hip", "gemm_gateup.hip", "gemm_down.hip", "gemm_large.hip", "diag.hip",
+           "noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

@@ -28,7 +28,8 @@ EXPORTS = ("ocq_version", "ocq_packed_bytes", "ocq_pack_weights_host", "ocq_pack
            "ocq_unpack_weights_host", "ocq_workspace_bytes", "ocq_mlp_forward", "ocq_check_blob",
            "ocq_set_stage_events", "ocq_last_error", "ocq_stack_workspace_bytes", "ocq_mlp_stack_forward",
            "ocq_calibrate_smoothing_host", "ocq_pack_weights_smoothed_host", "ocq_pack_weights_smoothed",
-           "ocq_diag_stream_read", "ocq_diag_empty", "ocq_diag_mfma_dot")
+           "ocq_diag_stream_read", "ocq_diag_empty", "ocq_diag_mfma_dot", "ocq_noalloc_scratch_bytes",
+           "ocq_mlp_forward_noalloc")
 
 
 class OcqError(RuntimeError):
@@ -78,6 +79,9 @@ def lib():
     L.ocq_stack_workspace_bytes.argtypes, L.ocq_stack_workspace_bytes.restype = [i, i, i, ip, i], sz
     L.ocq_mlp_stack_forward.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(sz), ip, i, vp, i, i, i, vp, vp, sz, vp]
     L.ocq_mlp_stack_forward.restype = i
+    L.ocq_noalloc_scratch_bytes.argtypes, L.ocq_noalloc_scratch_bytes.restype = [], sz
+    L.ocq_mlp_forward_noalloc.argtypes = [vp, sz, vp, i, i, i, i, vp, ctypes.POINTER(Taps), vp]
+    L.ocq_mlp_forward_noalloc.restype = i
     L.ocq_diag_stream_read.argtypes, L.ocq_diag_stream_read.restype = [vp, sz, vp, i, vp], i
     L.ocq_diag_empty.argtypes, L.ocq_diag_empty.restype = [vp], i
     L.ocq_diag_mfma_dot.argtypes, L.ocq_diag_mfma_dot.restype = [i, vp, vp, i, i, i, vp, vp], i
@@ -225,6 +229,21 @@ def _check_x(x, hidden):
     _need(x, "x", torch.bfloat16, x.device)
 
 
+def _taps_struct(taps, M, hidden, inter, prec_mode, dev):
+    """Checked Taps structure (or None) from a dict of optional tensors."""
+    import torch
+    if not taps:
+        return None
+    spec = {"x_codes": (torch.uint8, (M, hidden)), "x_scales": (torch.float32, (M,)),
+            "h_out": ((torch.int16, torch.uint16) if prec_mode == PREC_FP8_DOWN_BF16 else torch.uint8, (M, inter)),
+            "h_scales": (torch.float32, (M,))}
+    for k, (dt, shp) in spec.items():
+        if taps.get(k) is not None:
+            _need(taps[k], "taps[%s]" % k, dt, dev, shape=shp)
+    return Taps(*(taps[k].data_ptr() if taps.get(k) is not None else None
+                  for k in ("x_codes", "x_scales", "h_out", "h_scales")))
+
+
 def mlp_forward(blob, x, hidden, inter, prec_mode, y=None, workspace=None, taps=None, stream=None):
     """y = block(x) for x a bf16 [M, hidden] CUDA tensor; returns y (bf16 [M, hidden]).
 
@@ -244,21 +263,33 @@ def mlp_forward(blob, x, hidden, inter, prec_mode, y=None, workspace=None, taps=
         workspace = torch.empty(max(1, workspace_bytes(M, hidden, inter, prec_mode)), dtype=torch.uint8,
                                 device=dev)
     _need(workspace, "workspace", torch.uint8, dev)
-    t = None
-    if taps:
-        spec = {"x_codes": (torch.uint8, (M, hidden)), "x_scales": (torch.float32, (M,)),
-                "h_out": ((torch.int16, torch.uint16) if prec_mode == PREC_FP8_DOWN_BF16 else torch.uint8,
-                          (M, inter)),
-                "h_scales": (torch.float32, (M,))}
-        for k, (dt, shp) in spec.items():
-            if taps.get(k) is not None:
-                _need(taps[k], "taps[%s]" % k, dt, dev, shape=shp)
-        t = Taps(*(taps[k].data_ptr() if taps.get(k) is not None else None
-                   for k in ("x_codes", "x_scales", "h_out", "h_scales")))
+    t = _taps_struct(taps, M, hidden, inter, prec_mode, dev)
     _check(lib().ocq_mlp_forward(blob.data_ptr(), blob.numel(), x.data_ptr(), M, hidden, inter, prec_mode,
                                  y.data_ptr(), workspace.data_ptr(), workspace.numel(),
                                  ctypes.byref(t) if t is not None else None, _stream_handle(stream)))
     return y
+
+
+def mlp_forward_noalloc(blob, x, hidden, inter, prec_mode, y=None, taps=None, stream=None):
+    """As mlp_forward, through the entry point that allocates nothing (its
+    workspace is the library's fixed per-device scratch array).  y (bf16
+    [M, hidden]) must be given by callers that cannot allocate either."""
+    import torch
+    _check_x(x, hidden)
+    M, dev = x.shape[0], x.device
+    _need(blob, "blob", torch.uint8, dev, min_numel=packed_bytes(hidden, inter, prec_mode))
+    if y is None:
+        y = torch.empty((M, hidden), dtype=torch.bfloat16, device=dev)
+    _need(y, "y", torch.bfloat16, dev, shape=(M, hidden))
+    t = _taps_struct(taps, M, hidden, inter, prec_mode, dev)
+    _check(lib().ocq_mlp_forward_noalloc(blob.data_ptr(), blob.numel(), x.data_ptr(), M, hidden, inter, prec_mode,
+                                         y.data_ptr(), ctypes.byref(t) if t is not None else None,
+                                         _stream_handle(stream)))
+    return y
+
+
+def noalloc_scratch_bytes():
+    return lib().ocq_noalloc_scratch_bytes()
 
 
 def _int_array(vals):

@@ -235,3 +235,17 @@ def test_binding_rejects_host_tensors():
     with pytest.raises(ocq.OcqError) as e:
         ocq.mlp_forward(torch.zeros(10, dtype=torch.uint8), x, 256, 512, 0)
     assert e.value.status == ocq.ERR_INVALID_ARG
+
+
+def test_noalloc_argument_errors():
+    # checked before any device call: an invalid shape or M is reported as by
+    # ocq_mlp_forward, a call larger than the scratch array as too small
+    L = ocq.lib()
+    assert L.ocq_noalloc_scratch_bytes() == 32 << 20
+    assert L.ocq_mlp_forward_noalloc(0x10000, 1 << 30, 0x20000, 4, 2000, 512, 0, 0x30000, None, None) \
+        == ocq.ERR_UNSUPPORTED
+    assert L.ocq_mlp_forward_noalloc(0x10000, 1 << 30, 0x20000, 0, 256, 512, 0, 0x30000, None, None) \
+        == ocq.ERR_INVALID_ARG
+    assert L.ocq_mlp_forward_noalloc(0x10000, 1 << 30, 0x20000, 8192, 4096, 12288, 1, 0x30000, None, None) \
+        == ocq.ERR_BUFFER_TOO_SMALL
+    assert "no-allocation" in ocq.last_error()

@@ -239,6 +239,8 @@ def main():
     ap.add_argument("--no-stage-events", action="store_true", help="skip the gate/up kernel timing pass")
     ap.add_argument("--mode", choices=["graph", "eager"], default="graph",
                     help="graph: replay a captured HIP graph of R steps; eager: one call per step")
+    ap.add_argument("--fused-requant", type=int, choices=[0, 1], default=0,
+                    help="1: requantize h inside the gate/up kernel where its grid fits the GPU at once")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 256 MiB copy kernel (counter calibration for rocprofv3 --pmc)")
     args = ap.parse_args()
@@ -254,6 +256,7 @@ def main():
     from quantized_memory_bound_amd import inputs as I
     from quantized_memory_bound_amd import ocq
 
+    ocq.set_fused_requant(bool(args.fused_requant))
     if args.workload in I.STACKS:
         return run_stack(args)
     cfg = I.WORKLOADS[args.workload]
@@ -378,7 +381,8 @@ def main():
         "dtype": "e4m3" if prec == 0 else prec_name,
         "data": "synthetic (seeded; shapes and distributions of the workload)",
         "config": {"workload": args.workload, "hidden": H, "inter": Iw, "M": M, "prec_mode": prec_name,
-                   "weight_copies_rotated": R, "alg_bytes_per_block": ab},
+                   "weight_copies_rotated": R, "alg_bytes_per_block": ab,
+                   "requant": "inside gate/up" if args.fused_requant else "separate kernel"},
         "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
         "tokens_per_s": round(tok_s, 1),
         "us_per_block": round(ms_step * 1e3, 3),

@@ -257,6 +257,20 @@ ocq_status ocq_diag_empty(void* stream);
 ocq_status ocq_diag_mfma_dot(int form, const void* a_dev, const void* b_dev, int M, int N, int K, float* c_dev,
                              void* stream);
 
+/* Where the per-token requantization of h runs (process-wide; default 0).
+ * 1: inside the gate/up kernel whenever its whole grid can be resident at
+ * once (an occupancy check on the host before each launch): h stays in
+ * registers, the row maxima meet through device-scope atomics and the
+ * workgroups wait once for each other, bounded by 0.1 s (German page "Wie es
+ * funktioniert" of the post: SiLU fused with the quantization, the
+ * intermediate kept on chip).  Such a call must not share the GPU with
+ * kernels that keep its workgroups from becoming resident for that long; if
+ * the wait times out the call's y is NaN.  0: the two-pass form (fp32 h to
+ * the workspace, then a requantization kernel), which is faster on MI355X:
+ * each device-scope round trip the exchange needs costs more than a kernel
+ * launch.  Both give bit-identical results. */
+ocq_status ocq_set_fused_requant(int enable);
+
 /* Message for the last failure on this thread ("" if none). */
 const char* ocq_last_error(void);
 

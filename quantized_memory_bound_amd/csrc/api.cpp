@@ -56,6 +56,12 @@ ocq_status ocq_set_stage_events(void* const* events, int count) {
   return OCQ_OK;
 }
 
+ocq_status ocq_set_fused_requant(int enable) {
+  g_err.clear();
+  set_fused_requant(enable != 0);
+  return OCQ_OK;
+}
+
 size_t ocq_packed_bytes(int hidden, int inter, int prec_mode) {
   if (prec_mode < 0 || prec_mode > 2 || !shape_ok(hidden, inter)) return 0;
   return blob_layout(hidden, inter, prec_mode).total;

@@ -321,28 +321,47 @@ __device__ __forceinline__ void ks_mainloop_roll(const LanePtrs& p, int kidx, in
 // then stores two adjacent rows of the tile's 8 columns: 64 contiguous bytes
 // of the [tile][row][8] h32 block.  amax[e] accumulates |h| of value e.
 // SKIP_PAD: rows >= M (padding, never read back) store no h32.
-template <bool BF16H, int T, bool SKIP_PAD = false>
-__device__ __forceinline__ void gateup_tile_epilogue(const GateUpArgs& g, const v4f v, const v4f xs,
-                                                     float cg, float cu, int m_base, int ng, int t,
-                                                     float (&amax)[2]) {
-  const int lane = threadIdx.x & 63, gq = lane >> 4, r = lane & 15;
-  const bool lo = r < 8;
-  const int c = r & 7, n = (ng * T + t) * 8 + c;
+// h = SiLU(G) U of the lane's two values (value e: row 4 gq + 2 e of the
+// m-tile for gate lanes, 4 gq + 2 e + 1 for up lanes; column r % 8 of the
+// tile), from the accumulated tile v, the lane's row scales xs and the
+// column's gate / up scales.  BF16H: the exact-division SiLU (h becomes bf16).
+template <bool BF16H>
+__device__ __forceinline__ void gateup_tile_h(const v4f v, const v4f xs, float cg, float cu, float (&hv)[2]) {
+  const bool lo = (threadIdx.x & 15) < 8;
   // gate lanes send G of rows 1, 3 and receive U of rows 0, 2
   const float p0 = dpp<0x128>(lo ? v[1] : v[0]);
   const float p1 = dpp<0x128>(lo ? v[3] : v[2]);
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
-    // row 2e (gate lanes) or 2e + 1 (up lanes): selects, not a lane-dependent
-    // array index, which would put xs and v in scratch memory
-    const int i = 2 * e + (lo ? 0 : 1);
+    // selects, not a lane-dependent array index, which would put xs and v in
+    // scratch memory
     const float vi = lo ? v[2 * e] : v[2 * e + 1];
     const float xi = lo ? xs[2 * e] : xs[2 * e + 1];
     const float gv = lo ? vi : (e ? p1 : p0);
     const float uv = lo ? (e ? p1 : p0) : vi;
     const float ga = gv * xi * cg;
-    const float hv = (BF16H ? silu(ga) : silu_rcp(ga)) * (uv * xi * cu);
-    const int m = m_base + 4 * gq + i;
+    hv[e] = (BF16H ? silu(ga) : silu_rcp(ga)) * (uv * xi * cu);
+  }
+}
+
+// row (within the m-tile) of the lane's value e in gateup_tile_h
+__device__ __forceinline__ int gateup_value_row(int e) {
+  const int lane = threadIdx.x & 63;
+  return 4 * (lane >> 4) + 2 * e + ((lane & 8) ? 1 : 0);
+}
+
+template <bool BF16H, int T, bool SKIP_PAD = false>
+__device__ __forceinline__ void gateup_tile_epilogue(const GateUpArgs& g, const v4f v, const v4f xs,
+                                                     float cg, float cu, int m_base, int ng, int t,
+                                                     float (&amax)[2]) {
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 7, n = (ng * T + t) * 8 + c;
+  float h[2];
+  gateup_tile_h<BF16H>(v, xs, cg, cu, h);
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const float hv = h[e];
+    const int m = m_base + gateup_value_row(e);
     if constexpr (BF16H) {
       const uint16_t hb = (uint16_t)bf16_bits(hv);
       g.hb[frag_off16(m, n, g.I / 128)] = hb;
@@ -350,6 +369,106 @@ __device__ __forceinline__ void gateup_tile_epilogue(const GateUpArgs& g, const 
     } else {
       if (!SKIP_PAD || m < g.M) g.h32[((size_t)(ng * T + t) * g.Mpad + m) * 8 + c] = hv;
       amax[e] = fmaxf(amax[e], fabsf(hv));
+    }
+  }
+}
+
+// ---------------------------------------------------------------- per-token requantization inside gate/up
+//
+// The row scale sh = max_n |h| / 448 spans the columns of every gate/up
+// workgroup.  When the whole grid is resident at once (checked on the host
+// before such a launch), each workgroup folds its row maxima into amax_g with
+// device-scope atomic maxima, arrives at a device-scope counter and waits for
+// every workgroup to arrive; it then reads the finished maxima and quantizes
+// the h values it has kept in registers, so h never goes to memory (the
+// German page "Wie es funktioniert": SiLU and quantization fused, the
+// intermediate kept on chip).  Device-scope atomics and loads are coherent
+// across the XCDs' L2 caches, so no cache write-back or invalidation is
+// needed: a wave's atomics are complete once it has waited for its vector
+// memory counter, which every wave does before its workgroup arrives.  The
+// wait is bounded (kGridWaitTicks of the 100 MHz clock): if the grid is not
+// all resident (the GPU shared with other work) the waiting workgroups set
+// sync[1] and go on, and the down projection then writes NaN for y.
+
+constexpr uint64_t kGridWaitTicks = 10000000;   // 0.1 s
+
+// Returns the value the atomic replaced: the returning form of the atomic,
+// whose result arrives only once the maximum has been performed.  Callers
+// OR the results together and hand them to grid_arrive_and_wait, which waits
+// for them before the workgroup arrives.
+__device__ __forceinline__ uint32_t amax_atomic(uint32_t* amax_g, int m, float a) {
+  // |h| >= +0: the float order is the unsigned order of the bits
+  return __hip_atomic_fetch_max(amax_g + m, __float_as_uint(a), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float amax_load(const uint32_t* amax_g, int m) {
+  return __uint_as_float(__hip_atomic_load(amax_g + m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
+// Every wave of the workgroup calls this (two workgroup barriers inside);
+// seen: the OR of the wave's amax_atomic results (0 if it made none).
+__device__ __forceinline__ void grid_arrive_and_wait(uint32_t* sync, uint32_t nwg, uint32_t seen) {
+  asm volatile("" ::"v"(seen));   // the results have arrived: this wave's maxima are performed
+  wait_vm<0>();
+  lds_barrier();                  // ... and those of every wave of the workgroup
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    while (__hip_atomic_load(sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < nwg) {
+      __builtin_amdgcn_s_sleep(1);
+      if (__builtin_amdgcn_s_memrealtime() - t0 > kGridWaitTicks) {
+        __hip_atomic_store(sync + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+    }
+  }
+  lds_barrier();
+}
+
+// Row scale s = fl32(a / 448) of a row whose maximum |h| is a, and its
+// reciprocal (0 for a zero row)
+__device__ __forceinline__ void row_scale_of(float a, float& s, float& rcp) {
+  s = a / 448.0f;
+  rcp = s > 0.0f ? 1.0f / s : 0.0f;
+}
+
+// E4M3 code of the lane's value hv into the LDS stage [row][ncols] bytes of
+// the workgroup's block (rl: row within the block; col: column within the
+// block) with the row's scale s and its reciprocal (a zero row gets code 0)
+__device__ __forceinline__ void stage_code(uint8_t* stage, int ncols, int rl, int col, float hv, float s, float rcp) {
+  stage[rl * ncols + col] = (uint8_t)(s > 0.0f ? e4m3_quot1(hv, s, rcp) : 0u);
+}
+
+// Write-out of a fused requantization, by every thread of the workgroup
+// (nthreads): the staged codes of rows [row0, row0 + nrows) x columns
+// [n0, n0 + ncols) as 8-byte pieces in the down projection's fragment order
+// and to the plain tap; the row scales of those rows (scales: one workgroup
+// per m-block); and zero codes and scales for the rows [rows_end, Mpad) that
+// lie past every gate/up m-block but inside the down projection's
+// (last_mb: the workgroups of the last m-block, each for its own columns).
+__device__ __forceinline__ void fused_write_out(const GateUpArgs& g, const uint8_t* stage, int row0, int nrows,
+                                                int n0, int ncols, bool scales, bool last_mb, int rows_end,
+                                                int nthreads) {
+  const int C = g.I / kChunk, per_row = ncols / 8;
+  for (int p = threadIdx.x; p < nrows * per_row; p += nthreads) {
+    const int rl = p / per_row, t = p % per_row, m = row0 + rl, n = n0 + 8 * t;
+    const v2u w = *(const v2u*)(stage + rl * ncols + 8 * t);
+    *(v2u*)(g.hq + frag_off8(m, n, C)) = w;
+    if (g.tap_hq && m < g.M) *(v2u*)(g.tap_hq + (size_t)m * g.I + n) = w;
+  }
+  if (scales) {
+    for (int rl = threadIdx.x; rl < nrows; rl += nthreads) {
+      const int m = row0 + rl;
+      const float s = amax_load(g.amax_g, m) / 448.0f;
+      g.sh[m] = s;
+      if (g.tap_sh && m < g.M) g.tap_sh[m] = s;
+    }
+  }
+  if (last_mb) {
+    for (int p = threadIdx.x; p < (g.Mpad - rows_end) * per_row; p += nthreads) {
+      const int m = rows_end + p / per_row, n = n0 + 8 * (p % per_row);
+      *(v2u*)(g.hq + frag_off8(m, n, C)) = v2u{0u, 0u};
+      if (scales && p % per_row == 0) g.sh[m] = 0.0f;
     }
   }
 }

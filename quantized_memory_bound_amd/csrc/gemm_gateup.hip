@@ -62,9 +62,13 @@ __device__ __forceinline__ void gateup_block(const GateUpArgs& g, int ngroups, i
 
 // MT m-tiles per workgroup, MS x KS waves, MTW = ceil(MT / MS) m-tiles per wave
 // D > 0: prefetch depth of ks_mainloop; D = -1: ks_mainloop_roll with
-// padding chunks; D <= -2: ks_mainloop_roll with exactly -D chunks per wave
-template <int BF, int MT, int T, int MS, int KS, int D, bool BF16H>
+// padding chunks; D <= -2: ks_mainloop_roll with exactly -D chunks per wave.
+// FUSED: the per-token requantization of h happens here (grid-wide row
+// maxima, codes written by this kernel; see gemm_core.h), else fp32 h and
+// per-workgroup row maxima go to the workspace for k_requant.
+template <int BF, int MT, int T, int MS, int KS, int D, bool BF16H, bool FUSED>
 __global__ __launch_bounds__(64 * MS * KS) void ks_gateup(GateUpArgs g) {
+  static_assert(!(FUSED && BF16H), "the BF16-down mode has no requantization");
   constexpr int MTW = (MT + MS - 1) / MS;
   extern __shared__ v4f red4[];
   int mb, ng;
@@ -122,6 +126,8 @@ __global__ __launch_bounds__(64 * MS * KS) void ks_gateup(GateUpArgs g) {
 #pragma unroll
       for (int t = 0; t < T; ++t) red4[((wave * MT + j) * T + t) * 64 + lane] = acc[j][t];
     lds_barrier();
+    float hv[2] = {0.f, 0.f};   // FUSED: the lane's two h values of the wave's pair
+    uint32_t seen = 0u;
     if (wave < MT * T) {
       const int q = sq, t = st;
       v4f v = v4f{0.f, 0.f, 0.f, 0.f};
@@ -129,8 +135,14 @@ __global__ __launch_bounds__(64 * MS * KS) void ks_gateup(GateUpArgs g) {
       for (int ks = 0; ks < KS; ++ks) v += red4[((ks * MT + q) * T + t) * 64 + lane];
       const int n0 = ng * T + t;
       float am[2] = {0.f, 0.f};
-      // padding rows (>= M) are never read back: their h is not stored
-      gateup_tile_epilogue<BF16H, 1, true>(g, v, sxs, scg, scu, row0 + q * 16, n0, 0, am);
+      if constexpr (FUSED) {
+        gateup_tile_h<false>(v, sxs, scg, scu, hv);
+        am[0] = fabsf(hv[0]);
+        am[1] = fabsf(hv[1]);
+      } else {
+        // padding rows (>= M) are never read back: their h is not stored
+        gateup_tile_epilogue<BF16H, 1, true>(g, v, sxs, scg, scu, row0 + q * 16, n0, 0, am);
+      }
       if constexpr (!BF16H) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) am[e] = max8(am[e]);
@@ -148,8 +160,27 @@ __global__ __launch_bounds__(64 * MS * KS) void ks_gateup(GateUpArgs g) {
 #pragma unroll
         for (int t = 1; t < T; ++t) a = fmaxf(a, s_am[wave + t][lane]);
         const int m = row0 + sq * 16 + lane;
-        if (m < g.M) g.amax_part[(size_t)m * ((g.I / 8) / T) + ng] = a;
+        if (m < g.M) {
+          if constexpr (FUSED) seen = amax_atomic(g.amax_g, m, a);
+          else g.amax_part[(size_t)m * ((g.I / 8) / T) + ng] = a;
+        }
       }
+    }
+    if constexpr (FUSED) {
+      grid_arrive_and_wait(g.sync, gridDim.x, seen);
+      uint8_t* stage = (uint8_t*)red4;   // every partial tile was read before the barriers
+      constexpr int NC = T * 8;
+      if (wave < MT * T) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int rl = sq * 16 + gateup_value_row(e);
+          float sc, rcp;
+          row_scale_of(amax_load(g.amax_g, row0 + rl), sc, rcp);
+          stage_code(stage, NC, rl, st * 8 + (lane & 7), hv[e], sc, rcp);
+        }
+      }
+      lds_barrier();
+      fused_write_out(g, stage, row0, MT * 16, ng * NC, NC, ng == 0, mb == g.n_mb - 1, g.n_mb * MT * 16, 64 * NW);
     }
     return;
   }
@@ -163,6 +194,7 @@ __global__ __launch_bounds__(64 * MS * KS) void ks_gateup(GateUpArgs g) {
   float amax[Q][2];
 #pragma unroll
   for (int jq = 0; jq < Q; ++jq) amax[jq][0] = amax[jq][1] = 0.f;
+  float hvq[FUSED ? Q : 1][FUSED ? T : 1][2];   // FUSED: the wave's h values, kept for the requantization
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     // region t & 1 was last read for tile t - 2, before every wave passed the
@@ -179,10 +211,17 @@ __global__ __launch_bounds__(64 * MS * KS) void ks_gateup(GateUpArgs g) {
         v4f v = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) v += red[((qm + MS * ks) * MTW + qj) * 64 + lane];
-        gateup_tile_epilogue<BF16H, T>(g, v, es.xs[jq], es.cg[t], es.cu[t], row0 + q * 16, ng, t, amax[jq]);
+        if constexpr (FUSED) {
+          gateup_tile_h<false>(v, es.xs[jq], es.cg[t], es.cu[t], hvq[jq][t]);
+          amax[jq][0] = fmaxf(amax[jq][0], fabsf(hvq[jq][t][0]));
+          amax[jq][1] = fmaxf(amax[jq][1], fabsf(hvq[jq][t][1]));
+        } else {
+          gateup_tile_epilogue<BF16H, T>(g, v, es.xs[jq], es.cg[t], es.cu[t], row0 + q * 16, ng, t, amax[jq]);
+        }
       }
     }
   }
+  uint32_t seen = 0u;
   if constexpr (!BF16H) {
     const int ngroups = (g.I / 8) / T;
 #pragma unroll
@@ -194,10 +233,37 @@ __global__ __launch_bounds__(64 * MS * KS) void ks_gateup(GateUpArgs g) {
         if ((lane & 7) == 0) {      // lane 16 gq (rows 0, 2) and 16 gq + 8 (rows 1, 3)
           const int m = row0 + q * 16 + 4 * (lane >> 4) + ((lane & 8) ? 1 : 0);
 #pragma unroll
-          for (int e = 0; e < 2; ++e) g.amax_part[(size_t)(m + 2 * e) * ngroups + ng] = amax[jq][e];
+          for (int e = 0; e < 2; ++e) {
+            if constexpr (FUSED) {
+              if (m + 2 * e < g.M) seen |= amax_atomic(g.amax_g, m + 2 * e, amax[jq][e]);
+            } else {
+              g.amax_part[(size_t)(m + 2 * e) * ngroups + ng] = amax[jq][e];
+            }
+          }
         }
       }
     }
+  }
+  if constexpr (FUSED) {
+    grid_arrive_and_wait(g.sync, gridDim.x, seen);
+    uint8_t* stage = (uint8_t*)red4;   // the last tile's partials were read before the barriers
+    constexpr int NC = T * 8;
+#pragma unroll
+    for (int jq = 0; jq < Q; ++jq) {
+      const int q = wave + NW * jq;
+      if (q < MT) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int rl = q * 16 + gateup_value_row(e);
+          float sc, rcp;
+          row_scale_of(amax_load(g.amax_g, row0 + rl), sc, rcp);
+#pragma unroll
+          for (int t = 0; t < T; ++t) stage_code(stage, NC, rl, t * 8 + (lane & 7), hvq[jq][t][e], sc, rcp);
+        }
+      }
+    }
+    lds_barrier();
+    fused_write_out(g, stage, row0, MT * 16, ng * NC, NC, ng == 0, mb == g.n_mb - 1, g.n_mb * MT * 16, 64 * NW);
   }
 }
 
@@ -244,7 +310,7 @@ __device__ __forceinline__ int pc_f16_unit(int c, int t, int i) {
   return ((c / P::CPS) & 1) * P::SLOT + ((((c % P::CPS) * P::T) + t) * 4 + i) * 1024;
 }
 
-template <int BF, int T, int C, bool BF16H>
+template <int BF, int T, int C>
 __device__ __forceinline__ void pc_producer(const GateUpArgs& g, uint8_t* lds, int ng, int p) {
   using P = Pc<BF, T, C>;
   const int lane = threadIdx.x & 63;
@@ -308,7 +374,7 @@ __device__ __forceinline__ void pc_producer(const GateUpArgs& g, uint8_t* lds, i
   lds_barrier();   // partial tiles stored
 }
 
-template <int BF, int NV, int T, int C, bool BF16H>
+template <int BF, int NV, int T, int C, bool BF16H, bool FUSED>
 __device__ __forceinline__ void pc_consumer(const GateUpArgs& g, uint8_t* lds, int row0, int ng, int wave, int mt0) {
   using P = Pc<BF, T, C>;
   constexpr int MT = 13, Q = 2;
@@ -382,6 +448,7 @@ __device__ __forceinline__ void pc_consumer(const GateUpArgs& g, uint8_t* lds, i
   float amax[Q][2];
 #pragma unroll
   for (int jq = 0; jq < Q; ++jq) amax[jq][0] = amax[jq][1] = 0.f;
+  float hvq[FUSED ? Q : 1][FUSED ? T : 1][2];   // FUSED: the wave's h values, kept for the requantization
   v4f* red = (v4f*)lds;   // [wave][m-tile slot][tile][lane]
 #pragma unroll
   for (int j = 0; j < NV; ++j)
@@ -396,10 +463,17 @@ __device__ __forceinline__ void pc_consumer(const GateUpArgs& g, uint8_t* lds, i
 #pragma unroll
       for (int t = 0; t < T; ++t) {
         const v4f v = red[(((2 * msq) * 4 + jj) * T + t) * 64 + lane] + red[(((2 * msq + 1) * 4 + jj) * T + t) * 64 + lane];
-        gateup_tile_epilogue<BF16H, T>(g, v, es.xs[jq], es.cg[t], es.cu[t], row0 + q * 16, ng, t, amax[jq]);
+        if constexpr (FUSED) {
+          gateup_tile_h<false>(v, es.xs[jq], es.cg[t], es.cu[t], hvq[jq][t]);
+          amax[jq][0] = fmaxf(amax[jq][0], fabsf(hvq[jq][t][0]));
+          amax[jq][1] = fmaxf(amax[jq][1], fabsf(hvq[jq][t][1]));
+        } else {
+          gateup_tile_epilogue<BF16H, T>(g, v, es.xs[jq], es.cg[t], es.cu[t], row0 + q * 16, ng, t, amax[jq]);
+        }
       }
     }
   }
+  uint32_t seen = 0u;
   if constexpr (!BF16H) {
     const int ngroups = (g.I / 8) / T;
 #pragma unroll
@@ -411,29 +485,68 @@ __device__ __forceinline__ void pc_consumer(const GateUpArgs& g, uint8_t* lds, i
         if ((lane & 7) == 0) {      // lane 16 gq (rows 0, 2) and 16 gq + 8 (rows 1, 3)
           const int m = row0 + q * 16 + 4 * (lane >> 4) + ((lane & 8) ? 1 : 0);
 #pragma unroll
-          for (int e = 0; e < 2; ++e) g.amax_part[(size_t)(m + 2 * e) * ngroups + ng] = amax[jq][e];
+          for (int e = 0; e < 2; ++e) {
+            if constexpr (FUSED) {
+              if (m + 2 * e < g.M) seen |= amax_atomic(g.amax_g, m + 2 * e, amax[jq][e]);
+            } else {
+              g.amax_part[(size_t)(m + 2 * e) * ngroups + ng] = amax[jq][e];
+            }
+          }
+        }
+      }
+    }
+  }
+  if constexpr (FUSED) {
+    // every wave of the workgroup (producers too) arrives here; afterwards
+    // the codes go to an LDS stage [208 rows][T * 8 columns]
+    grid_arrive_and_wait(g.sync, gridDim.x, seen);
+    uint8_t* stage = lds;
+    constexpr int NC = T * 8;
+#pragma unroll
+    for (int jq = 0; jq < Q; ++jq) {
+      const int q = wave + kPcConsumers * jq;
+      if (q < MT) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int rl = q * 16 + gateup_value_row(e);
+          float sc, rcp;
+          row_scale_of(amax_load(g.amax_g, row0 + rl), sc, rcp);
+#pragma unroll
+          for (int t = 0; t < T; ++t) stage_code(stage, NC, rl, t * 8 + (lane & 7), hvq[jq][t][e], sc, rcp);
         }
       }
     }
   }
 }
 
-template <int BF, int T, int C, bool BF16H>
+template <int BF, int T, int C, bool BF16H, bool FUSED>
 __global__ __launch_bounds__(64 * (kPcConsumers + kPcProducers)) void pc_gateup(GateUpArgs g) {
+  static_assert(!(FUSED && BF16H), "the BF16-down mode has no requantization");
   extern __shared__ v4f pc_lds[];
   uint8_t* lds = (uint8_t*)pc_lds;
   int mb, ng;
   gateup_block(g, (g.I / 8) / T, mb, ng);
   const int row0 = mb * 13 * 16;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (wave >= kPcConsumers) pc_producer<BF, T, C, BF16H>(g, lds, ng, wave - kPcConsumers);
-  else if (wave < 2) pc_consumer<BF, 4, T, C, BF16H>(g, lds, row0, ng, wave, 0);
-  else pc_consumer<BF, 3, T, C, BF16H>(g, lds, row0, ng, wave, 1 + 3 * (wave >> 1));
+  if (wave >= kPcConsumers) {
+    pc_producer<BF, T, C>(g, lds, ng, wave - kPcConsumers);
+    if constexpr (FUSED) grid_arrive_and_wait(g.sync, gridDim.x, 0u);
+  } else if (wave < 2) {
+    pc_consumer<BF, 4, T, C, BF16H, FUSED>(g, lds, row0, ng, wave, 0);
+  } else {
+    pc_consumer<BF, 3, T, C, BF16H, FUSED>(g, lds, row0, ng, wave, 1 + 3 * (wave >> 1));
+  }
+  if constexpr (FUSED) {
+    lds_barrier();   // every code staged
+    constexpr int NC = T * 8;
+    fused_write_out(g, lds, row0, 13 * 16, ng * NC, NC, ng == 0, mb == g.n_mb - 1, g.n_mb * 13 * 16,
+                    64 * (kPcConsumers + kPcProducers));
+  }
 }
 
-template <int BF, int T, int C, bool BF16H>
+template <int BF, int T, int C, bool BF16H, bool FUSED>
 hipError_t launch_pc(const GateUpArgs& g, int grid, hipStream_t st, const LaunchEvents& ev) {
-  auto fn = pc_gateup<BF, T, C, BF16H>;
+  auto fn = pc_gateup<BF, T, C, BF16H, FUSED>;
   constexpr size_t lds = Pc<BF, T, C>::LDS;
   static std::atomic<uint64_t> lds_set{0};
   if (hipError_t e = allow_lds((const void*)fn, lds, lds_set); e != hipSuccess) return e;
@@ -443,15 +556,47 @@ hipError_t launch_pc(const GateUpArgs& g, int grid, hipStream_t st, const Launch
 
 // ---------------------------------------------------------------- dispatch
 
-template <int BF, bool BF16H, int MT, int T, int MS, int KS, int D>
-hipError_t launch_ks(const GateUpArgs& g, int grid, hipStream_t st, const LaunchEvents& ev) {
-  constexpr int MTW = (MT + MS - 1) / MS;
-  auto fn = ks_gateup<BF, MT, T, MS, KS, D, BF16H>;
-  const size_t lds = (size_t)(MS == 1 && MT * T <= MS * KS ? T : (T > 1 ? 2 : 1)) * MS * KS * MTW * 64 * sizeof(v4f);
-  static std::atomic<uint64_t> lds_set{0};
-  if (hipError_t e = allow_lds((const void*)fn, lds, lds_set); e != hipSuccess) return e;
-  launch_kernel(fn, dim3(grid), dim3(64 * MS * KS), lds, st, ev, g);
+// The fused variant of a launch is used only if the whole grid can be
+// resident at once (its workgroups wait for each other); otherwise, and for
+// the BF16-down mode, the unfused one, followed by k_requant.  `fused`: in,
+// may the launch fuse; out, did it.
+template <class KF, class KU>
+hipError_t launch_either(KF fused_fn, KU plain_fn, int threads, size_t lds, const GateUpArgs& g, int grid,
+                         hipStream_t st, const LaunchEvents& ev, bool& fused, std::atomic<uint64_t>& lds_f,
+                         std::atomic<uint64_t>& lds_u, std::atomic<int> (&cap)[kMaxDevices]) {
+  if (fused) {
+    if (hipError_t e = allow_lds((const void*)fused_fn, lds, lds_f); e != hipSuccess) return e;
+    if (resident_capacity((const void*)fused_fn, threads, lds, cap) >= grid) {
+      launch_kernel(fused_fn, dim3(grid), dim3(threads), lds, st, ev, g);
+      return hipGetLastError();
+    }
+    fused = false;
+  }
+  if (hipError_t e = allow_lds((const void*)plain_fn, lds, lds_u); e != hipSuccess) return e;
+  launch_kernel(plain_fn, dim3(grid), dim3(threads), lds, st, ev, g);
   return hipGetLastError();
+}
+
+template <int BF, bool BF16H, int MT, int T, int MS, int KS, int D>
+hipError_t launch_ks(const GateUpArgs& g, int grid, hipStream_t st, const LaunchEvents& ev, bool& fused) {
+  constexpr int MTW = (MT + MS - 1) / MS;
+  // partial tiles in LDS (also the stage of a fused requantization's codes)
+  const size_t lds = (size_t)(MS == 1 && MT * T <= MS * KS ? T : (T > 1 ? 2 : 1)) * MS * KS * MTW * 64 * sizeof(v4f);
+  static std::atomic<uint64_t> lds_f{0}, lds_u{0};
+  static std::atomic<int> cap[kMaxDevices];
+  fused = fused && !BF16H;
+  return launch_either(ks_gateup<BF, MT, T, MS, KS, D, BF16H, !BF16H>, ks_gateup<BF, MT, T, MS, KS, D, BF16H, false>,
+                       64 * MS * KS, lds, g, grid, st, ev, fused, lds_f, lds_u, cap);
+}
+
+template <int BF, int T, int C, bool BF16H>
+hipError_t launch_pc(const GateUpArgs& g, int grid, hipStream_t st, const LaunchEvents& ev, bool& fused) {
+  constexpr size_t lds = Pc<BF, T, C>::LDS;
+  static std::atomic<uint64_t> lds_f{0}, lds_u{0};
+  static std::atomic<int> cap[kMaxDevices];
+  fused = fused && !BF16H;
+  return launch_either(pc_gateup<BF, T, C, BF16H, !BF16H>, pc_gateup<BF, T, C, BF16H, false>,
+                       64 * (kPcConsumers + kPcProducers), lds, g, grid, st, ev, fused, lds_f, lds_u, cap);
 }
 
 // Eight waves (two per SIMD: each CU keeps enough operand loads in flight)
@@ -461,7 +606,7 @@ hipError_t launch_ks(const GateUpArgs& g, int grid, hipStream_t st, const Launch
 // unit (ks_mainloop_roll), which fits the 256 registers a wave has at two
 // waves per SIMD.
 template <int BF, bool BF16H, int MT, int T>
-hipError_t go(const GateUpArgs& g, int grid, hipStream_t st, const LaunchEvents& ev) {
+hipError_t go(const GateUpArgs& g, int grid, hipStream_t st, const LaunchEvents& ev, bool& fused) {
   constexpr int MS = MT >= 13 ? 2 : 1;
   constexpr int KS = 8 / MS;
   constexpr int MTW = (MT + MS - 1) / MS;
@@ -469,47 +614,54 @@ hipError_t go(const GateUpArgs& g, int grid, hipStream_t st, const LaunchEvents&
   // six NVFP4 tiles of 2-4 m-tiles: one chunk in flight per wave (two
   // would not fit the registers of two waves per SIMD)
   if constexpr ((BF == kB_FP8_F16 || BF == kB_FP4_F16) && MT == 13 && T <= 3) {
-    if (C == 16) return launch_pc<BF, T, 16, BF16H>(g, grid, st, ev);
-    if (C == 32) return launch_pc<BF, T, 32, BF16H>(g, grid, st, ev);
+    if (C == 16) return launch_pc<BF, T, 16, BF16H>(g, grid, st, ev, fused);
+    if (C == 32) return launch_pc<BF, T, 32, BF16H>(g, grid, st, ev, fused);
   }
-  if constexpr (T == 6) return launch_ks<BF, BF16H, MT, T, MS, KS, 1>(g, grid, st, ev);
-  else if constexpr (MTW <= 4) return launch_ks<BF, BF16H, MT, T, MS, KS, 2>(g, grid, st, ev);
-  else if (C == 4 * KS) return launch_ks<BF, BF16H, MT, T, MS, KS, -4>(g, grid, st, ev);
-  else if (C == 8 * KS) return launch_ks<BF, BF16H, MT, T, MS, KS, -8>(g, grid, st, ev);
-  else return launch_ks<BF, BF16H, MT, T, MS, KS, -1>(g, grid, st, ev);
+  if constexpr (T == 6) return launch_ks<BF, BF16H, MT, T, MS, KS, 1>(g, grid, st, ev, fused);
+  else if constexpr (MTW <= 4) return launch_ks<BF, BF16H, MT, T, MS, KS, 2>(g, grid, st, ev, fused);
+  else if (C == 4 * KS) return launch_ks<BF, BF16H, MT, T, MS, KS, -4>(g, grid, st, ev, fused);
+  else if (C == 8 * KS) return launch_ks<BF, BF16H, MT, T, MS, KS, -8>(g, grid, st, ev, fused);
+  else return launch_ks<BF, BF16H, MT, T, MS, KS, -1>(g, grid, st, ev, fused);
 }
 
 template <int BF, bool BF16H, int MT>
-hipError_t go_t(const GateUpArgs& g, int T, int grid, hipStream_t st, const LaunchEvents& ev) {
+hipError_t go_t(const GateUpArgs& g, int T, int grid, hipStream_t st, const LaunchEvents& ev, bool& fused) {
   switch (T) {
-    case 1: return go<BF, BF16H, MT, 1>(g, grid, st, ev);
-    case 2: return go<BF, BF16H, MT, 2>(g, grid, st, ev);
-    case 3: return go<BF, BF16H, MT, 3>(g, grid, st, ev);
-    case 6: if constexpr (BF == kB_FP4_F16 && (MT == 2 || MT == 4)) return go<BF, BF16H, MT, 6>(g, grid, st, ev);
+    case 1: return go<BF, BF16H, MT, 1>(g, grid, st, ev, fused);
+    case 2: return go<BF, BF16H, MT, 2>(g, grid, st, ev, fused);
+    case 3: return go<BF, BF16H, MT, 3>(g, grid, st, ev, fused);
+    case 6:
+      if constexpr (BF == kB_FP4_F16 && (MT == 2 || MT == 4)) return go<BF, BF16H, MT, 6>(g, grid, st, ev, fused);
   }
   return hipErrorInvalidValue;
 }
 
 template <int BF, bool BF16H>
-hipError_t go_mt(const GateUpArgs& g, int MT, int T, int grid, hipStream_t st, const LaunchEvents& ev) {
+hipError_t go_mt(const GateUpArgs& g, int MT, int T, int grid, hipStream_t st, const LaunchEvents& ev, bool& fused) {
   switch (MT) {
-    case 1: return go_t<BF, BF16H, 1>(g, T, grid, st, ev);
-    case 2: return go_t<BF, BF16H, 2>(g, T, grid, st, ev);
-    case 4: return go_t<BF, BF16H, 4>(g, T, grid, st, ev);
-    case 7: return go_t<BF, BF16H, 7>(g, T, grid, st, ev);
-    case 13: return go_t<BF, BF16H, 13>(g, T, grid, st, ev);
+    case 1: return go_t<BF, BF16H, 1>(g, T, grid, st, ev, fused);
+    case 2: return go_t<BF, BF16H, 2>(g, T, grid, st, ev, fused);
+    case 4: return go_t<BF, BF16H, 4>(g, T, grid, st, ev, fused);
+    case 7: return go_t<BF, BF16H, 7>(g, T, grid, st, ev, fused);
+    case 13: return go_t<BF, BF16H, 13>(g, T, grid, st, ev, fused);
   }
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_gateup(const Plan& p, const GateUpArgs& g, hipStream_t st, const LaunchEvents& ev) {
-  if (p.lg1) return launch_gateup_large(p, g, st, ev);
+hipError_t launch_gateup(const Plan& p, const GateUpArgs& g, hipStream_t st, const LaunchEvents& ev, bool& fused) {
+  if (p.lg1) {
+    fused = false;
+    return launch_gateup_large(p, g, st, ev);
+  }
   const int grid = p.ngroups1 * p.n_mblocks;
-  if (p.prec == kFP8) return go_mt<kB_FP8_F16, false>(g, p.MT, p.T1, grid, st, ev);
-  if (p.prec == kFP8DownBF16) return go_mt<kB_FP8_F16, true>(g, p.MT, p.T1, grid, st, ev);
-  return go_mt<kB_FP4_F16, false>(g, p.MT, p.T1, grid, st, ev);
+  if (p.prec == kFP8) return go_mt<kB_FP8_F16, false>(g, p.MT, p.T1, grid, st, ev, fused);
+  if (p.prec == kFP8DownBF16) {
+    fused = false;
+    return go_mt<kB_FP8_F16, true>(g, p.MT, p.T1, grid, st, ev, fused);
+  }
+  return go_mt<kB_FP4_F16, false>(g, p.MT, p.T1, grid, st, ev, fused);
 }
 
 }  // namespace ocq

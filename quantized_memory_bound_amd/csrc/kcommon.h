@@ -49,6 +49,13 @@ struct GateUpArgs {
   uint16_t* hb;             // bf16(h), fragment order (BF16-down mode)
   uint16_t* tap_hb;         // optional plain [M][I] copy of bf16(h) (BF16-down mode)
   float* amax_part;         // [Mpad][ngroups] max |h| of each row over each workgroup's columns
+  // per-token requantization inside the gate/up kernel (fused launches only):
+  uint32_t* amax_g;         // [Mpad] max |h| of each row (float bits, atomic max), zeroed by the x quantization
+  uint32_t* sync;           // [0] arrival count, [1] wait time-out flag, zeroed by the x quantization
+  uint8_t* hq;              // E4M3 codes of h, fragment order, Mpad rows
+  float* sh;                // [Mpad] row scales
+  uint8_t* tap_hq;          // optional plain [M][I] copy of the codes
+  float* tap_sh;            // optional plain [M] copy of the scales
   int H, I, M, n_mb, Mpad;
 };
 
@@ -60,6 +67,7 @@ struct DownArgs {
   const uint8_t* wbscales;  // NVFP4 block-scale groups
   const float* tscale;      // NVFP4: blob header s_down
   uint16_t* y;              // [M][H]
+  const uint32_t* sync;     // gate/up wait flags (sync[1] != 0: the fused requantization timed out)
   int H, I, M, n_mb, ngroups;
 };
 
@@ -90,8 +98,28 @@ inline hipError_t allow_lds(const void* fn, size_t bytes, std::atomic<uint64_t>&
   return e;
 }
 
-hipError_t launch_gateup(const Plan& p, const GateUpArgs& g, hipStream_t st, const LaunchEvents& ev);
+// fused: in (may the kernel requantize h itself) / out (did it)
+hipError_t launch_gateup(const Plan& p, const GateUpArgs& g, hipStream_t st, const LaunchEvents& ev, bool& fused);
 hipError_t launch_down(const Plan& p, const DownArgs& d, hipStream_t st);
+
+constexpr int kMaxDevices = 64;
+
+// Workgroups of kernel fn (threads per workgroup, dynamic LDS bytes) that
+// can be resident at once on the current device: occupancy per CU times the
+// CU count, cached per device ordinal in cap (0 = not yet known, -1 = none).
+inline int resident_capacity(const void* fn, int threads, size_t lds, std::atomic<int> (&cap)[kMaxDevices]) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  int c = cap[dev].load(std::memory_order_relaxed);
+  if (c != 0) return c;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, lds) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  c = per_cu * cus > 0 ? per_cu * cus : -1;
+  cap[dev].store(c, std::memory_order_relaxed);
+  return c;
+}
 hipError_t launch_gateup_large(const Plan& p, const GateUpArgs& g, hipStream_t st, const LaunchEvents& ev);
 hipError_t launch_down_large(const Plan& p, const DownArgs& d, hipStream_t st);
 
@@ -151,6 +179,19 @@ __device__ __forceinline__ v2u e4m3x8_quot(const float (&v)[8], float s, float r
   int hi = __builtin_amdgcn_cvt_pk_fp8_f32(q[4], q[5], 0, false);
   hi = __builtin_amdgcn_cvt_pk_fp8_f32(q[6], q[7], hi, true);
   return v2u{(uint32_t)lo, (uint32_t)hi};
+}
+
+// One E4M3 code (low byte) of fl32(v / s) for s > 0 with rcp = fl32(1 / s):
+// the single-value form of e4m3x8_quot (same window test, same fallback to
+// the exact quotient, same saturating hardware conversion).
+__device__ __forceinline__ uint32_t e4m3_quot1(float v, float s, float rcp) {
+  float q = v * rcp;
+  const float t = fabsf(q) * 512.0f;
+  const bool near = ((t < 8.0f) & (fabsf(__builtin_amdgcn_fractf(t) - 0.5f) < 0x1p-19f)) |
+                    ((__float_as_uint(q) & 0xFFFFFu) - 0x7FFFDu <= 6u);
+  if (near) q = v / s;
+  q = __builtin_amdgcn_fmed3f(q, -448.0f, 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q, 0.0f, 0, false) & 0xFFu;
 }
 
 __device__ __forceinline__ uint32_t bf16_bits(float v) {   // round to nearest even (finite v)

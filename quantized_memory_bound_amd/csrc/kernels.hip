@@ -3,14 +3,18 @@
 // stages live in gemm_gateup.hip and gemm_down.hip (main loops in
 // gemm_core.h).
 //
-// One forward call = four kernels on the caller's stream:
+// One forward call = three kernels on the caller's stream:
 //   k_xquant   per-token E4M3 quantization of x (scale amax/448), zero rows
 //              up to whole m-blocks.
 //   gate/up    G = xq Wg^T, U = xq Wu^T (exact products, fp32 accumulation),
-//              h = SiLU(G sx sw_g) * (U sx sw_u), per-workgroup row maxima of
-//              |h| (or bf16(h) for a BF16 down projection).
-//   k_requant  sh = max|h| / 448 per row, hq = E4M3(h / sh).
+//              h = SiLU(G sx sw_g) * (U sx sw_u), and in the same launch the
+//              per-token requantization sh = max|h| / 448, hq = E4M3(h / sh)
+//              (row maxima across workgroups through device-scope atomics,
+//              h kept in registers), or bf16(h) for a BF16 down projection.
 //   down       Y = hq Wd^T (or bf16(h) Wd^T), y = bf16(Y sh sw_d).
+// Where the gate/up grid cannot be resident all at once (several m-blocks,
+// the LDS-tiled kernels for many rows), it writes fp32 h and per-workgroup
+// row maxima instead and a fourth kernel, k_requant, quantizes.
 // Cited passages ("OCRia 推理栈：单卡 B200 提速近 10 倍"): "Reducing the data
 // moved: workload-aware quantization" (FP8 / NVFP4 / BF16 weights per layer),
 // "Generate more tokens per target pass" (M = requests x (1 + drafts) rows
@@ -56,12 +60,16 @@ inline int tile_row_grid(int mtiles, int nrest) { return (mtiles + 7) / 8 * 128 
 __global__ __launch_bounds__(kThreads) void k_xquant(const uint16_t* __restrict__ x, const float* __restrict__ xmul,
                                                      int M, int H, int Mpad,
                                                      uint8_t* __restrict__ xq, int f16, float* __restrict__ sx,
-                                                     uint8_t* __restrict__ tap_q, float* __restrict__ tap_s) {
+                                                     uint8_t* __restrict__ tap_q, float* __restrict__ tap_s,
+                                                     uint32_t* __restrict__ amax_g, uint32_t* __restrict__ sync) {
   __shared__ float s_max[kWaves];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   int m, rest;
   if (!tile_row_of(blockIdx.x, Mpad / 16, m, rest)) return;
   const int C = H / 128;
+  // the next kernel's grid-wide row maxima and arrival count start at zero
+  if (threadIdx.x == 0) amax_g[m] = 0u;
+  if (m == 0 && threadIdx.x < 2) sync[threadIdx.x] = 0u;
   if (m >= M) {                                     // padding row: zero codes, zero scale
     for (int k = threadIdx.x * 8; k < H; k += kThreads * 8) {
       if (f16) *(v4i*)((uint16_t*)xq + frag_off16(m, k, C)) = v4i{0, 0, 0, 0};
@@ -210,6 +218,13 @@ __global__ __launch_bounds__(kThreads) void k_requant(const float* __restrict__ 
 
 // ---------------------------------------------------------------- forward
 
+// Off by default: measured on MI355X, the grid-wide exchange of the row
+// maxima (device-scope atomics, arrival count, wait) costs more than the
+// separate requantization launch it replaces (spec-verify block 35 -> 50 us).
+static std::atomic<int> g_fused_requant{0};
+
+void set_fused_requant(bool on) { g_fused_requant.store(on ? 1 : 0, std::memory_order_relaxed); }
+
 static inline void stage(const FwdArgs& a, int i) {
   if (a.stage_events && a.stage_events[i]) (void)hipEventRecord((hipEvent_t)a.stage_events[i], (hipStream_t)a.stream);
 }
@@ -225,12 +240,14 @@ int launch_forward(const Plan& p, const FwdArgs& a) {
   uint8_t* hq = ws + p.off_hq;
   uint16_t* hb = (uint16_t*)(ws + p.off_hb);
   float* sh = (float*)(ws + p.off_sh);
+  uint32_t* amax_g = (uint32_t*)(ws + p.off_amaxg);
+  uint32_t* sync = (uint32_t*)(ws + p.off_sync);
 
   stage(a, 0);
   const bool bf16_down = p.prec == kFP8DownBF16;
   hipLaunchKernelGGL(k_xquant, dim3(tile_row_grid(p.Mpad / 16, 1)), dim3(kThreads), 0, st, a.x,
                      (const float*)(a.blob + L.off_xmul), p.M, p.hidden, p.Mpad, xq, p.lg1, sx,
-                     (uint8_t*)a.taps.x_codes, (float*)a.taps.x_scales);
+                     (uint8_t*)a.taps.x_codes, (float*)a.taps.x_scales, amax_g, sync);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return (int)e;
 
@@ -242,16 +259,20 @@ int launch_forward(const Plan& p, const FwdArgs& a) {
   g.tscales = (const float*)(a.blob + offsetof(BlobHeader, s_gate));
   g.h32 = h32; g.hb = hb; g.amax_part = amax_part;
   g.tap_hb = bf16_down ? (uint16_t*)a.taps.h_out : nullptr;
+  g.amax_g = amax_g; g.sync = sync; g.hq = hq; g.sh = sh;
+  g.tap_hq = bf16_down ? nullptr : (uint8_t*)a.taps.h_out;
+  g.tap_sh = (float*)a.taps.h_scales;
   g.H = p.hidden; g.I = p.inter; g.M = p.M; g.n_mb = p.n_mblocks; g.Mpad = p.Mpad;
   LaunchEvents gev;   // stage events 1 and 2 are taken by the gate/up launch itself
   if (a.stage_events) {
     gev.start = (hipEvent_t)a.stage_events[1];
     gev.end = (hipEvent_t)a.stage_events[2];
   }
-  e = launch_gateup(p, g, st, gev);
+  bool fused = !bf16_down && g_fused_requant.load(std::memory_order_relaxed) != 0;
+  e = launch_gateup(p, g, st, gev, fused);
   if (e != hipSuccess) return (int)e;
 
-  if (!bf16_down) {
+  if (!bf16_down && !fused) {
     hipLaunchKernelGGL(k_requant, dim3(tile_row_grid(p.Mpad / 16, (p.inter + kRqCols - 1) / kRqCols)),
                        dim3(kThreads), 0, st,
                        h32, amax_part,
@@ -270,6 +291,7 @@ int launch_forward(const Plan& p, const FwdArgs& a) {
   d.wbscales = a.blob + L.off_dn_bscales;
   d.tscale = (const float*)(a.blob + offsetof(BlobHeader, s_down));
   d.y = a.y;
+  d.sync = sync;
   d.H = p.hidden; d.I = p.inter; d.M = p.M; d.n_mb = p.n_mb2; d.ngroups = p.ngroups2;
   e = launch_down(p, d, st);
   stage(a, 4);

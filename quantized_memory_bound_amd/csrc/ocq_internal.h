@@ -38,6 +38,8 @@ struct FwdArgs {
 
 // enqueue the kernels of one forward call (kernels.hip); returns 0 or a hipError_t value
 int launch_forward(const Plan& p, const FwdArgs& a);
+// process-wide: may gate/up launches requantize h themselves (default on)
+void set_fused_requant(bool on);
 
 // measurement kernels (diag.hip); return 0 or a hipError_t value
 int diag_stream_read(const void* src, size_t bytes, void* out, int nblocks, void* stream);

@@ -132,8 +132,10 @@ struct Plan {
   // partial maxima of |h| per row written by the gate/up kernel: one per
   // workgroup (skinny kernels) or per wave column (LDS-tiled kernel)
   int namax;
-  // workspace offsets (xq, hq, hb are fragment-ordered operand buffers of Mpad rows)
-  size_t off_xq, off_sx, off_amax, off_h32, off_hq, off_hb, off_sh, total;
+  // workspace offsets (xq, hq, hb are fragment-ordered operand buffers of Mpad rows);
+  // amaxg / sync: grid-wide row maxima and the arrival counter of a gate/up
+  // launch that requantizes h itself
+  size_t off_xq, off_sx, off_amax, off_h32, off_hq, off_hb, off_sh, off_amaxg, off_sync, total;
 };
 
 inline int pick_mt(int M) {
@@ -218,6 +220,8 @@ inline Plan make_plan(int M, int hidden, int inter, int prec) {
   p.off_hq = o;   o = align_up(o + (prec == kFP8DownBF16 ? 0 : Mp * inter));
   p.off_hb = o;   o = align_up(o + (prec == kFP8DownBF16 ? Mp * inter * 2 : 0));
   p.off_sh = o;   o = align_up(o + Mp * 4);
+  p.off_amaxg = o; o = align_up(o + Mp * 4);
+  p.off_sync = o; o = align_up(o + 2 * 4);
   p.total = o;
   return p;
 }

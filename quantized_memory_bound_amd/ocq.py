@@ -29,7 +29,7 @@ EXPORTS = ("ocq_version", "ocq_packed_bytes", "ocq_pack_weights_host", "ocq_pack
            "ocq_set_stage_events", "ocq_last_error", "ocq_stack_workspace_bytes", "ocq_mlp_stack_forward",
            "ocq_calibrate_smoothing_host", "ocq_pack_weights_smoothed_host", "ocq_pack_weights_smoothed",
            "ocq_diag_stream_read", "ocq_diag_empty", "ocq_diag_mfma_dot", "ocq_noalloc_scratch_bytes",
-           "ocq_mlp_forward_noalloc")
+           "ocq_mlp_forward_noalloc", "ocq_set_fused_requant")
 
 
 class OcqError(RuntimeError):
@@ -79,6 +79,7 @@ def lib():
     L.ocq_stack_workspace_bytes.argtypes, L.ocq_stack_workspace_bytes.restype = [i, i, i, ip, i], sz
     L.ocq_mlp_stack_forward.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(sz), ip, i, vp, i, i, i, vp, vp, sz, vp]
     L.ocq_mlp_stack_forward.restype = i
+    L.ocq_set_fused_requant.argtypes, L.ocq_set_fused_requant.restype = [i], i
     L.ocq_noalloc_scratch_bytes.argtypes, L.ocq_noalloc_scratch_bytes.restype = [], sz
     L.ocq_mlp_forward_noalloc.argtypes = [vp, sz, vp, i, i, i, i, vp, ctypes.POINTER(Taps), vp]
     L.ocq_mlp_forward_noalloc.restype = i
@@ -187,6 +188,12 @@ def pack_weights(w_gate, w_up, w_down, prec_mode, device="cuda", stream=None, sm
                                            None if sm is None else sm.ctypes.data, hidden, inter, prec_mode,
                                            blob.data_ptr(), n, _stream_handle(stream)))
     return blob
+
+
+def set_fused_requant(enable):
+    """Process-wide: requantize h inside the gate/up kernel where its grid
+    fits the GPU at once (True), or in a second kernel (False, the default)."""
+    _check(lib().ocq_set_fused_requant(1 if enable else 0))
 
 
 def set_stage_events(events):

@@ -296,3 +296,30 @@ def test_binding_rejects_bad_tensors():
         args.update(kw)
         with pytest.raises(ocq.OcqError):
             ocq.mlp_forward(**args)
+
+
+# The per-token requantization inside the gate/up kernel (grid-wide row
+# maxima, h kept in registers) and the two-pass form (fp32 h to the
+# workspace, then k_requant) compute the same h, the same maxima and the
+# same codes: every output must be bit-identical.  Shapes: the skinny
+# kernels (one pair per wave, and several m-tiles per wave), the 13-m-tile
+# kernel with weight producers (E4M3 and NVFP4 weights), the decode and
+# spec-verify workloads' shapes, and NVFP4 with six tiles per workgroup.
+@pytest.mark.parametrize("H,Iw,M,prec", [(256, 512, 4, 0), (384, 640, 17, 2), (512, 1024, 100, 0),
+                                         (2048, 6144, 208, 0), (2048, 6144, 16, 0), (2048, 1024, 150, 2),
+                                         (4096, 12288, 52, 2), (256, 768, 208, 0)])
+def test_fused_requant_matches_two_pass(H, Iw, M, prec):
+    print("case fused requant hidden=%d inter=%d M=%d prec=%d" % (H, Iw, M, prec), flush=True)
+    d = I.make_inputs(H, Iw, M, x_outliers=True, w_std=0.02, seed=H + Iw + M + prec)
+    blob = ocq.pack_weights(d["w_gate"], d["w_up"], d["w_down"], prec)
+    try:
+        ocq.set_fused_requant(False)
+        g2, _ = run_gpu(d, prec, blob=blob)
+        ocq.set_fused_requant(True)
+        g1, _ = run_gpu(d, prec, blob=blob)
+    finally:
+        ocq.set_fused_requant(False)
+    for k in ("y", "xq", "sx", "hq", "sh"):
+        assert np.array_equal(g1[k], g2[k]), k
+    r = O.block_reference(d["x_bits"], d["w_gate"], d["w_up"], d["w_down"], prec)
+    compare(g1, r, prec, what="fused %dx%d M=%d prec=%d" % (H, Iw, M, prec))

@@ -65,28 +65,53 @@ struct Lg {
   static_assert(LDS <= 160 * 1024, "LDS of one CU");
 };
 
-// Issue this wave's loads of stage s into `slot`.  a: activation block of the
-// workgroup's first m-tile (+ lane * 16), nva: m-tiles that exist (later ones
-// reload the last; their results are dropped); w: weight tile 0 (+ lane * 16).
-// Unit x of the stage goes to slot + x KB: unit position x / UT, then
-// (m-tile, activation unit) or weight tile by x % UT.
+// This wave's load sources.  Load q of every stage fetches unit x = wave +
+// q NW of the stage: unit position x / UT, then (m-tile, activation unit) or
+// weight tile by x % UT.  Which operand, m-tile (those past nva reload the
+// last; their results are dropped), sub-unit and tile a load slot reads is
+// the same in every stage, so it is resolved once here; per stage only the
+// chunk and the first unit position move the sources, by one offset per
+// operand (a few scalar instructions per stage instead of the whole index
+// arithmetic per load).  a: activation block of the workgroup's first m-tile,
+// w: weight tile 0 (both + lane * 16).
 template <class G>
-__device__ __forceinline__ void lg_issue(const uint8_t* a, int nva, size_t a_mt, const uint8_t* w, size_t w_tile,
-                                         int s, uint8_t* slot, int wave) {
-  const int c = s / G::SPC, u0 = (s % G::SPC) * G::UPS;
+struct LgSrc {
+  const uint8_t* p[G::PW];   // the slot's unit at chunk 0, unit position 0
+  bool act[G::PW];           // activation unit (else weight)
+};
+
+template <class G>
+__device__ __forceinline__ LgSrc<G> lg_sources(const uint8_t* a, int nva, size_t a_mt, const uint8_t* w,
+                                               size_t w_tile, int wave) {
+  LgSrc<G> r;
 #pragma unroll
   for (int q = 0; q < G::PW; ++q) {
-    const int x = wave + q * G::NW;   // wave-uniform
-    if (q == G::PW - 1 && x >= G::NU) break;
+    const int x0 = wave + q * G::NW;
+    const int x = x0 < G::NU ? x0 : G::NU - 1;   // the last slot of waves >= FULL is never issued
     const int uu = x / G::UT, y = x % G::UT;
-    const uint8_t* src;
+    r.act[q] = y < G::AW;
     if (y < G::AW) {
       const int mt = y / G::AU < nva ? y / G::AU : nva - 1;
-      src = a + mt * a_mt + (size_t)c * G::A_BLK + ((u0 + uu) * G::AU + y % G::AU) * 1024;
+      r.p[q] = a + mt * a_mt + (size_t)(uu * G::AU + y % G::AU) * 1024;
     } else {
-      src = w + (y - G::AW) * w_tile + (size_t)c * Fmt<G::BF>::kGlobal + (u0 + uu) * 1024;
+      r.p[q] = w + (y - G::AW) * w_tile + (size_t)uu * 1024;
     }
-    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(slot + x * 1024), 16, 0, 0);
+  }
+  return r;
+}
+
+// Issue this wave's loads of stage s into `slot`.
+template <class G>
+__device__ __forceinline__ void lg_issue(const LgSrc<G>& src, int s, uint8_t* slot, int wave, bool full) {
+  const int c = s / G::SPC, u0 = (s % G::SPC) * G::UPS;
+  const size_t off_a = (size_t)c * G::A_BLK + (size_t)u0 * G::AU * 1024;
+  const size_t off_w = (size_t)c * Fmt<G::BF>::kGlobal + (size_t)u0 * 1024;
+#pragma unroll
+  for (int q = 0; q < G::PW; ++q) {
+    if (q == G::PW - 1 && !full) break;
+    const int x = wave + q * G::NW;   // wave-uniform
+    __builtin_amdgcn_global_load_lds((const void*)(src.p[q] + (src.act[q] ? off_a : off_w)),
+                                     (lds_void*)(slot + x * 1024), 16, 0, 0);
   }
 }
 
@@ -159,6 +184,15 @@ __device__ __forceinline__ void lg_mfma(const LgFrag<G>& fa, const LgWFrag<G>& f
   }
 }
 
+// Tell the compiler's wait tracking that this wave has no LDS or scalar-memory
+// access outstanding.  It cannot see the wait inside lds_barrier (inline asm),
+// and with more LDS reads in flight than the counter can name it falls back to
+// waiting for all of them, which would hold each piece's MFMAs until the next
+// piece's reads had landed.  Placed where everything issued before has long
+// completed (after a barrier, after a piece's MFMA issue), it costs nothing and
+// lets the reads of the next piece overlap the MFMAs of the current one.
+__device__ __forceinline__ void lgkm_settled() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
 // acc over all NS stages (NS even).  All NSTG slots are filled up front;
 // after the barrier of stage s + 1 every wave has finished its LDS reads of
 // stage s, so stage s + NSTG goes into that slot.  Stage indices past the
@@ -178,8 +212,9 @@ __device__ __forceinline__ void lg_mainloop(const uint8_t* a, int nva, size_t a_
   const int lane = threadIdx.x & 63;
   const bool full = wave < G::FULL;
   auto slot = [&](int s) { return lds + (size_t)(s % G::NSTG) * G::NU * 1024 + lane * 16; };
+  const LgSrc<G> src = lg_sources<G>(a, nva, a_mt, w, w_tile, wave);
   auto issue = [&](int s) {
-    lg_issue<G>(a, nva, a_mt, w, w_tile, s < NS ? s : NS - 1, lds + (size_t)(s % G::NSTG) * G::NU * 1024, wave);
+    lg_issue<G>(src, s < NS ? s : NS - 1, lds + (size_t)(s % G::NSTG) * G::NU * 1024, wave, full);
   };
 #pragma unroll
   for (int s = 0; s < G::NSTG; ++s) issue(s);
@@ -205,6 +240,7 @@ __device__ __forceinline__ void lg_mainloop(const uint8_t* a, int nva, size_t a_
       } else {   // also after the last stage: no branch, so no conservative wait at a join
         lg_wait<G, G::NSTG - 2>(full);
         lds_barrier();
+        lgkm_settled();
         issue(s + G::NSTG);
         lg_read_a<G>(fa[1 - cur], slot(s + 1), wm, kw, 0);
         lg_read_b<G>(fb[1 - E], slot(s + 1), wt, kw);
@@ -213,9 +249,11 @@ __device__ __forceinline__ void lg_mainloop(const uint8_t* a, int nva, size_t a_
       __builtin_amdgcn_sched_barrier(0);
       lg_mfma<G>(fa[cur], fb[E], q, acc);
       __builtin_amdgcn_sched_barrier(0);
+      lgkm_settled();
     }
   };
   for (int s = 0; s < NS; s += 2) {
+    lgkm_settled();
     stage(s, std::integral_constant<int, 0>{});
     stage(s + 1, std::integral_constant<int, 1>{});
   }

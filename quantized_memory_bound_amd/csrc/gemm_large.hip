@@ -184,6 +184,32 @@ __device__ __forceinline__ void lg_mfma(const LgFrag<G>& fa, const LgWFrag<G>& f
   }
 }
 
+// Gate/up with 16-bit activations: the MFMAs of one piece take B already in
+// fp16 (bh_cur) and the E4M3 B of the next piece (sub-step i_next of fb_next)
+// is converted between them, so the converts issue while the matrix core runs
+// instead of ahead of the batch.  Conversion u follows MFMA 3 (u + 2) + 1: late
+// enough for B that was read from LDS just before the batch.
+template <class G>
+__device__ __forceinline__ void lg_mfma_pipelined(const LgFrag<G>& fa, const v8h (&bh_cur)[G::TW],
+                                                  const LgWFrag<G>& fb_next, int i_next, v8h (&bh_next)[G::TW],
+                                                  v4f (&acc)[G::MTW][G::TW]) {
+  static_assert(G::MTW * G::TW >= 3 * (G::TW + 2), "room to interleave the conversions");
+#pragma unroll
+  for (int j = 0; j < G::MTW; ++j) {
+#pragma unroll
+    for (int t = 0; t < G::TW; ++t) {
+      acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, fa.a[j]), bh_cur[t], acc[j][t], 0, 0, 0);
+      const int k = j * G::TW + t;
+      if (k % 3 == 2 && k / 3 >= 2 && k / 3 - 2 < G::TW) {
+        const int u = k / 3 - 2;
+        bh_next[u] = e4m3x8_to_f16((uint32_t)fb_next.b[u][2 * i_next], (uint32_t)fb_next.b[u][2 * i_next + 1]);
+        asm volatile("" : "+v"(bh_next[u]));   // keep the conversion here (not sunk to its use)
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
 // Tell the compiler's wait tracking that this wave has no LDS or scalar-memory
 // access outstanding.  It cannot see the wait inside lds_barrier (inline asm),
 // and with more LDS reads in flight than the counter can name it falls back to
@@ -228,6 +254,12 @@ __device__ __forceinline__ void lg_mainloop(const uint8_t* a, int nva, size_t a_
   LgWFrag<G> fb[2];
   lg_read_a<G>(fa[0], slot(0), wm, kw, 0);
   lg_read_b<G>(fb[0], slot(0), wt, kw);
+  constexpr bool PIPE = G::BF == kB_FP8_F16 && G::A16;
+  v8h bh[2][G::TW];
+  if constexpr (PIPE) {
+#pragma unroll
+    for (int t = 0; t < G::TW; ++t) bh[0][t] = e4m3x8_to_f16((uint32_t)fb[0].b[t][0], (uint32_t)fb[0].b[t][1]);
+  }
   // one stage with B buffer E (compile-time), A buffers fixed per piece when
   // a stage has two pieces, else alternating with the stage
   auto stage = [&](int s, auto ec) {
@@ -247,7 +279,12 @@ __device__ __forceinline__ void lg_mainloop(const uint8_t* a, int nva, size_t a_
       }
       // fences: the compiler would otherwise sink the reads to their uses
       __builtin_amdgcn_sched_barrier(0);
-      lg_mfma<G>(fa[cur], fb[E], q, acc);
+      if constexpr (PIPE) {
+        if (q == 0) lg_mfma_pipelined<G>(fa[cur], bh[0], fb[E], 1, bh[1], acc);
+        else lg_mfma_pipelined<G>(fa[cur], bh[1], fb[1 - E], 0, bh[0], acc);
+      } else {
+        lg_mfma<G>(fa[cur], fb[E], q, acc);
+      }
       __builtin_amdgcn_sched_barrier(0);
       lgkm_settled();
     }
@@ -341,6 +378,15 @@ __global__ __launch_bounds__(G::THREADS) void lg_gateup(GateUpArgs g) {
     cu[t] = g.wscales[g.I + n];
   }
   const int ngp = ngroups * G::WT;   // partial row maxima per row
+  // bf16(h) goes through LDS: each lane holds 2 of the 4 rows x 8 channels of
+  // a tile's value group, so storing it directly would be 2-byte stores
+  // spread over many lines; staged as [m-tile][row][tile][8 channels] per
+  // wave, each lane then writes 16 B (8 channels of one row) to the fragment
+  // order and the row-major tap.
+  constexpr int kStage = G::MTW * 16 * G::TW * 16;   // bytes per wave
+  static_assert(!BF16H || G::NW * kStage <= G::LDS, "staging fits the ring");
+  uint16_t* st = (uint16_t*)(lds + (size_t)wave * kStage);
+  if constexpr (BF16H) lds_barrier();   // every wave is done reading the ring
 #pragma unroll
   for (int j = 0; j < G::MTW; ++j) {
     const int mt = wm * G::MTW + j;
@@ -367,9 +413,7 @@ __global__ __launch_bounds__(G::THREADS) void lg_gateup(GateUpArgs g) {
         const float hv = (BF16H ? silu(ga) : silu_rcp(ga)) * (uv * xi * cu[t]);
         const int m = m_base + i;
         if constexpr (BF16H) {
-          const uint16_t hb = (uint16_t)bf16_bits(hv);
-          g.hb[frag_off16(m, n, g.I / 128)] = hb;
-          if (g.tap_hb && m < g.M) g.tap_hb[(size_t)m * g.I + n] = hb;
+          st[((j * 16 + (m - row0 - mt * 16)) * G::TW + t) * 8 + c] = (uint16_t)bf16_bits(hv);
         } else {
           g.h32[((size_t)tile * g.Mpad + m) * 8 + c] = hv;
           amax[e] = fmaxf(amax[e], fabsf(hv));
@@ -383,6 +427,23 @@ __global__ __launch_bounds__(G::THREADS) void lg_gateup(GateUpArgs g) {
         const int m = m_base + ((lane & 8) ? 1 : 0);
 #pragma unroll
         for (int e = 0; e < 2; ++e) g.amax_part[(size_t)(m + 2 * e) * ngp + ng * G::WT + wt] = amax[e];
+      }
+    }
+  }
+  if constexpr (BF16H) {
+    // the wave reads back what it staged (its own LDS accesses complete in order)
+    constexpr int kItems = G::MTW * 16 * G::TW;   // (m-tile, row, tile) groups of 8 channels
+    const int C128 = g.I / 128;
+#pragma unroll
+    for (int k0 = 0; k0 < kItems; k0 += 64) {
+      const int k = k0 + lane;
+      const int j = k / (16 * G::TW), rr = (k / G::TW) % 16, t = k % G::TW;
+      const int mt = wm * G::MTW + j;
+      if (k < kItems && mt < nva) {
+        const v4i d = *(const v4i*)(st + (size_t)k * 8);
+        const int m = row0 + mt * 16 + rr, n0 = (tile0 + t) * 8;
+        *(v4i*)(g.hb + frag_off16(m, n0, C128)) = d;
+        if (g.tap_hb && m < g.M) *(v4i*)(g.tap_hb + (size_t)m * g.I + n0) = d;
       }
     }
   }

@@ -340,7 +340,7 @@ __device__ __forceinline__ void gateup_tile_h(const v4f v, const v4f xs, float c
     const float gv = lo ? vi : (e ? p1 : p0);
     const float uv = lo ? (e ? p1 : p0) : vi;
     const float ga = gv * xi * cg;
-    hv[e] = (BF16H ? silu(ga) : silu_rcp(ga)) * (uv * xi * cu);
+    hv[e] = (BF16H ? silu_div(ga) : silu_rcp(ga)) * (uv * xi * cu);
   }
 }
 

@@ -340,6 +340,8 @@ __device__ __forceinline__ void lg_block(int n_mb, int ngroups, int& mb, int& ng
 
 // ---------------------------------------------------------------- gate/up
 
+constexpr size_t kLgScaleBytes = 2048;   // epilogue scales behind the gate/up ring
+
 template <class G, bool BF16H>
 __global__ __launch_bounds__(G::THREADS) void lg_gateup(GateUpArgs g) {
   extern __shared__ float lds_f[];
@@ -354,6 +356,20 @@ __global__ __launch_bounds__(G::THREADS) void lg_gateup(GateUpArgs g) {
   const int left = g.Mpad / 16 - row0 / 16;
   const int nva = left < G::RM ? left : G::RM;
   const size_t wtile = (size_t)C * Fmt<G::BF>::kGlobal;
+  // the epilogue's scales (the workgroup's row scales of x, then the gate
+  // and up column scales) go to LDS behind the ring with direct-to-LDS loads
+  // issued before the ring's: the first stage's wait covers them, and the
+  // epilogue reads them without a global round trip
+  float* sc = (float*)(lds + G::LDS);
+  constexpr int kRows = G::RM * 16, kCols = G::RT * 8;
+  static_assert(kRows + 2 * kCols <= kLgScaleBytes / 4, "scale area");
+  if (wave * 64 < kRows + 2 * kCols) {
+    const int k = wave * 64 + lane;
+    const float* src = k < kRows ? g.sx + row0 + (k < nva * 16 ? k : 0)
+                     : k < kRows + kCols ? g.wscales + ng * kCols + (k - kRows)
+                     : k < kRows + 2 * kCols ? g.wscales + g.I + ng * kCols + (k - kRows - kCols) : g.sx + row0;
+    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(sc + wave * 64), 4, 0, 0);
+  }
   v4f acc[G::MTW][G::TW];
 #pragma unroll
   for (int j = 0; j < G::MTW; ++j)
@@ -373,9 +389,9 @@ __global__ __launch_bounds__(G::THREADS) void lg_gateup(GateUpArgs g) {
   float cg[G::TW], cu[G::TW];
 #pragma unroll
   for (int t = 0; t < G::TW; ++t) {
-    const int n = (tile0 + t) * 8 + c;
-    cg[t] = g.wscales[n];
-    cu[t] = g.wscales[g.I + n];
+    const int k = (wt * G::TW + t) * 8 + c;   // column of the workgroup's group
+    cg[t] = sc[kRows + k];
+    cu[t] = sc[kRows + kCols + k];
   }
   const int ngp = ngroups * G::WT;   // partial row maxima per row
   // bf16(h) goes through LDS: each lane holds 2 of the 4 rows x 8 channels of
@@ -394,7 +410,7 @@ __global__ __launch_bounds__(G::THREADS) void lg_gateup(GateUpArgs g) {
     const int m_base = row0 + mt * 16 + 4 * (lane >> 4);
     v4f xs;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) xs[i] = g.sx[m_base + i];
+    for (int i = 0; i < 4; ++i) xs[i] = sc[m_base - row0 + i];
     float amax[2] = {0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < G::TW; ++t) {
@@ -410,7 +426,7 @@ __global__ __launch_bounds__(G::THREADS) void lg_gateup(GateUpArgs g) {
         const float gv = lo ? vi : (e ? p1 : p0);
         const float uv = lo ? (e ? p1 : p0) : vi;
         const float ga = gv * xi * cg[t];
-        const float hv = (BF16H ? silu(ga) : silu_rcp(ga)) * (uv * xi * cu[t]);
+        const float hv = (BF16H ? silu_div(ga) : silu_rcp(ga)) * (uv * xi * cu[t]);
         const int m = m_base + i;
         if constexpr (BF16H) {
           st[((j * 16 + (m - row0 - mt * 16)) * G::TW + t) * 8 + c] = (uint16_t)bf16_bits(hv);
@@ -493,9 +509,9 @@ __global__ __launch_bounds__(G::THREADS) void lg_down_bf16(DownArgs d) {
 
 template <class G, class Arg>
 hipError_t lg_launch(void (*fn)(Arg), int grid, const Arg& arg, hipStream_t st, std::atomic<uint64_t>& lds_set,
-                     const LaunchEvents& ev = LaunchEvents{}) {
-  if (hipError_t e = allow_lds((const void*)fn, G::LDS, lds_set); e != hipSuccess) return e;
-  launch_kernel(fn, dim3(grid), dim3(G::THREADS), G::LDS, st, ev, arg);
+                     const LaunchEvents& ev = LaunchEvents{}, size_t lds = G::LDS) {
+  if (hipError_t e = allow_lds((const void*)fn, lds, lds_set); e != hipSuccess) return e;
+  launch_kernel(fn, dim3(grid), dim3(G::THREADS), lds, st, ev, arg);
   return hipGetLastError();
 }
 
@@ -515,10 +531,10 @@ hipError_t launch_gateup_large(const Plan& p, const GateUpArgs& g, hipStream_t s
   const int grid = p.n_mblocks * ((p.inter / 8) / GUL::RT);
   if (p.prec == kFP8DownBF16) {
     static std::atomic<uint64_t> lds_set{0};
-    return lg_launch<GUL>(lg_gateup<GUL, true>, grid, g, st, lds_set, ev);
+    return lg_launch<GUL>(lg_gateup<GUL, true>, grid, g, st, lds_set, ev, GUL::LDS + kLgScaleBytes);
   }
   static std::atomic<uint64_t> lds_set{0};
-  return lg_launch<GUL>(lg_gateup<GUL, false>, grid, g, st, lds_set, ev);
+  return lg_launch<GUL>(lg_gateup<GUL, false>, grid, g, st, lds_set, ev, GUL::LDS + kLgScaleBytes);
 }
 
 hipError_t launch_down_large(const Plan& p, const DownArgs& d, hipStream_t st) {

@@ -228,16 +228,26 @@ __device__ __forceinline__ void e4m3x2_scales(uint32_t two, v2h& s0, v2h& s1) {
   s1 = v2h{sc[1], sc[1]};
 }
 
-// SiLU(g) = g / (1 + e^-g): hardware exp2, correctly rounded fp32 division
-// (h feeds bf16 / E4M3 rounding decisions, so the division is kept exact);
-// e^-g overflowing to +inf gives -0 for very negative g.
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
-
-// SiLU through the hardware reciprocal (about one unit in the last place):
-// for h that is requantized to E4M3, whose 3-bit mantissa makes such a
-// difference change a code only right next to a rounding midpoint.  The bf16
-// h of a BF16 down projection (8-bit mantissa) keeps the exact division.
+// SiLU(g) = g / (1 + e^-g) through the hardware exp2 and reciprocal (each
+// about one unit in the last place of fp32): for h that is requantized to
+// E4M3, whose 3-bit mantissa makes such a difference change a code only right
+// next to a rounding midpoint.  e^-g overflowing to +inf gives -0 for very
+// negative g.
 __device__ __forceinline__ float silu_rcp(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
+
+// The same with the quotient refined by one residual step, q = q0 + (g - d q0) / d
+// (the reciprocal's error no longer reaches the result, which is then the
+// correctly rounded quotient but in rare cases), for the bf16 h of a BF16 down
+// projection: its 8-bit mantissa makes a unit-in-the-last-place difference
+// change bf16(h) far more often than an E4M3 code.  Cheaper than the IEEE
+// division sequence (no scaling steps: d lies in [1, +inf]).
+__device__ __forceinline__ float silu_div(float g) {
+  const float d = 1.0f + __expf(-g);
+  const float r = __builtin_amdgcn_rcpf(d);
+  const float q0 = g * r;
+  const float q = __builtin_fmaf(__builtin_fmaf(-d, q0, g), r, q0);
+  return d == __builtin_inff() ? q0 : q;   // d = +inf: q0 = -0 (the refinement would be NaN)
+}
 
 // Cross-lane moves inside 16-lane rows through DPP (no LDS round trip).
 // CTRL: 0x128 row_ror:8 (lane r <- r ^ 8), 0xB1 quad_perm [1,0,3,2] (r ^ 1),

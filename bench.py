@@ -202,6 +202,36 @@ def stream_ceiling(torch, ocq, nbytes, dev, reps=64):
     return n / sec / 1e9
 
 
+def l2_ceiling(torch, ocq, dev, window=1 << 20, passes=64, blocks=512):
+    """GB/s at which L2 feeds the CUs: every workgroup re-reads one 1 MiB
+    window (resident in each XCD's L2) with the library's window-read
+    kernel; one timed launch after a warm-up launch."""
+    buf = torch.ones(window, dtype=torch.uint8, device=dev)
+    out = torch.empty(blocks, dtype=torch.int32, device=dev)
+    ocq.diag_window_read(buf, window, passes, out, blocks)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    ocq.diag_window_read(buf, window, passes, out, blocks)
+    t1.record()
+    torch.cuda.synchronize()
+    return window * passes * blocks / (t0.elapsed_time(t1) * 1e-3) / 1e9
+
+
+def mfma_ceiling(torch, ocq, dev, iters=4000, blocks=512):
+    """TFLOP/s of independent f16 MFMA 16x16x32 on register operands (two
+    8-wave workgroups per CU), one timed launch after a warm-up launch."""
+    out = torch.empty(512 * blocks, dtype=torch.float32, device=dev)
+    ocq.diag_mfma_rate(iters, out, blocks)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    flops = ocq.diag_mfma_rate(iters, out, blocks)
+    t1.record()
+    torch.cuda.synchronize()
+    return flops / (t0.elapsed_time(t1) * 1e-3) / 1e12
+
+
 def launch_floor(torch, ocq, reps=200):
     """Seconds per launch of an empty kernel, replayed from a graph."""
     g = capture_steps(torch, lambda i: ocq.diag_empty(), reps)
@@ -357,6 +387,11 @@ def main():
         roof["stream_ceiling_GBps"] = round(ceil, 1)
         roof["frac_of_stream_ceiling"] = round(gbytes / (gu_ms * 1e-3) / 1e9 / ceil, 4)
         roof["launch_floor_us"] = round(launch_floor(torch, ocq) * 1e6, 3)
+        l2 = l2_ceiling(torch, ocq, dev)
+        roof["l2_ceiling_GBps"] = round(l2, 1)
+        mf = mfma_ceiling(torch, ocq, dev)
+        roof["mfma_f16_ceiling_TFLOPs"] = round(mf, 1)
+        roof["frac_of_mfma_f16_ceiling"] = round(gflops / (gu_ms * 1e-3) / 1e12 / mf, 4)
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -242,6 +242,17 @@ ocq_status ocq_set_stage_events(void* const* events, int count);
  *   for one launch of that many bytes (the block streams its weights the
  *   same way: "Why decoding dominates latency" in the post, weights read on
  *   every step).
+ * ocq_diag_window_read: `blocks` workgroups of 256 lanes each read the same
+ *   window of `window_bytes` bytes (a multiple of 32768, at most 2^30) at
+ *   src_dev `passes` times with 16-byte loads, each writing one uint32 to
+ *   out_dev[block]: with a window that fits L2, the rate at which L2 feeds
+ *   the CUs (bytes read = blocks * passes * window_bytes), the ceiling for
+ *   operands that many workgroups re-read.
+ * ocq_diag_mfma_rate: `blocks` workgroups of 8 waves each issue iters x 16
+ *   independent f16 MFMA 16x16x32 on register operands (1 <= iters <= 2^20);
+ *   out_dev receives blocks * 512 floats (kept so the work is not dead);
+ *   *flops (if non-null) the floating-point operations of the launch: the
+ *   matrix-core rate the chip sustains, beside the published dense peak.
  * ocq_diag_empty: one empty kernel (the fixed cost of a launch).
  * ocq_diag_mfma_dot: c[m][n] = sum_k dec(a[m][k]) dec(b[n][k]) over E4M3
  *   codes (a: uint8 [M][K], b: uint8 [N][K], c: float [M][N], row-major,
@@ -253,6 +264,9 @@ ocq_status ocq_set_stage_events(void* const* events, int count);
  *     form 2: MFMA 16x16x32 fp8 x fp8 on the E4M3 codes
  *   so that each form's sums can be compared against exact ones. */
 ocq_status ocq_diag_stream_read(const void* src_dev, size_t bytes, void* out_dev, int blocks, void* stream);
+ocq_status ocq_diag_window_read(const void* src_dev, size_t window_bytes, int passes, void* out_dev, int blocks,
+                                void* stream);
+ocq_status ocq_diag_mfma_rate(int iters, void* out_dev, int blocks, void* stream, double* flops);
 ocq_status ocq_diag_empty(void* stream);
 ocq_status ocq_diag_mfma_dot(int form, const void* a_dev, const void* b_dev, int M, int N, int K, float* c_dev,
                              void* stream);

@@ -194,6 +194,27 @@ ocq_status ocq_diag_stream_read(const void* src_dev, size_t bytes, void* out_dev
   return rc ? set_hip_error((hipError_t)rc, "kernel launch") : OCQ_OK;
 }
 
+ocq_status ocq_diag_window_read(const void* src_dev, size_t window_bytes, int passes, void* out_dev, int blocks,
+                                void* stream) {
+  g_err.clear();
+  if (!src_dev || !out_dev || !aligned16(src_dev)) return set_error(OCQ_ERR_INVALID_ARG, "null or misaligned pointer");
+  if (window_bytes < 32768 || window_bytes % 32768 || window_bytes > ((size_t)1 << 30) || passes < 1 ||
+      passes > 65536 || blocks < 1 || blocks > 65536)
+    return set_error(OCQ_ERR_INVALID_ARG,
+                     "window_bytes a multiple of 32768 up to 2^30, passes in [1, 65536], blocks in [1, 65536]");
+  int rc = diag_window_read(src_dev, window_bytes, passes, out_dev, blocks, stream);
+  return rc ? set_hip_error((hipError_t)rc, "kernel launch") : OCQ_OK;
+}
+
+ocq_status ocq_diag_mfma_rate(int iters, void* out_dev, int blocks, void* stream, double* flops) {
+  g_err.clear();
+  if (!out_dev || iters < 1 || iters > (1 << 20) || blocks < 1 || blocks > 65536)
+    return set_error(OCQ_ERR_INVALID_ARG, "out_dev non-null, iters in [1, 2^20], blocks in [1, 65536]");
+  if (flops) *flops = (double)diag_mfma_rate_flops(iters, blocks);
+  int rc = diag_mfma_rate(iters, (float*)out_dev, blocks, stream);
+  return rc ? set_hip_error((hipError_t)rc, "kernel launch") : OCQ_OK;
+}
+
 ocq_status ocq_diag_empty(void* stream) {
   g_err.clear();
   int rc = diag_empty(stream);

@@ -4,6 +4,13 @@
 //   k_stream_read  a plain streaming read of a device buffer (16-byte loads,
 //                  several in flight per lane), the practical HBM ceiling for
 //                  a read of that many bytes in one launch;
+//   k_window_read  every workgroup reads the same small window several times
+//                  (16-byte loads): with the window resident in L2, the rate
+//                  at which L2 feeds the CUs, which bounds kernels whose
+//                  workgroups re-read shared operands;
+//   k_mfma_rate    independent f16 MFMA 16x16x32 on register operands, the
+//                  matrix-core rate the chip sustains (against the published
+//                  dense peak);
 //   k_empty        an empty kernel, the fixed cost of one launch;
 //   k_mfma_dot     C = A B^T over E4M3 codes through one matrix-core
 //                  instruction form, with the operand fragment order and the
@@ -38,6 +45,57 @@ __global__ __launch_bounds__(kStreamThreads) void k_stream_read(const v4i* __res
   uint32_t w = (uint32_t)(acc[0] ^ acc[1] ^ acc[2] ^ acc[3]);
   w = __reduce_or_sync(~0ull, w);
   if (threadIdx.x == 0) out[blockIdx.x] = w;
+}
+
+// Every workgroup reads the window [src, src + n16) `passes` times, 8 loads of
+// 16 B per lane in flight, starting at a per-workgroup offset (so workgroups
+// do not walk the window in lockstep); one word per workgroup is written.
+__global__ __launch_bounds__(kStreamThreads) void k_window_read(const v4i* __restrict__ src, size_t n16, int passes,
+                                                                 uint32_t* __restrict__ out) {
+  constexpr size_t kStep = (size_t)kStreamThreads * kStreamUnroll;
+  const size_t n = n16 / kStep * kStep;   // whole passes of the unrolled loop
+  const size_t start = ((size_t)blockIdx.x * 37 * kStep) % n;
+  v4i acc = v4i{0, 0, 0, 0};
+  for (int p = 0; p < passes; ++p) {
+    for (size_t base = threadIdx.x; base < n; base += kStep) {
+      v4i v[kStreamUnroll];
+#pragma unroll
+      for (int u = 0; u < kStreamUnroll; ++u) {
+        size_t i = start + base + (size_t)u * kStreamThreads;
+        i = i < n ? i : i - n;
+        v[u] = src[i];
+      }
+#pragma unroll
+      for (int u = 0; u < kStreamUnroll; ++u) acc ^= v[u];
+    }
+  }
+  uint32_t w = (uint32_t)(acc[0] ^ acc[1] ^ acc[2] ^ acc[3]);
+  w = __reduce_or_sync(~0ull, w);
+  if (threadIdx.x == 0) out[blockIdx.x] = w;
+}
+
+// Each wave keeps kMfmaAcc independent accumulators and issues iters rounds of
+// one MFMA on each; every lane writes one float so nothing is dead.
+constexpr int kMfmaAcc = 16;
+constexpr int kMfmaThreads = 512;
+__global__ __launch_bounds__(kMfmaThreads) void k_mfma_rate(int iters, float* __restrict__ out) {
+  v8h a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (_Float16)((threadIdx.x & 7) * 0.125f + i);
+    b[i] = (_Float16)(i * 0.0625f);
+  }
+  v4f acc[kMfmaAcc];
+#pragma unroll
+  for (int j = 0; j < kMfmaAcc; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < kMfmaAcc; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[j], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < kMfmaAcc; ++j) s += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
+  out[(size_t)blockIdx.x * kMfmaThreads + threadIdx.x] = s;
 }
 
 __global__ void k_empty() {}
@@ -87,6 +145,21 @@ __global__ __launch_bounds__(64) void k_mfma_dot(const uint8_t* __restrict__ a, 
 int diag_stream_read(const void* src, size_t bytes, void* out, int nblocks, void* stream) {
   hipLaunchKernelGGL(k_stream_read, dim3(nblocks), dim3(kStreamThreads), 0, (hipStream_t)stream, (const v4i*)src,
                      bytes / 16, (uint32_t*)out);
+  return (int)hipGetLastError();
+}
+
+int diag_window_read(const void* src, size_t window_bytes, int passes, void* out, int nblocks, void* stream) {
+  hipLaunchKernelGGL(k_window_read, dim3(nblocks), dim3(kStreamThreads), 0, (hipStream_t)stream, (const v4i*)src,
+                     window_bytes / 16, passes, (uint32_t*)out);
+  return (int)hipGetLastError();
+}
+
+size_t diag_mfma_rate_flops(int iters, int nblocks) {
+  return (size_t)2 * 16 * 16 * 32 * kMfmaAcc * (size_t)iters * (kMfmaThreads / 64) * (size_t)nblocks;
+}
+
+int diag_mfma_rate(int iters, float* out, int nblocks, void* stream) {
+  hipLaunchKernelGGL(k_mfma_rate, dim3(nblocks), dim3(kMfmaThreads), 0, (hipStream_t)stream, iters, out);
   return (int)hipGetLastError();
 }
 

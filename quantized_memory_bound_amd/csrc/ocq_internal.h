@@ -43,6 +43,9 @@ void set_fused_requant(bool on);
 
 // measurement kernels (diag.hip); return 0 or a hipError_t value
 int diag_stream_read(const void* src, size_t bytes, void* out, int nblocks, void* stream);
+int diag_window_read(const void* src, size_t window_bytes, int passes, void* out, int nblocks, void* stream);
+size_t diag_mfma_rate_flops(int iters, int nblocks);
+int diag_mfma_rate(int iters, float* out, int nblocks, void* stream);
 int diag_empty(void* stream);
 int diag_mfma_dot(int form, const uint8_t* a, const uint8_t* b, int M, int N, int K, float* c, void* stream);
 

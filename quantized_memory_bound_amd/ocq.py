@@ -28,7 +28,7 @@ EXPORTS = ("ocq_version", "ocq_packed_bytes", "ocq_pack_weights_host", "ocq_pack
            "ocq_unpack_weights_host", "ocq_workspace_bytes", "ocq_mlp_forward", "ocq_check_blob",
            "ocq_set_stage_events", "ocq_last_error", "ocq_stack_workspace_bytes", "ocq_mlp_stack_forward",
            "ocq_calibrate_smoothing_host", "ocq_pack_weights_smoothed_host", "ocq_pack_weights_smoothed",
-           "ocq_diag_stream_read", "ocq_diag_empty", "ocq_diag_mfma_dot", "ocq_noalloc_scratch_bytes",
+           "ocq_diag_stream_read", "ocq_diag_window_read", "ocq_diag_mfma_rate", "ocq_diag_empty", "ocq_diag_mfma_dot", "ocq_noalloc_scratch_bytes",
            "ocq_mlp_forward_noalloc", "ocq_set_fused_requant")
 
 
@@ -84,6 +84,8 @@ def lib():
     L.ocq_mlp_forward_noalloc.argtypes = [vp, sz, vp, i, i, i, i, vp, ctypes.POINTER(Taps), vp]
     L.ocq_mlp_forward_noalloc.restype = i
     L.ocq_diag_stream_read.argtypes, L.ocq_diag_stream_read.restype = [vp, sz, vp, i, vp], i
+    L.ocq_diag_window_read.argtypes, L.ocq_diag_window_read.restype = [vp, sz, i, vp, i, vp], i
+    L.ocq_diag_mfma_rate.argtypes, L.ocq_diag_mfma_rate.restype = [i, vp, i, vp, ctypes.POINTER(ctypes.c_double)], i
     L.ocq_diag_empty.argtypes, L.ocq_diag_empty.restype = [vp], i
     L.ocq_diag_mfma_dot.argtypes, L.ocq_diag_mfma_dot.restype = [i, vp, vp, i, i, i, vp, vp], i
     _lib = L
@@ -365,6 +367,32 @@ def diag_stream_read(src, out, blocks, stream=None):
     if out.numel() * out.element_size() < 4 * blocks:
         raise OcqError(ERR_BUFFER_TOO_SMALL, "out holds fewer than 4 * blocks bytes")
     _check(lib().ocq_diag_stream_read(src.data_ptr(), src.numel(), out.data_ptr(), blocks, _stream_handle(stream)))
+
+
+def diag_window_read(src, window_bytes, passes, out, blocks, stream=None):
+    """Every one of `blocks` workgroups reads src[:window_bytes] `passes` times
+    (src: uint8 CUDA tensor; out: int32 / uint8 CUDA tensor of >= 4 * blocks
+    bytes)."""
+    import torch
+    _need(src, "src", torch.uint8, src.device)
+    if window_bytes > src.numel():
+        raise OcqError(ERR_BUFFER_TOO_SMALL, "window larger than src")
+    if out.numel() * out.element_size() < 4 * blocks:
+        raise OcqError(ERR_BUFFER_TOO_SMALL, "out holds fewer than 4 * blocks bytes")
+    _check(lib().ocq_diag_window_read(src.data_ptr(), window_bytes, passes, out.data_ptr(), blocks,
+                                      _stream_handle(stream)))
+
+
+def diag_mfma_rate(iters, out, blocks, stream=None):
+    """Launch the matrix-core rate kernel (out: float32 CUDA tensor of >= 512 *
+    blocks elements); returns the launch's floating-point operations."""
+    import torch
+    _need(out, "out", torch.float32, out.device)
+    if out.numel() < 512 * blocks:
+        raise OcqError(ERR_BUFFER_TOO_SMALL, "out holds fewer than 512 * blocks floats")
+    fl = ctypes.c_double()
+    _check(lib().ocq_diag_mfma_rate(iters, out.data_ptr(), blocks, _stream_handle(stream), ctypes.byref(fl)))
+    return fl.value
 
 
 def diag_empty(stream=None):

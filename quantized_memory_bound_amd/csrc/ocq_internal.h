@@ -38,7 +38,7 @@ struct FwdArgs {
 
 // enqueue the kernels of one forward call (kernels.hip); returns 0 or a hipError_t value
 int launch_forward(const Plan& p, const FwdArgs& a);
-// process-wide: may gate/up launches requantize h themselves (default on)
+// process-wide: may gate/up launches requantize h themselves (default off)
 void set_fused_requant(bool on);
 
 // measurement kernels (diag.hip); return 0 or a hipError_t value

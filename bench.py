@@ -245,6 +245,46 @@ def launch_floor(torch, ocq, reps=200):
     return t0.elapsed_time(t1) * 1e-3 / reps
 
 
+def vendor_gemm(args, reps=200):
+    """Context, not the block: torch's matmul (hipBLASLt) in fp16 and bf16 on
+    the workload's two GEMM shapes (M x H x 2I for gate/up, M x I x H for
+    down), plain GEMMs on random operands without the block's quantization,
+    SiLU epilogue or operand conversions.  One JSON line."""
+    import torch
+    from quantized_memory_bound_amd import inputs as I
+    cfg = I.WORKLOADS[args.workload]
+    H, Iw = cfg["hidden"], cfg["inter"]
+    M = args.M if args.M is not None else cfg["M"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    torch.manual_seed(0)
+    rows = []
+    for dt in (torch.float16, torch.bfloat16):
+        for what, k, n in (("gate/up", H, 2 * Iw), ("down", Iw, H)):
+            a = torch.randn(M, k, device=dev, dtype=dt)
+            # weights stored [N, K] as the block stores them (used transposed), or [K, N]
+            for layout in ("NK", "KN"):
+                b = torch.randn(n, k, device=dev, dtype=dt).t() if layout == "NK" else \
+                    torch.randn(k, n, device=dev, dtype=dt)
+                for _ in range(10):
+                    torch.mm(a, b)
+                torch.cuda.synchronize()
+                t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                t0.record()
+                for _ in range(reps):
+                    torch.mm(a, b)
+                t1.record()
+                torch.cuda.synchronize()
+                us = t0.elapsed_time(t1) * 1e3 / reps
+                fl = 2.0 * M * k * n
+                rows.append({"gemm": what, "dtype": str(dt).split(".")[-1], "weights": layout, "M": M, "K": k, "N": n,
+                             "us": round(us, 2), "TFLOPs": round(fl / us / 1e6, 1),
+                             "frac_f16_peak": round(fl / us / 1e6 / MFMA_F16_PEAK_TFLOPS, 4)})
+                del b
+            del a
+    print(json.dumps({"vendor_gemm": rows, "workload": args.workload, "reps": reps}))
+
+
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -273,6 +313,9 @@ def main():
                     help="1: requantize h inside the gate/up kernel where its grid fits the GPU at once")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 256 MiB copy kernel (counter calibration for rocprofv3 --pmc)")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="instead of the block: time torch's fp16 / bf16 matmul (the vendor GEMM) on the "
+                         "workload's gate/up and down shapes, for context")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -287,6 +330,8 @@ def main():
     from quantized_memory_bound_amd import ocq
 
     ocq.set_fused_requant(bool(args.fused_requant))
+    if args.vendor_gemm:
+        return vendor_gemm(args)
     if args.workload in I.STACKS:
         return run_stack(args)
     cfg = I.WORKLOADS[args.workload]

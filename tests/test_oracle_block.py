@@ -406,3 +406,44 @@ def test_tie_block_e4m3_h():
     out = O.block_reference(x_bits, wg, wu, wd, O.PREC_FP8)
     assert out["sh"][0] == np.float32(256.0)
     assert list(out["hq"][0]) == [0x78, 0x79, 0x7E]
+
+
+# ------------------------------------------------------------------ brute force on 8 x 8 outputs
+#
+# The projection step (code-domain sum, then the token and column scales)
+# against exact rational arithmetic written out as loops over every output
+# and input: for E4M3 x E4M3 and E4M3 x (E2M1 x E4M3 block scale) operands
+# the fp64 sums are exact, so only the two scale multiplications round (at
+# most one unit in the last place each).  A transposed operand, a scale on
+# the wrong axis or a dropped block scale breaks these.
+
+@pytest.mark.parametrize("kind", ["fp8", "fp4"])
+def test_projection_brute_force_8x8(kind):
+    from fractions import Fraction
+    rng = np.random.default_rng(21 if kind == "fp8" else 22)
+    T, N, K = 8, 8, 32                     # two 16-input NVFP4 blocks per row
+    a = rng.integers(0, 255, (T, K)).astype(np.uint8)
+    a[(a & 0x7F) == 0x7F] = 0x7E           # no NaN codes
+    sa = (rng.random(T) * 0.01 + 1e-4).astype(np.float32)
+    if kind == "fp8":
+        wc = rng.integers(0, 255, (N, K)).astype(np.uint8)
+        wc[(wc & 0x7F) == 0x7F] = 0x7E
+        sw = (rng.random(N) * 0.01 + 1e-4).astype(np.float32)
+        packed = (wc, sw)
+        wval = lambda n, k: Fraction(float(F.E4M3[wc[n, k]]))
+        col = lambda n: Fraction(float(sw[n]))
+    else:
+        wc = rng.integers(0, 16, (N, K)).astype(np.uint8)
+        sb = rng.integers(0x08, 0x70, (N, K // 16)).astype(np.uint8)   # positive normal E4M3 block scales
+        S = np.float32(0.00123)
+        packed = (wc, sb, S)
+        wval = lambda n, k: Fraction(float(F.E2M1[wc[n, k]])) * Fraction(float(F.E4M3[sb[n, k // 16]]))
+        col = lambda n: Fraction(float(S))
+    got = O._projection(F.dec_e4m3(a), sa, packed, kind)
+    assert got.shape == (T, N)
+    for t in range(T):
+        for n in range(N):
+            exact = sum(Fraction(float(F.E4M3[a[t, k]])) * wval(n, k) for k in range(K))
+            exact *= Fraction(float(sa[t])) * col(n)
+            ref = float(exact)
+            assert abs(got[t, n] - ref) <= 2 * 2.0 ** -52 * abs(ref) + 1e-300, (t, n, got[t, n], ref)

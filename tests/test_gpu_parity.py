@@ -66,7 +66,8 @@ def compare(g, r, prec, rows=None, what=""):
         check_codes(sel(g["hb"]), r["hb"], bf16_rank, what + " hb", bf16_near_zero(sel(g["hb"]), r["hb"]))
     else:
         check_codes(sel(g["hq"]), r["hq"], e4m3_rank, what + " hq")
-        dsh = np.abs(sel(g["sh"]).astype(np.float64) - r["sh"]) / np.maximum(r["sh"], 1e-300)
+        rsh = np.asarray(r["sh"], dtype=np.float64)   # (1e-300 is 0 in float32)
+        dsh = np.abs(sel(g["sh"]).astype(np.float64) - rsh) / np.maximum(rsh, 1e-300)
         print("%s sh: max relative difference %.2e" % (what, float(np.max(dsh)) if dsh.size else 0.0))
         np.testing.assert_allclose(sel(g["sh"]), r["sh"], rtol=SH_RTOL, atol=0, err_msg=what + " sh")
     return check_y(sel(g["y"]), r["y"], what + " y")

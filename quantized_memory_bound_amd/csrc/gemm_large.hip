@@ -108,16 +108,22 @@ __device__ __forceinline__ void lg_issue(const LgSrc<G>& src, int s, uint8_t* sl
   const size_t off_w = (size_t)c * Fmt<G::BF>::kGlobal + (size_t)u0 * 1024;
 #pragma unroll
   for (int q = 0; q < G::PW; ++q) {
-    if (q == G::PW - 1 && !full) break;
-    const int x = wave + q * G::NW;   // wave-uniform
+    constexpr bool kAll = G::BF == kB_FP8_F16 && G::A16;   // every wave issues PW loads (see lg_wait)
+    if (!kAll && q == G::PW - 1 && !full) break;
+    int x = wave + q * G::NW;   // wave-uniform
+    if (kAll) x = x < G::NU ? x : G::NU - 1;   // a duplicate load of an existing unit (the same bytes)
     __builtin_amdgcn_global_load_lds((const void*)(src.p[q] + (src.act[q] ? off_a : off_w)),
                                      (lds_void*)(slot + x * 1024), 16, 0, 0);
   }
 }
 
 // wait until at most K stages of this wave's loads are outstanding
+// (the gate/up with 16-bit activations issues PW loads on every wave, the
+// surplus ones duplicating an existing unit, so that its loads can sit
+// between MFMAs without a branch)
 template <class G, int K>
 __device__ __forceinline__ void lg_wait(bool full) {
+  if (G::BF == kB_FP8_F16 && G::A16) { wait_vm<K * G::PW>(); return; }
   if (full) wait_vm<K * G::PW>();
   else wait_vm<K * (G::PW - 1)>();
 }
@@ -189,10 +195,10 @@ __device__ __forceinline__ void lg_mfma(const LgFrag<G>& fa, const LgWFrag<G>& f
 // is converted between them, so the converts issue while the matrix core runs
 // instead of ahead of the batch.  Conversion u follows MFMA 3 (u + 2) + 1: late
 // enough for B that was read from LDS just before the batch.
-template <class G>
+template <class G, class Hook>
 __device__ __forceinline__ void lg_mfma_pipelined(const LgFrag<G>& fa, const v8h (&bh_cur)[G::TW],
                                                   const LgWFrag<G>& fb_next, int i_next, v8h (&bh_next)[G::TW],
-                                                  v4f (&acc)[G::MTW][G::TW]) {
+                                                  v4f (&acc)[G::MTW][G::TW], Hook hook) {
   static_assert(G::MTW * G::TW >= 3 * (G::TW + 2), "room to interleave the conversions");
 #pragma unroll
   for (int j = 0; j < G::MTW; ++j) {
@@ -205,6 +211,7 @@ __device__ __forceinline__ void lg_mfma_pipelined(const LgFrag<G>& fa, const v8h
         bh_next[u] = e4m3x8_to_f16((uint32_t)fb_next.b[u][2 * i_next], (uint32_t)fb_next.b[u][2 * i_next + 1]);
         asm volatile("" : "+v"(bh_next[u]));   // keep the conversion here (not sunk to its use)
       }
+      hook(k);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -273,15 +280,34 @@ __device__ __forceinline__ void lg_mainloop(const uint8_t* a, int nva, size_t a_
         lg_wait<G, G::NSTG - 2>(full);
         lds_barrier();
         lgkm_settled();
-        issue(s + G::NSTG);
+        if constexpr (!PIPE) issue(s + G::NSTG);
         lg_read_a<G>(fa[1 - cur], slot(s + 1), wm, kw, 0);
         lg_read_b<G>(fb[1 - E], slot(s + 1), wt, kw);
       }
       // fences: the compiler would otherwise sink the reads to their uses
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (PIPE) {
-        if (q == 0) lg_mfma_pipelined<G>(fa[cur], bh[0], fb[E], 1, bh[1], acc);
-        else lg_mfma_pipelined<G>(fa[cur], bh[1], fb[1 - E], 0, bh[0], acc);
+        if (q == 0) {
+          lg_mfma_pipelined<G>(fa[cur], bh[0], fb[E], 1, bh[1], acc, [](int) {});
+        } else {
+          // the loads of stage s + NSTG go between this piece's MFMAs (one
+          // after every other MFMA): issued together right after the barrier
+          // they held the matrix cores idle (about 9 CU cycles per load)
+          const int sl = s + G::NSTG < NS ? s + G::NSTG : NS - 1;
+          const int c = sl / G::SPC, u0 = (sl % G::SPC) * G::UPS;
+          const size_t off_a = (size_t)c * G::A_BLK + (size_t)u0 * G::AU * 1024;
+          const size_t off_w = (size_t)c * Fmt<G::BF>::kGlobal + (size_t)u0 * 1024;
+          uint8_t* dst = lds + (size_t)((s + G::NSTG) % G::NSTG) * G::NU * 1024;
+          lg_mfma_pipelined<G>(fa[cur], bh[1], fb[1 - E], 0, bh[0], acc, [&](int k) {
+            if (k % 2 == 0 && k / 2 < G::PW) {
+              const int q2 = k / 2;
+              const int x0 = wave + q2 * G::NW;
+              const int x = x0 < G::NU ? x0 : G::NU - 1;   // duplicate of an existing unit (same bytes)
+              __builtin_amdgcn_global_load_lds((const void*)(src.p[q2] + (src.act[q2] ? off_a : off_w)),
+                                               (lds_void*)(dst + x * 1024), 16, 0, 0);
+            }
+          });
+        }
       } else {
         lg_mfma<G>(fa[cur], fb[E], q, acc);
       }

@@ -49,8 +49,7 @@ struct Lg {
   static constexpr int AW = WM * MTW * AU;           // activation units per unit position
   static constexpr int UT = AW + RT;                 // units per unit position: activations, then weights
   static constexpr int NU = UPS * UT;                // units per stage
-  static constexpr int PW = (NU + NW - 1) / NW;      // loads per wave per stage (waves < FULL) ...
-  static constexpr int FULL = NU - (PW - 1) * NW;    // ... the others PW - 1
+  static constexpr int PW = (NU + NW - 1) / NW;      // loads per wave per stage (a surplus one repeats a unit)
   static constexpr int UPC = 4 / SUB;                // weight units per 128-input chunk
   static constexpr int SPC = UPC / UPS;              // stages per chunk
   static constexpr int UPK = UPS / KW;               // unit positions of a stage per K-wave
@@ -87,7 +86,7 @@ __device__ __forceinline__ LgSrc<G> lg_sources(const uint8_t* a, int nva, size_t
 #pragma unroll
   for (int q = 0; q < G::PW; ++q) {
     const int x0 = wave + q * G::NW;
-    const int x = x0 < G::NU ? x0 : G::NU - 1;   // the last slot of waves >= FULL is never issued
+    const int x = x0 < G::NU ? x0 : G::NU - 1;   // a surplus load slot repeats the stage's last unit
     const int uu = x / G::UT, y = x % G::UT;
     r.act[q] = y < G::AW;
     if (y < G::AW) {
@@ -100,32 +99,32 @@ __device__ __forceinline__ LgSrc<G> lg_sources(const uint8_t* a, int nva, size_t
   return r;
 }
 
-// Issue this wave's loads of stage s into `slot`.
+// Issue load q of stage s into `slot` (the stage's LDS slot).  Every wave
+// issues PW loads per stage: a surplus one repeats the stage's last unit, the
+// same bytes to the same place, so no branch depends on the wave.
 template <class G>
-__device__ __forceinline__ void lg_issue(const LgSrc<G>& src, int s, uint8_t* slot, int wave, bool full) {
+__device__ __forceinline__ void lg_issue_one(const LgSrc<G>& src, int s, uint8_t* slot, int wave, int q) {
   const int c = s / G::SPC, u0 = (s % G::SPC) * G::UPS;
   const size_t off_a = (size_t)c * G::A_BLK + (size_t)u0 * G::AU * 1024;
   const size_t off_w = (size_t)c * Fmt<G::BF>::kGlobal + (size_t)u0 * 1024;
+  int x = wave + q * G::NW;   // wave-uniform
+  x = x < G::NU ? x : G::NU - 1;
+  __builtin_amdgcn_global_load_lds((const void*)(src.p[q] + (src.act[q] ? off_a : off_w)),
+                                   (lds_void*)(slot + x * 1024), 16, 0, 0);
+}
+
+template <class G>
+__device__ __forceinline__ void lg_issue(const LgSrc<G>& src, int s, uint8_t* slot, int wave) {
 #pragma unroll
-  for (int q = 0; q < G::PW; ++q) {
-    constexpr bool kAll = G::BF == kB_FP8_F16 && G::A16;   // every wave issues PW loads (see lg_wait)
-    if (!kAll && q == G::PW - 1 && !full) break;
-    int x = wave + q * G::NW;   // wave-uniform
-    if (kAll) x = x < G::NU ? x : G::NU - 1;   // a duplicate load of an existing unit (the same bytes)
-    __builtin_amdgcn_global_load_lds((const void*)(src.p[q] + (src.act[q] ? off_a : off_w)),
-                                     (lds_void*)(slot + x * 1024), 16, 0, 0);
-  }
+  for (int q = 0; q < G::PW; ++q) lg_issue_one<G>(src, s, slot, wave, q);
 }
 
 // wait until at most K stages of this wave's loads are outstanding
-// (the gate/up with 16-bit activations issues PW loads on every wave, the
-// surplus ones duplicating an existing unit, so that its loads can sit
-// between MFMAs without a branch)
+// (every wave issues PW loads per stage, the surplus ones repeating an
+// existing unit, so that the loads can sit between MFMAs without a branch)
 template <class G, int K>
-__device__ __forceinline__ void lg_wait(bool full) {
-  if (G::BF == kB_FP8_F16 && G::A16) { wait_vm<K * G::PW>(); return; }
-  if (full) wait_vm<K * G::PW>();
-  else wait_vm<K * (G::PW - 1)>();
+__device__ __forceinline__ void lg_wait() {
+  wait_vm<K * G::PW>();
 }
 
 // Operand registers of one piece of a wave's work: its MTW activation
@@ -159,16 +158,20 @@ __device__ __forceinline__ void lg_read_b(LgWFrag<G>& f, const uint8_t* base, in
 // sub-steps (bytes 0-7, 8-15) or bf16 values of one; 16-bit activations hold
 // one sub-step per unit, E4M3 ones two like the weights.  Both operands order
 // the inputs of a sub-step alike, so each sub-step is one MFMA over 32 inputs.
-template <class G>
+// hook(k) runs after the piece's k-th MFMA (it issues the stage's loads).
+template <class G, class Hook>
 __device__ __forceinline__ void lg_mfma(const LgFrag<G>& fa, const LgWFrag<G>& fb, int qa,
-                                        v4f (&acc)[G::MTW][G::TW]) {
+                                        v4f (&acc)[G::MTW][G::TW], Hook hook) {
   if constexpr (G::BF == kB_BF16) {
 #pragma unroll
     for (int j = 0; j < G::MTW; ++j) {
       const v8bf av = __builtin_bit_cast(v8bf, fa.a[j]);
 #pragma unroll
-      for (int t = 0; t < G::TW; ++t)
+      for (int t = 0; t < G::TW; ++t) {
         acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(v8bf, fb.b[t]), acc[j][t], 0, 0, 0);
+        hook(j * G::TW + t);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   } else {
 #pragma unroll
@@ -183,8 +186,10 @@ __device__ __forceinline__ void lg_mfma(const LgFrag<G>& fa, const LgWFrag<G>& f
         if constexpr (G::A16) av = __builtin_bit_cast(v8h, fa.a[j]);
         else av = e4m3x8_to_f16((uint32_t)fa.a[j][2 * i], (uint32_t)fa.a[j][2 * i + 1]);
 #pragma unroll
-        for (int t = 0; t < G::TW; ++t)
+        for (int t = 0; t < G::TW; ++t) {
           acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv[t], acc[j][t], 0, 0, 0);
+          hook((ii * G::MTW + j) * G::TW + t);
+        }
       }
     }
   }
@@ -243,15 +248,14 @@ __device__ __forceinline__ void lg_mainloop(const uint8_t* a, int nva, size_t a_
   constexpr int NP = G::A16 ? G::SUB : 1;   // pieces per stage
   static_assert(G::UPK == 1, "one unit position per wave and stage");
   const int lane = threadIdx.x & 63;
-  const bool full = wave < G::FULL;
   auto slot = [&](int s) { return lds + (size_t)(s % G::NSTG) * G::NU * 1024 + lane * 16; };
   const LgSrc<G> src = lg_sources<G>(a, nva, a_mt, w, w_tile, wave);
   auto issue = [&](int s) {
-    lg_issue<G>(src, s < NS ? s : NS - 1, lds + (size_t)(s % G::NSTG) * G::NU * 1024, wave, full);
+    lg_issue<G>(src, s < NS ? s : NS - 1, lds + (size_t)(s % G::NSTG) * G::NU * 1024, wave);
   };
 #pragma unroll
   for (int s = 0; s < G::NSTG; ++s) issue(s);
-  lg_wait<G, G::NSTG - 1>(full);
+  lg_wait<G, G::NSTG - 1>();
   lds_barrier();
   // lgkmcnt(0) through the builtin as well: the compiler's wait tracking
   // does not see the one inside the barrier, and would otherwise treat
@@ -277,39 +281,27 @@ __device__ __forceinline__ void lg_mainloop(const uint8_t* a, int nva, size_t a_
       if (q + 1 < NP) {
         lg_read_a<G>(fa[1 - cur], slot(s), wm, kw, q + 1);
       } else {   // also after the last stage: no branch, so no conservative wait at a join
-        lg_wait<G, G::NSTG - 2>(full);
+        lg_wait<G, G::NSTG - 2>();
         lds_barrier();
         lgkm_settled();
-        if constexpr (!PIPE) issue(s + G::NSTG);
         lg_read_a<G>(fa[1 - cur], slot(s + 1), wm, kw, 0);
         lg_read_b<G>(fb[1 - E], slot(s + 1), wt, kw);
       }
       // fences: the compiler would otherwise sink the reads to their uses
       __builtin_amdgcn_sched_barrier(0);
+      // After the barrier, the loads of stage s + NSTG go between this
+      // piece's MFMAs, one after every other MFMA: issued together right after
+      // the barrier they held the matrix cores idle (about 9 CU cycles each).
+      const int sl = s + G::NSTG < NS ? s + G::NSTG : NS - 1;
+      uint8_t* dst = lds + (size_t)((s + G::NSTG) % G::NSTG) * G::NU * 1024;
+      auto loads = [&](int k) {
+        if (q + 1 == NP && k % 2 == 0 && k / 2 < G::PW) lg_issue_one<G>(src, sl, dst, wave, k / 2);
+      };
       if constexpr (PIPE) {
-        if (q == 0) {
-          lg_mfma_pipelined<G>(fa[cur], bh[0], fb[E], 1, bh[1], acc, [](int) {});
-        } else {
-          // the loads of stage s + NSTG go between this piece's MFMAs (one
-          // after every other MFMA): issued together right after the barrier
-          // they held the matrix cores idle (about 9 CU cycles per load)
-          const int sl = s + G::NSTG < NS ? s + G::NSTG : NS - 1;
-          const int c = sl / G::SPC, u0 = (sl % G::SPC) * G::UPS;
-          const size_t off_a = (size_t)c * G::A_BLK + (size_t)u0 * G::AU * 1024;
-          const size_t off_w = (size_t)c * Fmt<G::BF>::kGlobal + (size_t)u0 * 1024;
-          uint8_t* dst = lds + (size_t)((s + G::NSTG) % G::NSTG) * G::NU * 1024;
-          lg_mfma_pipelined<G>(fa[cur], bh[1], fb[1 - E], 0, bh[0], acc, [&](int k) {
-            if (k % 2 == 0 && k / 2 < G::PW) {
-              const int q2 = k / 2;
-              const int x0 = wave + q2 * G::NW;
-              const int x = x0 < G::NU ? x0 : G::NU - 1;   // duplicate of an existing unit (same bytes)
-              __builtin_amdgcn_global_load_lds((const void*)(src.p[q2] + (src.act[q2] ? off_a : off_w)),
-                                               (lds_void*)(dst + x * 1024), 16, 0, 0);
-            }
-          });
-        }
+        if (q == 0) lg_mfma_pipelined<G>(fa[cur], bh[0], fb[E], 1, bh[1], acc, loads);
+        else lg_mfma_pipelined<G>(fa[cur], bh[1], fb[1 - E], 0, bh[0], acc, loads);
       } else {
-        lg_mfma<G>(fa[cur], fb[E], q, acc);
+        lg_mfma<G>(fa[cur], fb[E], q, acc, loads);
       }
       __builtin_amdgcn_sched_barrier(0);
       lgkm_settled();

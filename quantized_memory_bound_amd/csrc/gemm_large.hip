@@ -432,7 +432,7 @@ __global__ __launch_bounds__(G::THREADS) void lg_gateup(GateUpArgs g) {
     float amax[2] = {0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < G::TW; ++t) {
-      const int tile = tile0 + t, n = tile * 8 + c;
+      const int tile = tile0 + t;
       const v4f& v = acc[j][t];
       const float p0 = dpp<0x128>(lo ? v[1] : v[0]);
       const float p1 = dpp<0x128>(lo ? v[3] : v[2]);

@@ -187,8 +187,8 @@ __device__ __forceinline__ v2u e4m3x8_quot(const float (&v)[8], float s, float r
 __device__ __forceinline__ uint32_t e4m3_quot1(float v, float s, float rcp) {
   float q = v * rcp;
   const float t = fabsf(q) * 512.0f;
-  const bool near = ((t < 8.0f) & (fabsf(__builtin_amdgcn_fractf(t) - 0.5f) < 0x1p-19f)) |
-                    ((__float_as_uint(q) & 0xFFFFFu) - 0x7FFFDu <= 6u);
+  const bool near = (((int)(t < 8.0f) & (int)(fabsf(__builtin_amdgcn_fractf(t) - 0.5f) < 0x1p-19f)) |
+                     (int)((__float_as_uint(q) & 0xFFFFFu) - 0x7FFFDu <= 6u)) != 0;   // no branch
   if (near) q = v / s;
   q = __builtin_amdgcn_fmed3f(q, -448.0f, 448.0f);
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q, 0.0f, 0, false) & 0xFFu;

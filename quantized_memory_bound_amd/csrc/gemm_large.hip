@@ -198,21 +198,21 @@ __device__ __forceinline__ void lg_mfma(const LgFrag<G>& fa, const LgWFrag<G>& f
 // Gate/up with 16-bit activations: the MFMAs of one piece take B already in
 // fp16 (bh_cur) and the E4M3 B of the next piece (sub-step i_next of fb_next)
 // is converted between them, so the converts issue while the matrix core runs
-// instead of ahead of the batch.  Conversion u follows MFMA 3 (u + 2) + 1: late
-// enough for B that was read from LDS just before the batch.
+// instead of ahead of the batch.  Conversion u follows MFMA 12 + 3 u: late
+// enough for B read from LDS during the first MFMAs of the batch.
 template <class G, class Hook>
 __device__ __forceinline__ void lg_mfma_pipelined(const LgFrag<G>& fa, const v8h (&bh_cur)[G::TW],
                                                   const LgWFrag<G>& fb_next, int i_next, v8h (&bh_next)[G::TW],
                                                   v4f (&acc)[G::MTW][G::TW], Hook hook) {
-  static_assert(G::MTW * G::TW >= 3 * (G::TW + 2), "room to interleave the conversions");
+  static_assert(G::MTW * G::TW >= 12 + 3 * G::TW - 2, "room to interleave the conversions");
 #pragma unroll
   for (int j = 0; j < G::MTW; ++j) {
 #pragma unroll
     for (int t = 0; t < G::TW; ++t) {
       acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, fa.a[j]), bh_cur[t], acc[j][t], 0, 0, 0);
       const int k = j * G::TW + t;
-      if (k % 3 == 2 && k / 3 >= 2 && k / 3 - 2 < G::TW) {
-        const int u = k / 3 - 2;
+      if (k >= 12 && k % 3 == 0 && (k - 12) / 3 < G::TW) {
+        const int u = (k - 12) / 3;
         bh_next[u] = e4m3x8_to_f16((uint32_t)fb_next.b[u][2 * i_next], (uint32_t)fb_next.b[u][2 * i_next + 1]);
         asm volatile("" : "+v"(bh_next[u]));   // keep the conversion here (not sunk to its use)
       }
@@ -237,10 +237,9 @@ __device__ __forceinline__ void lgkm_settled() { __builtin_amdgcn_s_waitcnt(0xC0
 // last are clamped (the loads repeat the last stage into a slot whose reads
 // are over, and the reads after the last stage fetch registers nobody uses),
 // so every wave has the same number of loads outstanding at each wait.
-// Register ping-pong: the LDS reads of the next piece are issued before the
-// MFMAs of the current one, so after each barrier the matrix cores have work
-// that does not depend on the reads just issued.  On return no load of the
-// wave is outstanding.
+// Register ping-pong: the LDS reads of the next piece are issued among the
+// MFMAs of the current one, which never wait for them.  On return no load
+// of the wave is outstanding.
 template <class G>
 __device__ __forceinline__ void lg_mainloop(const uint8_t* a, int nva, size_t a_mt, const uint8_t* w, size_t w_tile,
                                             int NS, uint8_t* lds, int wave, int wm, int wt, int kw,
@@ -278,24 +277,30 @@ __device__ __forceinline__ void lg_mainloop(const uint8_t* a, int nva, size_t a_
 #pragma unroll
     for (int q = 0; q < NP; ++q) {
       const int cur = NP == 2 ? q : E;
-      if (q + 1 < NP) {
-        lg_read_a<G>(fa[1 - cur], slot(s), wm, kw, q + 1);
-      } else {   // also after the last stage: no branch, so no conservative wait at a join
+      if (q + 1 == NP) {   // also after the last stage: no branch, so no conservative wait at a join
         lg_wait<G, G::NSTG - 2>();
         lds_barrier();
         lgkm_settled();
-        lg_read_a<G>(fa[1 - cur], slot(s + 1), wm, kw, 0);
-        lg_read_b<G>(fb[1 - E], slot(s + 1), wt, kw);
       }
+      // the next piece's LDS reads, one after each of the first MFMAs
+      const uint8_t* rbase = slot(q + 1 < NP ? s : s + 1);
+      const int rq = q + 1 < NP ? q + 1 : 0;
+      constexpr int NR = G::MTW + G::TW;
       // fences: the compiler would otherwise sink the reads to their uses
       __builtin_amdgcn_sched_barrier(0);
-      // After the barrier, the loads of stage s + NSTG go between this
-      // piece's MFMAs, one after every other MFMA: issued together right after
-      // the barrier they held the matrix cores idle (about 9 CU cycles each).
+      // The next piece's LDS reads and, after the barrier, the loads of stage
+      // s + NSTG go between this piece's MFMAs (reads after the first MFMAs,
+      // loads after every other one): issued together ahead of the batch they
+      // held the matrix cores idle (about 9 CU cycles per load).
       const int sl = s + G::NSTG < NS ? s + G::NSTG : NS - 1;
       uint8_t* dst = lds + (size_t)((s + G::NSTG) % G::NSTG) * G::NU * 1024;
       auto loads = [&](int k) {
-        if (q + 1 == NP && k % 2 == 0 && k / 2 < G::PW) lg_issue_one<G>(src, sl, dst, wave, k / 2);
+        if (k < G::MTW) {
+          fa[1 - cur].a[k] = *(const v4i*)(rbase + (size_t)kw * G::UT * 1024 + (size_t)((wm * G::MTW + k) * G::AU + rq) * 1024);
+        } else if (q + 1 == NP && k < NR) {
+          fb[1 - E].b[k - G::MTW] = *(const v4i*)(rbase + (size_t)kw * G::UT * 1024 + (size_t)(G::AW + wt * G::TW + k - G::MTW) * 1024);
+        }
+        if (q + 1 == NP && k % 2 == 1 && k / 2 < G::PW) lg_issue_one<G>(src, sl, dst, wave, k / 2);
       };
       if constexpr (PIPE) {
         if (q == 0) lg_mfma_pipelined<G>(fa[cur], bh[0], fb[E], 1, bh[1], acc, loads);

@@ -75,3 +75,30 @@ def test_permutation_pins_catch(name, monkeypatch):
             except (AssertionError, ValueError, IndexError):
                 caught += 1
     assert caught > 0, "planted mistake %s passes every permutation pin" % name
+
+
+# mistakes in how the block composes its steps: caught by the lossless-grid
+# pins (every quantization exact, so the block must equal the textbook MLP)
+COMPOSE_PLANTS = {
+    # SiLU applied to the up projection instead of the gate
+    "silu_on_up": ("h = silu(G) * U", "h = silu(U) * G"),
+    # the gate projection without the token scale
+    "gate_without_token_scale": ('G = _projection(X, sx, packed["gate"], kind_gu)',
+                                 'G = _projection(X, np.ones_like(sx), packed["gate"], kind_gu)'),
+    # the NVFP4 per-tensor scale dropped
+    "nvfp4_tensor_scale_dropped": ("return acc * a_scale.astype(np.float64)[:, None] * np.float64(w_packed[2])",
+                                   "return acc * a_scale.astype(np.float64)[:, None]"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(COMPOSE_PLANTS))
+def test_lossless_pins_catch(name, monkeypatch):
+    monkeypatch.setattr(T, "O", _planted(*COMPOSE_PLANTS[name]))
+    caught = 0
+    for pin in (T.test_lossless_fp8_block_equals_textbook_mlp, T.test_lossless_bf16_down_equals_textbook,
+                T.test_lossless_nvfp4_block):
+        try:
+            pin(0)
+        except AssertionError:
+            caught += 1
+    assert caught > 0, "planted mistake %s passes the lossless-grid pins" % name

@@ -46,7 +46,8 @@ struct Lg {
   static constexpr int TW = RT / WT;                 // weight tiles per wave
   static constexpr int SUB = BF == kB_BF16 ? 1 : 2;  // MFMA sub-steps (32 inputs each) per weight unit
   static constexpr int AU = A16 ? SUB : 1;           // activation units per weight unit
-  static constexpr int AW = WM * MTW * AU;           // activation units per unit position
+  static constexpr int AW = RM * AU;                 // activation units per unit position (a wave's
+                                                     // m-tiles past RM read the last one)
   static constexpr int UT = AW + RT;                 // units per unit position: activations, then weights
   static constexpr int NU = UPS * UT;                // units per stage
   static constexpr int PW = (NU + NW - 1) / NW;      // loads per wave per stage (a surplus one repeats a unit)
@@ -58,7 +59,9 @@ struct Lg {
   static constexpr int THREADS = 64 * NW;
   static_assert(BF == kB_FP8_F16 || (BF == kB_BF16 && A16), "formats");
   static_assert(RT % WT == 0, "weight tiles split evenly over the wave columns");
-  static_assert(UPC % UPS == 0 && UPS % KW == 0 && SPC % 2 == 0, "stage and K-wave split of a chunk");
+  static_assert(UPC % UPS == 0 && UPS % KW == 0, "stage and K-wave split of a chunk");
+  static constexpr int NPU = A16 ? SUB : 1;          // pieces (MFMA batches) per unit position
+  static constexpr int NP = NPU * UPK;               // pieces per stage
   static_assert(NSTG >= 2 && PW >= 2 && (NSTG - 1) * PW < 64, "outstanding loads within the vmcnt range");
   static_assert((KW - 1) * WM * WT * MTW * TW * 1024 <= LDS, "reduction fits the ring");
   static_assert(LDS <= 160 * 1024, "LDS of one CU");
@@ -139,19 +142,31 @@ struct LgWFrag {
   v4i b[G::TW];
 };
 
-// LDS reads of piece qa of this wave's unit position in the stage at `base`
-// (lane offset included)
+// LDS offsets (lane part excluded) in a stage slot: activation unit of the
+// wave's m-tile j (wave row wm; an m-tile slot past RM reads the last m-tile,
+// its results are dropped) for sub-step qa, and weight unit of the wave's
+// tile t (wave column wt), both of the stage's unit position up
 template <class G>
-__device__ __forceinline__ void lg_read_a(LgFrag<G>& f, const uint8_t* base, int wm, int kw, int qa) {
-  const uint8_t* ub = base + (size_t)kw * G::UT * 1024;
-#pragma unroll
-  for (int j = 0; j < G::MTW; ++j) f.a[j] = *(const v4i*)(ub + (size_t)((wm * G::MTW + j) * G::AU + qa) * 1024);
+__device__ __forceinline__ int lg_a_unit(int up, int wm, int j, int qa) {
+  const int mt = wm * G::MTW + j < G::RM ? wm * G::MTW + j : G::RM - 1;
+  return ((up * G::UT + mt * G::AU) + qa) * 1024;
 }
 template <class G>
-__device__ __forceinline__ void lg_read_b(LgWFrag<G>& f, const uint8_t* base, int wt, int kw) {
-  const uint8_t* ub = base + (size_t)kw * G::UT * 1024;
+__device__ __forceinline__ int lg_b_unit(int up, int wt, int t) {
+  return (up * G::UT + G::AW + wt * G::TW + t) * 1024;
+}
+
+// LDS reads of sub-step qa of unit position up in the stage at `base` (lane
+// offset included)
+template <class G>
+__device__ __forceinline__ void lg_read_a(LgFrag<G>& f, const uint8_t* base, int up, int wm, int qa) {
 #pragma unroll
-  for (int t = 0; t < G::TW; ++t) f.b[t] = *(const v4i*)(ub + (size_t)(G::AW + wt * G::TW + t) * 1024);
+  for (int j = 0; j < G::MTW; ++j) f.a[j] = *(const v4i*)(base + lg_a_unit<G>(up, wm, j, qa));
+}
+template <class G>
+__device__ __forceinline__ void lg_read_b(LgWFrag<G>& f, const uint8_t* base, int up, int wt) {
+#pragma unroll
+  for (int t = 0; t < G::TW; ++t) f.b[t] = *(const v4i*)(base + lg_b_unit<G>(up, wt, t));
 }
 
 // MFMAs of one piece.  A lane's 16 B of a weight unit: E4M3 codes of two
@@ -231,12 +246,16 @@ __device__ __forceinline__ void lg_mfma_pipelined(const LgFrag<G>& fa, const v8h
 // lets the reads of the next piece overlap the MFMAs of the current one.
 __device__ __forceinline__ void lgkm_settled() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-// acc over all NS stages (NS even).  All NSTG slots are filled up front;
-// after the barrier of stage s + 1 every wave has finished its LDS reads of
-// stage s, so stage s + NSTG goes into that slot.  Stage indices past the
-// last are clamped (the loads repeat the last stage into a slot whose reads
-// are over, and the reads after the last stage fetch registers nobody uses),
-// so every wave has the same number of loads outstanding at each wait.
+// acc over all NS stages (NS even).  All NSTG slots are filled up front.  A
+// stage holds UPK unit positions per K-wave, each processed in NPU pieces
+// (MFMA batches); the workgroup barrier sits at the start of a stage's last
+// piece: by then every wave has finished its LDS reads of the stage (the
+// last piece's operands were read during the piece before), so stage
+// s + NSTG goes into that slot, and the loads of stage s + 1 have landed, so
+// the last piece reads the first operands of stage s + 1.  Stage indices past
+// the last are clamped (the loads repeat the last stage into a slot whose
+// reads are over, and the reads after the last stage fetch registers nobody
+// uses), so every wave has the same number of loads outstanding at each wait.
 // Register ping-pong: the LDS reads of the next piece are issued among the
 // MFMAs of the current one, which never wait for them.  On return no load
 // of the wave is outstanding.
@@ -244,8 +263,8 @@ template <class G>
 __device__ __forceinline__ void lg_mainloop(const uint8_t* a, int nva, size_t a_mt, const uint8_t* w, size_t w_tile,
                                             int NS, uint8_t* lds, int wave, int wm, int wt, int kw,
                                             v4f (&acc)[G::MTW][G::TW]) {
-  constexpr int NP = G::A16 ? G::SUB : 1;   // pieces per stage
-  static_assert(G::UPK == 1, "one unit position per wave and stage");
+  constexpr int NP = G::NP, NPU = G::NPU;
+  static_assert(NP == 1 || NP % 2 == 0, "operand buffers alternate with the pieces or the stages");
   const int lane = threadIdx.x & 63;
   auto slot = [&](int s) { return lds + (size_t)(s % G::NSTG) * G::NU * 1024 + lane * 16; };
   const LgSrc<G> src = lg_sources<G>(a, nva, a_mt, w, w_tile, wave);
@@ -262,21 +281,30 @@ __device__ __forceinline__ void lg_mainloop(const uint8_t* a, int nva, size_t a_
   __builtin_amdgcn_s_waitcnt(0xC07F);
   LgFrag<G> fa[2];
   LgWFrag<G> fb[2];
-  lg_read_a<G>(fa[0], slot(0), wm, kw, 0);
-  lg_read_b<G>(fb[0], slot(0), wt, kw);
+  lg_read_a<G>(fa[0], slot(0), kw * G::UPK, wm, 0);
+  lg_read_b<G>(fb[0], slot(0), kw * G::UPK, wt);
   constexpr bool PIPE = G::BF == kB_FP8_F16 && G::A16;
   v8h bh[2][G::TW];
   if constexpr (PIPE) {
 #pragma unroll
     for (int t = 0; t < G::TW; ++t) bh[0][t] = e4m3x8_to_f16((uint32_t)fb[0].b[t][0], (uint32_t)fb[0].b[t][1]);
   }
-  // one stage with B buffer E (compile-time), A buffers fixed per piece when
-  // a stage has two pieces, else alternating with the stage
+  // MFMAs of a piece, and the spacing of the stage's loads between those of
+  // its last piece
+  constexpr int NM = G::MTW * G::TW * (G::A16 ? 1 : G::SUB);
+  constexpr int LSTEP = 2 * G::PW <= NM ? 2 : 1;
+  static_assert(LSTEP * G::PW <= NM, "every load of a stage between two MFMAs of its last piece");
+  // one stage; E = s % 2 (compile-time)
   auto stage = [&](int s, auto ec) {
     constexpr int E = decltype(ec)::value;
 #pragma unroll
     for (int q = 0; q < NP; ++q) {
-      const int cur = NP == 2 ? q : E;
+      const int up = q / NPU, qa = q % NPU;                    // this piece: unit position, sub-step
+      const int qn = q + 1 < NP ? q + 1 : 0;                   // the next piece (this stage or the next)
+      const int upn = qn / NPU, qan = qn % NPU;
+      const bool newu = qan == 0;                              // ... starts a unit position
+      const int cur = NP % 2 == 0 ? q % 2 : E;                 // A buffers: by piece, or by stage
+      const int bcur = (E * G::UPK + up) % 2, bnext = (E * G::UPK + up + 1) % 2;   // B buffers: by unit position
       if (q + 1 == NP) {   // also after the last stage: no branch, so no conservative wait at a join
         lg_wait<G, G::NSTG - 2>();
         lds_barrier();
@@ -284,31 +312,37 @@ __device__ __forceinline__ void lg_mainloop(const uint8_t* a, int nva, size_t a_
       }
       // the next piece's LDS reads, one after each of the first MFMAs
       const uint8_t* rbase = slot(q + 1 < NP ? s : s + 1);
-      const int rq = q + 1 < NP ? q + 1 : 0;
+      const int rup = kw * G::UPK + upn;
       constexpr int NR = G::MTW + G::TW;
       // fences: the compiler would otherwise sink the reads to their uses
       __builtin_amdgcn_sched_barrier(0);
       // The next piece's LDS reads and, after the barrier, the loads of stage
       // s + NSTG go between this piece's MFMAs (reads after the first MFMAs,
-      // loads after every other one): issued together ahead of the batch they
-      // held the matrix cores idle (about 9 CU cycles per load).
+      // loads after every LSTEP-th one): issued together ahead of the batch
+      // they held the matrix cores idle (about 9 CU cycles per load).
       const int sl = s + G::NSTG < NS ? s + G::NSTG : NS - 1;
       uint8_t* dst = lds + (size_t)((s + G::NSTG) % G::NSTG) * G::NU * 1024;
       auto loads = [&](int k) {
         if (k < G::MTW) {
-          fa[1 - cur].a[k] = *(const v4i*)(rbase + (size_t)kw * G::UT * 1024 + (size_t)((wm * G::MTW + k) * G::AU + rq) * 1024);
-        } else if (q + 1 == NP && k < NR) {
-          fb[1 - E].b[k - G::MTW] = *(const v4i*)(rbase + (size_t)kw * G::UT * 1024 + (size_t)(G::AW + wt * G::TW + k - G::MTW) * 1024);
+          fa[1 - cur].a[k] = *(const v4i*)(rbase + lg_a_unit<G>(rup, wm, k, qan));
+        } else if (newu && k < NR) {
+          fb[bnext].b[k - G::MTW] = *(const v4i*)(rbase + lg_b_unit<G>(rup, wt, k - G::MTW));
         }
-        if (q + 1 == NP && k % 2 == 1 && k / 2 < G::PW) lg_issue_one<G>(src, sl, dst, wave, k / 2);
+        if (q + 1 == NP && k % LSTEP == LSTEP - 1 && k / LSTEP < G::PW) lg_issue_one<G>(src, sl, dst, wave, k / LSTEP);
       };
+      // gate/up: the wave's MFMA batch at raised priority, so that of the two
+      // waves on a SIMD the one issuing matrix work keeps the issue slots
+      // (M=832 gate/up 149.8 -> 146.6 us in kernel traces of alternating runs
+      // on one box; no gain for the BF16 down projection, whose batches are
+      // shorter: 14 MFMAs against 21)
+      if constexpr (PIPE) __builtin_amdgcn_s_setprio(1);
       if constexpr (PIPE) {
-        if (q == 0) lg_mfma_pipelined<G>(fa[cur], bh[0], fb[E], 1, bh[1], acc, loads);
-        else lg_mfma_pipelined<G>(fa[cur], bh[1], fb[1 - E], 0, bh[0], acc, loads);
+        lg_mfma_pipelined<G>(fa[cur], bh[q % 2], fb[newu ? bnext : bcur], qan, bh[(q + 1) % 2], acc, loads);
       } else {
-        lg_mfma<G>(fa[cur], fb[E], q, acc, loads);
+        lg_mfma<G>(fa[cur], fb[bcur], qa, acc, loads);
       }
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (PIPE) __builtin_amdgcn_s_setprio(0);
       lgkm_settled();
     }
   };
@@ -539,12 +573,20 @@ hipError_t lg_launch(void (*fn)(Arg), int grid, const Arg& arg, hipStream_t st, 
 }
 
 // gate/up: 13 m-tiles x 12 tiles per workgroup; 2 x 4 waves of 7 m-tiles x 3
-// tiles, one weight unit position per stage (64 inputs), three stages (120 KB)
+// tiles.  A stage is one whole chunk (two weight unit positions, 128 inputs,
+// 76 KB) in a two-stage ring, so that each workgroup barrier is shared by
+// twice the matrix work of a one-unit stage (the per-stage cost of the
+// barrier, its wait for the slower wave of each SIMD and the restart was
+// about a third of the stage); with an odd chunk count, one unit position
+// per stage in a three-stage ring.
+using GUL2 = Lg<kB_FP8_F16, true, kLgRM, kLgRT1, 2, kLgWT1, 1, 2, 2>;
 using GUL = Lg<kB_FP8_F16, true, kLgRM, kLgRT1, 2, kLgWT1, 1, 1, 3>;
 // down: 7 m-tiles x 8 tiles per workgroup (112 rows x 128 columns: more
 // multiply-adds per staged byte than 208 x 64); 1 x 4 waves of 7 m-tiles x 2
 // tiles, each pair of K-waves splitting the two unit positions of a stage (64
-// inputs), four stages (120 KB)
+// inputs), four stages (120 KB).  Whole-chunk stages in a two-stage ring were
+// slower here (M=832: 94 -> 127 us): the weight loads, which come from HBM,
+// then have one short stage to land instead of three.
 using GDL = Lg<kB_BF16, true, kLgRM2, kLgRT2, 1, 4, 2, 2, 4>;
 
 }  // namespace
@@ -552,11 +594,15 @@ using GDL = Lg<kB_BF16, true, kLgRM2, kLgRT2, 1, 4, 2, 2, 4>;
 hipError_t launch_gateup_large(const Plan& p, const GateUpArgs& g, hipStream_t st, const LaunchEvents& ev) {
   if ((p.inter / 8) % GUL::RT || p.hidden % kChunk) return hipErrorInvalidValue;
   const int grid = p.n_mblocks * ((p.inter / 8) / GUL::RT);
+  // stages are processed in pairs: a whole-chunk stage needs an even chunk count
+  const bool whole = (p.hidden / kChunk) % 2 == 0;
   if (p.prec == kFP8DownBF16) {
-    static std::atomic<uint64_t> lds_set{0};
+    static std::atomic<uint64_t> lds_set{0}, lds_set2{0};
+    if (whole) return lg_launch<GUL2>(lg_gateup<GUL2, true>, grid, g, st, lds_set2, ev, GUL2::LDS + kLgScaleBytes);
     return lg_launch<GUL>(lg_gateup<GUL, true>, grid, g, st, lds_set, ev, GUL::LDS + kLgScaleBytes);
   }
-  static std::atomic<uint64_t> lds_set{0};
+  static std::atomic<uint64_t> lds_set{0}, lds_set2{0};
+  if (whole) return lg_launch<GUL2>(lg_gateup<GUL2, false>, grid, g, st, lds_set2, ev, GUL2::LDS + kLgScaleBytes);
   return lg_launch<GUL>(lg_gateup<GUL, false>, grid, g, st, lds_set, ev, GUL::LDS + kLgScaleBytes);
 }
 

@@ -271,6 +271,26 @@ ocq_status ocq_diag_empty(void* stream);
 ocq_status ocq_diag_mfma_dot(int form, const void* a_dev, const void* b_dev, int M, int N, int K, float* c_dev,
                              void* stream);
 
+/* Per-wave phase stamps of the GEMM main loops, for finding where a kernel's
+ * time goes (the roofline method of "Why decoding dominates latency" in the
+ * post, applied inside one kernel).  Only a library built with
+ * `python -m quantized_memory_bound_amd.build --phase-stamps`
+ * (libocq_phases.so) records them; the plain library returns
+ * OCQ_ERR_UNSUPPORTED.  Copies, synchronously, the table of the last launch
+ * of the chosen kernel family into host_out (caller-owned host memory of at
+ * least the stated bytes, else OCQ_ERR_BUFFER_TOO_SMALL), as uint64 values
+ * for workgroups 0..511:
+ *   kernel 0, LDS-tiled GEMMs (524,288 B): [gate/up, down][workgroup][wave
+ *     0..7][load wait, barrier, MFMA batches, LDS-read wait after the batches,
+ *     whole loop, stage count], totals in shader-clock ticks;
+ *   kernel 1, producer/consumer gate/up (393,216 B): [workgroup][wave 0..11:
+ *     8 consumers, then 4 producers][entry, consumer loop start, loop end,
+ *     partial tiles stored, wave end, 0, 0, 0], 100 MHz time stamps (the
+ *     consumer-only fields are 0 for producers).
+ * OCQ_ERR_INVALID_ARG for another kernel value or a null pointer,
+ * OCQ_ERR_DEVICE if the copy fails. */
+ocq_status ocq_diag_phase_stamps(int kernel, void* host_out, size_t bytes);
+
 /* Where the per-token requantization of h runs (process-wide; default 0).
  * 1: inside the gate/up kernel whenever its whole grid can be resident at
  * once (an occupancy check on the host before each launch): h stays in

@@ -14,6 +14,23 @@
 #include "gemm_core.h"
 
 namespace ocq {
+
+#ifdef OCQ_PHASE_STAMPS
+// Time stamps (100 MHz clock, s_memrealtime) of the last launch of the
+// producer/consumer gate/up, built only with OCQ_PHASE_STAMPS:
+// [workgroup < 512][wave: 8 consumers, then 4 producers][entry, consumer loop
+// start, loop end, K halves' partial tiles stored, wave end, -, -, -].
+__device__ uint64_t g_pc_phases[kPhaseWGs][12][8];
+static_assert(sizeof(g_pc_phases) == kPcPhaseBytes, "layout stated in ocq_internal.h");
+__device__ __forceinline__ void pc_stamp(int wave, int i) {
+  const uint64_t t = __builtin_amdgcn_s_memrealtime();
+  if ((threadIdx.x & 63) == 0 && blockIdx.x < kPhaseWGs) g_pc_phases[blockIdx.x][wave][i] = t;
+}
+#define OCQ_PC_STAMP(w, i) pc_stamp(w, i)
+#else
+#define OCQ_PC_STAMP(w, i)
+#endif
+
 namespace {
 
 // Epilogue operands of one lane, loaded together before they are used:
@@ -408,6 +425,7 @@ __device__ __forceinline__ void pc_consumer(const GateUpArgs& g, uint8_t* lds, i
   }
   // fp16 weights of two sub-steps: the next one is read while the current
   // one's MFMAs run
+  OCQ_PC_STAMP(wave, 1);
   v8h bq[2][T];
 #pragma unroll
   for (int k = 0; k < P::NK; ++k) {
@@ -444,6 +462,7 @@ __device__ __forceinline__ void pc_consumer(const GateUpArgs& g, uint8_t* lds, i
   // Epilogue: every partial tile to LDS at once ([wave][m-tile][tile][lane],
   // one barrier), then the wave that owns m-tile q sums its two K halves
   // (wave 2 ms, then 2 ms + 1) tile by tile.
+  OCQ_PC_STAMP(wave, 2);
   lds_barrier();   // every consumer is done with the weights; the ring is reused
   float amax[Q][2];
 #pragma unroll
@@ -455,6 +474,7 @@ __device__ __forceinline__ void pc_consumer(const GateUpArgs& g, uint8_t* lds, i
 #pragma unroll
     for (int t = 0; t < T; ++t) red[((wave * 4 + j) * T + t) * 64 + lane] = acc[j][t];
   lds_barrier();
+  OCQ_PC_STAMP(wave, 3);
 #pragma unroll
   for (int jq = 0; jq < Q; ++jq) {
     const int q = wave + kPcConsumers * jq;
@@ -528,6 +548,7 @@ __global__ __launch_bounds__(64 * (kPcConsumers + kPcProducers)) void pc_gateup(
   gateup_block(g, (g.I / 8) / T, mb, ng);
   const int row0 = mb * 13 * 16;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  OCQ_PC_STAMP(wave, 0);
   if (wave >= kPcConsumers) {
     pc_producer<BF, T, C>(g, lds, ng, wave - kPcConsumers);
     if constexpr (FUSED) grid_arrive_and_wait(g.sync, gridDim.x, 0u);
@@ -536,6 +557,10 @@ __global__ __launch_bounds__(64 * (kPcConsumers + kPcProducers)) void pc_gateup(
   } else {
     pc_consumer<BF, 3, T, C, BF16H, FUSED>(g, lds, row0, ng, wave, 1 + 3 * (wave >> 1));
   }
+#ifdef OCQ_PHASE_STAMPS
+  __builtin_amdgcn_s_waitcnt(0);
+  OCQ_PC_STAMP(wave, 4);
+#endif
   if constexpr (FUSED) {
     lds_barrier();   // every code staged
     constexpr int NC = T * 8;
@@ -649,6 +674,16 @@ hipError_t go_mt(const GateUpArgs& g, int MT, int T, int grid, hipStream_t st, c
 }
 
 }  // namespace
+
+int pc_phase_copy(void* host, size_t bytes) {
+#ifdef OCQ_PHASE_STAMPS
+  if (bytes < sizeof(g_pc_phases)) return (int)hipErrorInvalidValue;
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(g_pc_phases), sizeof(g_pc_phases));
+#else
+  (void)host; (void)bytes;
+  return -1;
+#endif
+}
 
 hipError_t launch_gateup(const Plan& p, const GateUpArgs& g, hipStream_t st, const LaunchEvents& ev, bool& fused) {
   if (p.lg1) {

@@ -31,6 +31,17 @@
 #include "gemm_core.h"
 
 namespace ocq {
+
+#ifdef OCQ_PHASE_STAMPS
+// Per-wave phase totals of the last launch of each LDS-tiled kernel (built
+// only with OCQ_PHASE_STAMPS): [gate/up, down][workgroup < 512][wave < 8]
+// [load wait, barrier, MFMA batches, LDS-read wait after the batches, whole
+// loop, stages] in shader-clock ticks (s_memtime), the time stamps placed
+// where the waves wait for LDS reads anyway.
+__device__ uint64_t g_lg_phases[2][kPhaseWGs][8][8];
+static_assert(sizeof(g_lg_phases) == kLgPhaseBytes, "layout stated in ocq_internal.h");
+#endif
+
 namespace {
 
 // Geometry of one LDS-tiled kernel.  BF: weight format (kB_FP8_F16: E4M3
@@ -294,6 +305,9 @@ __device__ __forceinline__ void lg_mainloop(const uint8_t* a, int nva, size_t a_
   constexpr int NM = G::MTW * G::TW * (G::A16 ? 1 : G::SUB);
   constexpr int LSTEP = 2 * G::PW <= NM ? 2 : 1;
   static_assert(LSTEP * G::PW <= NM, "every load of a stage between two MFMAs of its last piece");
+#ifdef OCQ_PHASE_STAMPS
+  uint64_t p_vm = 0, p_bar = 0, p_mma = 0, p_set = 0;
+#endif
   // one stage; E = s % 2 (compile-time)
   auto stage = [&](int s, auto ec) {
     constexpr int E = decltype(ec)::value;
@@ -305,11 +319,27 @@ __device__ __forceinline__ void lg_mainloop(const uint8_t* a, int nva, size_t a_
       const bool newu = qan == 0;                              // ... starts a unit position
       const int cur = NP % 2 == 0 ? q % 2 : E;                 // A buffers: by piece, or by stage
       const int bcur = (E * G::UPK + up) % 2, bnext = (E * G::UPK + up + 1) % 2;   // B buffers: by unit position
+#ifdef OCQ_PHASE_STAMPS
+      uint64_t t_s;
+      if (q + 1 == NP) {
+        const uint64_t ta = __builtin_amdgcn_s_memtime();
+        lg_wait<G, G::NSTG - 2>();
+        const uint64_t tb = __builtin_amdgcn_s_memtime();
+        lds_barrier();
+        lgkm_settled();
+        t_s = __builtin_amdgcn_s_memtime();
+        p_vm += tb - ta;
+        p_bar += t_s - tb;
+      } else {
+        t_s = __builtin_amdgcn_s_memtime();
+      }
+#else
       if (q + 1 == NP) {   // also after the last stage: no branch, so no conservative wait at a join
         lg_wait<G, G::NSTG - 2>();
         lds_barrier();
         lgkm_settled();
       }
+#endif
       // the next piece's LDS reads, one after each of the first MFMAs
       const uint8_t* rbase = slot(q + 1 < NP ? s : s + 1);
       const int rup = kw * G::UPK + upn;
@@ -343,15 +373,33 @@ __device__ __forceinline__ void lg_mainloop(const uint8_t* a, int nva, size_t a_
       }
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (PIPE) __builtin_amdgcn_s_setprio(0);
+#ifdef OCQ_PHASE_STAMPS
+      const uint64_t t_e = __builtin_amdgcn_s_memtime();
       lgkm_settled();
+      p_mma += t_e - t_s;
+      p_set += __builtin_amdgcn_s_memtime() - t_e;
+#else
+      lgkm_settled();
+#endif
     }
   };
+#ifdef OCQ_PHASE_STAMPS
+  const uint64_t t_loop0 = __builtin_amdgcn_s_memtime();
+#endif
   for (int s = 0; s < NS; s += 2) {
     lgkm_settled();
     stage(s, std::integral_constant<int, 0>{});
     stage(s + 1, std::integral_constant<int, 1>{});
   }
   wait_vm<0>();
+#ifdef OCQ_PHASE_STAMPS
+  const uint64_t t_loop1 = __builtin_amdgcn_s_memtime();
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  if (lane == 0 && blockIdx.x < kPhaseWGs && wave < 8) {
+    uint64_t* o = g_lg_phases[G::BF == kB_BF16 ? 1 : 0][blockIdx.x][wave];
+    o[0] = p_vm; o[1] = p_bar; o[2] = p_mma; o[3] = p_set; o[4] = t_loop1 - t_loop0; o[5] = (uint64_t)NS;
+  }
+#endif
 }
 
 // Sum the KW partial tiles into the kw = 0 waves in a fixed order, reusing
@@ -590,6 +638,16 @@ using GUL = Lg<kB_FP8_F16, true, kLgRM, kLgRT1, 2, kLgWT1, 1, 1, 3>;
 using GDL = Lg<kB_BF16, true, kLgRM2, kLgRT2, 1, 4, 2, 2, 4>;
 
 }  // namespace
+
+int lg_phase_copy(void* host, size_t bytes) {
+#ifdef OCQ_PHASE_STAMPS
+  if (bytes < sizeof(g_lg_phases)) return (int)hipErrorInvalidValue;
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(g_lg_phases), sizeof(g_lg_phases));
+#else
+  (void)host; (void)bytes;
+  return -1;
+#endif
+}
 
 hipError_t launch_gateup_large(const Plan& p, const GateUpArgs& g, hipStream_t st, const LaunchEvents& ev) {
   if ((p.inter / 8) % GUL::RT || p.hidden % kChunk) return hipErrorInvalidValue;

@@ -49,4 +49,14 @@ int diag_mfma_rate(int iters, float* out, int nblocks, void* stream);
 int diag_empty(void* stream);
 int diag_mfma_dot(int form, const uint8_t* a, const uint8_t* b, int M, int N, int K, float* c, void* stream);
 
+// Per-wave phase stamps of the GEMM main loops, recorded only by a library
+// built with OCQ_PHASE_STAMPS, for workgroups below kPhaseWGs: copy the last
+// launch's values to host memory of at least the stated bytes.  Return 0, a
+// hipError_t value, or -1 when the library was built without the stamps.
+constexpr int kPhaseWGs = 512;
+constexpr size_t kLgPhaseBytes = (size_t)2 * kPhaseWGs * 8 * 8 * 8;    // gemm_large.hip
+constexpr size_t kPcPhaseBytes = (size_t)kPhaseWGs * 12 * 8 * 8;       // gemm_gateup.hip
+int lg_phase_copy(void* host, size_t bytes);
+int pc_phase_copy(void* host, size_t bytes);
+
 }  // namespace ocq

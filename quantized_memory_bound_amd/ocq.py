@@ -11,7 +11,10 @@ import os
 
 import numpy as np
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libocq.so")
+# OCQ_LIBRARY names another build of the library (for instance
+# libocq_phases.so, built with --phase-stamps); the default is the in-tree
+# libocq.so
+LIB_PATH = os.environ.get("OCQ_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libocq.so")
 
 PREC_FP8 = 0
 PREC_FP8_DOWN_BF16 = 1
@@ -28,7 +31,7 @@ EXPORTS = ("ocq_version", "ocq_packed_bytes", "ocq_pack_weights_host", "ocq_pack
            "ocq_unpack_weights_host", "ocq_workspace_bytes", "ocq_mlp_forward", "ocq_check_blob",
            "ocq_set_stage_events", "ocq_last_error", "ocq_stack_workspace_bytes", "ocq_mlp_stack_forward",
            "ocq_calibrate_smoothing_host", "ocq_pack_weights_smoothed_host", "ocq_pack_weights_smoothed",
-           "ocq_diag_stream_read", "ocq_diag_window_read", "ocq_diag_mfma_rate", "ocq_diag_empty", "ocq_diag_mfma_dot", "ocq_noalloc_scratch_bytes",
+           "ocq_diag_stream_read", "ocq_diag_window_read", "ocq_diag_mfma_rate", "ocq_diag_empty", "ocq_diag_mfma_dot", "ocq_diag_phase_stamps", "ocq_noalloc_scratch_bytes",
            "ocq_mlp_forward_noalloc", "ocq_set_fused_requant")
 
 
@@ -88,6 +91,7 @@ def lib():
     L.ocq_diag_mfma_rate.argtypes, L.ocq_diag_mfma_rate.restype = [i, vp, i, vp, ctypes.POINTER(ctypes.c_double)], i
     L.ocq_diag_empty.argtypes, L.ocq_diag_empty.restype = [vp], i
     L.ocq_diag_mfma_dot.argtypes, L.ocq_diag_mfma_dot.restype = [i, vp, vp, i, i, i, vp, vp], i
+    L.ocq_diag_phase_stamps.argtypes, L.ocq_diag_phase_stamps.restype = [i, vp, sz], i
     _lib = L
     return L
 
@@ -397,6 +401,20 @@ def diag_mfma_rate(iters, out, blocks, stream=None):
 
 def diag_empty(stream=None):
     _check(lib().ocq_diag_empty(_stream_handle(stream)))
+
+
+PHASE_SHAPES = {0: (2, 512, 8, 8), 1: (512, 12, 8)}
+
+
+def diag_phase_stamps(kernel):
+    """Phase stamp table of the last launch (kernel 0: LDS-tiled GEMMs,
+    kernel 1: producer/consumer gate/up) as a uint64 array of shape
+    PHASE_SHAPES[kernel]; needs a library built with --phase-stamps."""
+    if kernel not in PHASE_SHAPES:
+        raise OcqError(ERR_INVALID_ARG, "kernel must be 0 or 1")
+    out = np.zeros(PHASE_SHAPES[kernel], dtype=np.uint64)
+    _check(lib().ocq_diag_phase_stamps(kernel, out.ctypes.data, out.nbytes))
+    return out
 
 
 def diag_mfma_dot(form, a_codes, b_codes, stream=None):

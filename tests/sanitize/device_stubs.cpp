@@ -22,5 +22,8 @@ size_t diag_mfma_rate_flops(int, int) { unreachable("diag_mfma_rate_flops"); }
 int diag_mfma_rate(int, float*, int, void*) { unreachable("diag_mfma_rate"); }
 int diag_empty(void*) { unreachable("diag_empty"); }
 int diag_mfma_dot(int, const uint8_t*, const uint8_t*, int, int, int, float*, void*) { unreachable("diag_mfma_dot"); }
+// as in a library built without phase stamps
+int lg_phase_copy(void*, size_t) { return -1; }
+int pc_phase_copy(void*, size_t) { return -1; }
 
 }  // namespace ocq

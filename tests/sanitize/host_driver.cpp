@@ -130,6 +130,15 @@ int main() {
   EXPECT(ocq_diag_window_read(x, 1000, 1, y, 1, nullptr) == OCQ_ERR_INVALID_ARG);
   EXPECT(ocq_diag_mfma_rate(0, y, 1, nullptr, nullptr) == OCQ_ERR_INVALID_ARG);
   EXPECT(ocq_diag_mfma_dot(3, x, y, 16, 16, 128, (float*)ws, nullptr) == OCQ_ERR_INVALID_ARG);
+  {
+    std::vector<uint64_t> stamps(2 * 512 * 8 * 8);
+    const size_t sb = stamps.size() * sizeof(uint64_t);
+    EXPECT(ocq_diag_phase_stamps(2, stamps.data(), sb) == OCQ_ERR_INVALID_ARG);
+    EXPECT(ocq_diag_phase_stamps(0, nullptr, sb) == OCQ_ERR_INVALID_ARG);
+    EXPECT(ocq_diag_phase_stamps(0, stamps.data(), sb - 1) == OCQ_ERR_BUFFER_TOO_SMALL);
+    EXPECT(ocq_diag_phase_stamps(0, stamps.data(), sb) == OCQ_ERR_UNSUPPORTED);
+    EXPECT(ocq_diag_phase_stamps(1, stamps.data(), sb) == OCQ_ERR_UNSUPPORTED);
+  }
   EXPECT(ocq_set_fused_requant(0) == OCQ_OK);
   std::printf("%s (%d failed checks)\n", g_fail ? "FAIL" : "OK", g_fail);
   return g_fail ? 1 : 0;

@@ -286,7 +286,11 @@ ocq_status ocq_diag_mfma_dot(int form, const void* a_dev, const void* b_dev, int
  *   kernel 1, producer/consumer gate/up (393,216 B): [workgroup][wave 0..11:
  *     8 consumers, then 4 producers][entry, consumer loop start, loop end,
  *     partial tiles stored, wave end, 0, 0, 0], 100 MHz time stamps (the
- *     consumer-only fields are 0 for producers).
+ *     consumer-only fields are 0 for producers);
+ *   kernel 2, x quantization and requantization (32,768 B): [x-quant,
+ *     requant][workgroup 0..1023][start, end once its stores have landed],
+ *     100 MHz time stamps (0 for workgroups that end early: padding rows,
+ *     unused slots of the last group of m-tiles).
  * OCQ_ERR_INVALID_ARG for another kernel value or a null pointer,
  * OCQ_ERR_DEVICE if the copy fails. */
 ocq_status ocq_diag_phase_stamps(int kernel, void* host_out, size_t bytes);

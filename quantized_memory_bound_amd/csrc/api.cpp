@@ -223,11 +223,12 @@ ocq_status ocq_diag_empty(void* stream) {
 
 ocq_status ocq_diag_phase_stamps(int kernel, void* host_out, size_t bytes) {
   g_err.clear();
-  if (kernel != 0 && kernel != 1) return set_error(OCQ_ERR_INVALID_ARG, "kernel must be 0 or 1");
+  if (kernel < 0 || kernel > 2) return set_error(OCQ_ERR_INVALID_ARG, "kernel must be 0, 1 or 2");
   if (!host_out) return set_error(OCQ_ERR_INVALID_ARG, "host_out is null");
-  const size_t need = kernel == 0 ? kLgPhaseBytes : kPcPhaseBytes;
+  const size_t need = kernel == 0 ? kLgPhaseBytes : kernel == 1 ? kPcPhaseBytes : kQPhaseBytes;
   if (bytes < need) return set_error(OCQ_ERR_BUFFER_TOO_SMALL, "host_out smaller than the stamp table");
-  const int rc = kernel == 0 ? lg_phase_copy(host_out, bytes) : pc_phase_copy(host_out, bytes);
+  const int rc = kernel == 0 ? lg_phase_copy(host_out, bytes)
+               : kernel == 1 ? pc_phase_copy(host_out, bytes) : q_phase_copy(host_out, bytes);
   if (rc == -1) return set_error(OCQ_ERR_UNSUPPORTED, "library built without phase stamps (build --phase-stamps)");
   return rc ? set_hip_error((hipError_t)rc, "copy of the stamp table") : OCQ_OK;
 }

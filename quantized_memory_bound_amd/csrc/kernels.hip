@@ -23,6 +23,27 @@
 #include "kcommon.h"
 
 namespace ocq {
+
+#ifdef OCQ_PHASE_STAMPS
+// Start and end (100 MHz clock) of every workgroup of the last x-quant and
+// requantization launches, built only with OCQ_PHASE_STAMPS:
+// [x-quant, requant][workgroup < 1024][start, end after its stores landed].
+__device__ uint64_t g_q_phases[2][kQPhaseWGs][2];
+static_assert(sizeof(g_q_phases) == kQPhaseBytes, "layout stated in ocq_internal.h");
+#define OCQ_Q_START() const uint64_t q_t0 = __builtin_amdgcn_s_memrealtime()
+#define OCQ_Q_END(k)                                                                        \
+  do {                                                                                      \
+    __builtin_amdgcn_s_waitcnt(0);                                                          \
+    if (threadIdx.x == 0 && blockIdx.x < kQPhaseWGs) {                                      \
+      g_q_phases[k][blockIdx.x][0] = q_t0;                                                  \
+      g_q_phases[k][blockIdx.x][1] = __builtin_amdgcn_s_memrealtime();                      \
+    }                                                                                       \
+  } while (0)
+#else
+#define OCQ_Q_START()
+#define OCQ_Q_END(k)
+#endif
+
 namespace {
 
 constexpr int kWaves = 4;
@@ -64,6 +85,7 @@ __global__ __launch_bounds__(kThreads) void k_xquant(const uint16_t* __restrict_
                                                      uint32_t* __restrict__ amax_g, uint32_t* __restrict__ sync) {
   __shared__ float s_max[kWaves];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  OCQ_Q_START();
   int m, rest;
   if (!tile_row_of(blockIdx.x, Mpad / 16, m, rest)) return;
   const int C = H / 128;
@@ -143,6 +165,7 @@ __global__ __launch_bounds__(kThreads) void k_xquant(const uint16_t* __restrict_
     sx[m] = s;
     if (tap_s) tap_s[m] = s;
   }
+  OCQ_Q_END(0);
 }
 
 // ---------------------------------------------------------------- k_requant
@@ -163,6 +186,7 @@ __global__ __launch_bounds__(kThreads) void k_requant(const float* __restrict__ 
                                                       float* __restrict__ tap_s) {
   __shared__ float s_max[kWaves];
   int m, xb;
+  OCQ_Q_START();
   if (!tile_row_of(blockIdx.x, Mpad / 16, m, xb)) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int k = xb * kRqCols + threadIdx.x * 8;
@@ -212,6 +236,7 @@ __global__ __launch_bounds__(kThreads) void k_requant(const float* __restrict__ 
   }
   *(v2u*)(hq + frag_off8(m, k, I / 128)) = out;
   if (tap_q) *(v2u*)(tap_q + (size_t)m * I + k) = out;
+  OCQ_Q_END(1);
 }
 
 }  // namespace
@@ -227,6 +252,16 @@ void set_fused_requant(bool on) { g_fused_requant.store(on ? 1 : 0, std::memory_
 
 static inline void stage(const FwdArgs& a, int i) {
   if (a.stage_events && a.stage_events[i]) (void)hipEventRecord((hipEvent_t)a.stage_events[i], (hipStream_t)a.stream);
+}
+
+int q_phase_copy(void* host, size_t bytes) {
+#ifdef OCQ_PHASE_STAMPS
+  if (bytes < sizeof(g_q_phases)) return (int)hipErrorInvalidValue;
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(g_q_phases), sizeof(g_q_phases));
+#else
+  (void)host; (void)bytes;
+  return -1;
+#endif
 }
 
 int launch_forward(const Plan& p, const FwdArgs& a) {

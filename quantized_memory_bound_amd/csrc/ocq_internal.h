@@ -56,7 +56,10 @@ int diag_mfma_dot(int form, const uint8_t* a, const uint8_t* b, int M, int N, in
 constexpr int kPhaseWGs = 512;
 constexpr size_t kLgPhaseBytes = (size_t)2 * kPhaseWGs * 8 * 8 * 8;    // gemm_large.hip
 constexpr size_t kPcPhaseBytes = (size_t)kPhaseWGs * 12 * 8 * 8;       // gemm_gateup.hip
+constexpr int kQPhaseWGs = 1024;
+constexpr size_t kQPhaseBytes = (size_t)2 * kQPhaseWGs * 2 * 8;         // kernels.hip
 int lg_phase_copy(void* host, size_t bytes);
 int pc_phase_copy(void* host, size_t bytes);
+int q_phase_copy(void* host, size_t bytes);
 
 }  // namespace ocq

@@ -403,15 +403,16 @@ def diag_empty(stream=None):
     _check(lib().ocq_diag_empty(_stream_handle(stream)))
 
 
-PHASE_SHAPES = {0: (2, 512, 8, 8), 1: (512, 12, 8)}
+PHASE_SHAPES = {0: (2, 512, 8, 8), 1: (512, 12, 8), 2: (2, 1024, 2)}
 
 
 def diag_phase_stamps(kernel):
     """Phase stamp table of the last launch (kernel 0: LDS-tiled GEMMs,
-    kernel 1: producer/consumer gate/up) as a uint64 array of shape
-    PHASE_SHAPES[kernel]; needs a library built with --phase-stamps."""
+    kernel 1: producer/consumer gate/up, kernel 2: x quantization and
+    requantization) as a uint64 array of shape PHASE_SHAPES[kernel]; needs a
+    library built with --phase-stamps."""
     if kernel not in PHASE_SHAPES:
-        raise OcqError(ERR_INVALID_ARG, "kernel must be 0 or 1")
+        raise OcqError(ERR_INVALID_ARG, "kernel must be 0, 1 or 2")
     out = np.zeros(PHASE_SHAPES[kernel], dtype=np.uint64)
     _check(lib().ocq_diag_phase_stamps(kernel, out.ctypes.data, out.nbytes))
     return out

@@ -15,7 +15,10 @@ prints, from the stamps of the last launch:
   the batches (wave slot w runs on SIMD w mod 4);
 * the producer/consumer gate/up (one 208-row block): microseconds from the
   first wave's start to each consumer's loop start, loop end, stored partial
-  tiles and end, as medians over the workgroups.
+  tiles and end, as medians over the workgroups;
+* the x quantization and the requantization: the span from the first
+  workgroup's start to the last one's end (its stores landed) and the median
+  workgroup's duration, to set beside the kernels' traced durations.
 
 The stamps are only a timing aid; the blocks they time compute the same
 results as the plain library (the stamps sit where the waves wait anyway).
@@ -75,6 +78,20 @@ def pc_summary(t):
             "  last wave end %.2f" % (((b[:, :, 4] - t0) / 100.0).max())]
 
 
+def quant_summary(t):
+    lines = []
+    for k, name in enumerate(("x quantization", "requantization")):
+        v = t[k].astype(np.float64)
+        v = v[v[:, 0] > 0]
+        if not len(v):
+            continue
+        t0 = v[:, 0].min()
+        lines.append("%s: %d workgroups; last start %.2f us, median workgroup %.2f us, last end %.2f us after the first start"
+                     % (name, len(v), (v[:, 0].max() - t0) / 100.0, np.median(v[:, 1] - v[:, 0]) / 100.0,
+                        (v[:, 1].max() - t0) / 100.0))
+    return lines
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--workload", default="mixed_bf16_down", choices=sorted(I.WORKLOADS))
@@ -96,7 +113,8 @@ def main(argv=None):
         ocq.mlp_forward(blobs[i % len(blobs)], x, H, Iw, p, y=y, workspace=ws)
     torch.cuda.synchronize()
     print("workload %s, M=%d, library %s" % (a.workload, M, ocq.LIB_PATH))
-    for line in lds_tiled_summary(ocq.diag_phase_stamps(0)) + pc_summary(ocq.diag_phase_stamps(1)):
+    for line in (lds_tiled_summary(ocq.diag_phase_stamps(0)) + pc_summary(ocq.diag_phase_stamps(1)) +
+                 quant_summary(ocq.diag_phase_stamps(2))):
         print(line)
 
 

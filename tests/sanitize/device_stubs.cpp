@@ -25,5 +25,6 @@ int diag_mfma_dot(int, const uint8_t*, const uint8_t*, int, int, int, float*, vo
 // as in a library built without phase stamps
 int lg_phase_copy(void*, size_t) { return -1; }
 int pc_phase_copy(void*, size_t) { return -1; }
+int q_phase_copy(void*, size_t) { return -1; }
 
 }  // namespace ocq

@@ -133,7 +133,8 @@ int main() {
   {
     std::vector<uint64_t> stamps(2 * 512 * 8 * 8);
     const size_t sb = stamps.size() * sizeof(uint64_t);
-    EXPECT(ocq_diag_phase_stamps(2, stamps.data(), sb) == OCQ_ERR_INVALID_ARG);
+    EXPECT(ocq_diag_phase_stamps(3, stamps.data(), sb) == OCQ_ERR_INVALID_ARG);
+    EXPECT(ocq_diag_phase_stamps(2, stamps.data(), sb) == OCQ_ERR_UNSUPPORTED);
     EXPECT(ocq_diag_phase_stamps(0, nullptr, sb) == OCQ_ERR_INVALID_ARG);
     EXPECT(ocq_diag_phase_stamps(0, stamps.data(), sb - 1) == OCQ_ERR_BUFFER_TOO_SMALL);
     EXPECT(ocq_diag_phase_stamps(0, stamps.data(), sb) == OCQ_ERR_UNSUPPORTED);

@@ -38,14 +38,16 @@ def test_phase_stamps_need_the_stamped_build():
         pytest.skip("another library was selected through OCQ_LIBRARY")
     L = ocq.lib()
     buf = np.zeros(2 * 512 * 8 * 8, dtype=np.uint64)
-    assert L.ocq_diag_phase_stamps(2, buf.ctypes.data, buf.nbytes) == ocq.ERR_INVALID_ARG
+    assert L.ocq_diag_phase_stamps(3, buf.ctypes.data, buf.nbytes) == ocq.ERR_INVALID_ARG
+    assert L.ocq_diag_phase_stamps(-1, buf.ctypes.data, buf.nbytes) == ocq.ERR_INVALID_ARG
     assert L.ocq_diag_phase_stamps(0, None, buf.nbytes) == ocq.ERR_INVALID_ARG
     assert L.ocq_diag_phase_stamps(0, buf.ctypes.data, buf.nbytes - 8) == ocq.ERR_BUFFER_TOO_SMALL
     assert L.ocq_diag_phase_stamps(1, buf.ctypes.data, 512 * 12 * 8 * 8 - 1) == ocq.ERR_BUFFER_TOO_SMALL
-    for kernel in (0, 1):
+    assert L.ocq_diag_phase_stamps(2, buf.ctypes.data, 2 * 1024 * 2 * 8 - 1) == ocq.ERR_BUFFER_TOO_SMALL
+    for kernel in (0, 1, 2):
         assert L.ocq_diag_phase_stamps(kernel, buf.ctypes.data, buf.nbytes) == ocq.ERR_UNSUPPORTED
         assert b"phase stamps" in ocq.lib().ocq_last_error()
-    assert ocq.PHASE_SHAPES[0] == (2, 512, 8, 8) and ocq.PHASE_SHAPES[1] == (512, 12, 8)
+    assert ocq.PHASE_SHAPES == {0: (2, 512, 8, 8), 1: (512, 12, 8), 2: (2, 1024, 2)}
 
 
 def _packer_vs_oracle(hidden, inter, prec, seed=0, w_std=0.02):

@@ -636,7 +636,7 @@ hipError_t go(const GateUpArgs& g, int grid, hipStream_t st, const LaunchEvents&
   constexpr int KS = 8 / MS;
   constexpr int MTW = (MT + MS - 1) / MS;
   const int C = g.H / kChunk;
-  // six NVFP4 tiles of 2-4 m-tiles: one chunk in flight per wave (two
+  // six NVFP4 tiles of 1-4 m-tiles: one chunk in flight per wave (two
   // would not fit the registers of two waves per SIMD)
   if constexpr ((BF == kB_FP8_F16 || BF == kB_FP4_F16) && MT == 13 && T <= 3) {
     if (C == 16) return launch_pc<BF, T, 16, BF16H>(g, grid, st, ev, fused);
@@ -656,7 +656,7 @@ hipError_t go_t(const GateUpArgs& g, int T, int grid, hipStream_t st, const Laun
     case 2: return go<BF, BF16H, MT, 2>(g, grid, st, ev, fused);
     case 3: return go<BF, BF16H, MT, 3>(g, grid, st, ev, fused);
     case 6:
-      if constexpr (BF == kB_FP4_F16 && (MT == 2 || MT == 4)) return go<BF, BF16H, MT, 6>(g, grid, st, ev, fused);
+      if constexpr (BF == kB_FP4_F16 && MT <= 4) return go<BF, BF16H, MT, 6>(g, grid, st, ev, fused);
   }
   return hipErrorInvalidValue;
 }

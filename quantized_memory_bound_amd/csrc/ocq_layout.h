@@ -182,12 +182,13 @@ inline Plan make_plan(int M, int hidden, int inter, int prec) {
   p.n_mblocks = (M + rows_per_block - 1) / rows_per_block;
   // gate/up: tiles of 8 gate + 8 up columns; 3 tiles per workgroup when that
   // still gives >= 192 workgroups (one per CU at the configured sizes); 6 for
-  // NVFP4 with 2-4 m-tiles, whose workgroups hold one per CU (512 workgroups of
-  // 3 tiles would run in two rounds)
+  // NVFP4 with 1-4 m-tiles, whose workgroups hold one per CU (512 workgroups of
+  // 3 tiles would run in two rounds with 2-4 m-tiles; with one m-tile, two per
+  // CU, the six-tile workgroups measured 2 % faster at M = 1 and 13)
   int nt1 = inter / 8;
   p.T1 = 1;
   for (int t : {6, 3, 2}) {
-    if (nt1 % t == 0 && nt1 / t >= 192 && (t < 6 || (prec == kFP4 && (p.MT == 2 || p.MT == 4)))) { p.T1 = t; break; }
+    if (nt1 % t == 0 && nt1 / t >= 192 && (t < 6 || (prec == kFP4 && p.MT <= 4))) { p.T1 = t; break; }
   }
   p.ngroups1 = nt1 / p.T1;
   p.namax = p.ngroups1;

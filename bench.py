@@ -50,14 +50,16 @@ def alg_bytes(M, H, I, prec):
     return w + H * 4 + 2 * M * H * 2
 
 
-def gateup_alg(M, H, I, prec):
+def gateup_alg(M, H, I, prec, requant_inside=False):
     """Gate/up kernel: weight codes + scales + x codes and scales read once
-    (h stays on chip in the method, so its spill is not counted) and flops."""
+    (h stays on chip in the method, so its spill is not counted), plus the h
+    codes and row scales it writes when it requantizes h itself; and flops."""
     if prec in (0, 1):
         w = 2 * I * H + 2 * I * 4
     else:
         w = I * H + 2 * I * H // 16 + 8
-    return w + M * H + M * 4, 2.0 * M * H * 2 * I
+    out = M * I + M * 4 if requant_inside else 0
+    return w + M * H + M * 4 + out, 2.0 * M * H * 2 * I
 
 
 class HipEvents:
@@ -309,8 +311,9 @@ def main():
     ap.add_argument("--no-stage-events", action="store_true", help="skip the gate/up kernel timing pass")
     ap.add_argument("--mode", choices=["graph", "eager"], default="graph",
                     help="graph: replay a captured HIP graph of R steps; eager: one call per step")
-    ap.add_argument("--fused-requant", type=int, choices=[0, 1], default=0,
-                    help="1: requantize h inside the gate/up kernel where its grid fits the GPU at once")
+    ap.add_argument("--fused-requant", type=int, choices=[0, 1, 2], default=2,
+                    help="where h is requantized: 0 a second kernel, 1 inside the gate/up kernel where its "
+                         "grid fits the GPU at once, 2 (the library's default) the latter up to 64 rows")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 256 MiB copy kernel (counter calibration for rocprofv3 --pmc)")
     ap.add_argument("--vendor-gemm", action="store_true",
@@ -329,7 +332,7 @@ def main():
     from quantized_memory_bound_amd import inputs as I
     from quantized_memory_bound_amd import ocq
 
-    ocq.set_fused_requant(bool(args.fused_requant))
+    ocq.set_fused_requant(args.fused_requant)
     if args.vendor_gemm:
         return vendor_gemm(args)
     if args.workload in I.STACKS:
@@ -419,13 +422,15 @@ def main():
     gbps = ab / (ms_step * 1e-3) / 1e9
     tok_s = M / (ms_step * 1e-3)
 
+    inside = ocq.last_requant_in_gateup() == 1
     roof = None
     if gu_ms:
-        gbytes, gflops = gateup_alg(M, H, Iw, prec)
+        gbytes, gflops = gateup_alg(M, H, Iw, prec, inside)
         traffic = read_traffic(args.workload if args.M is None else "%s_M%d" % (args.workload, M),
                                kernel_source_digest())
         roof = roofline(gbytes, gflops, prec, gu_ms * 1e-3, traffic)
-        roof["kernel"] = "gate/up GEMM + SiLU*up + per-token amax"
+        roof["kernel"] = ("gate/up GEMM + SiLU*up + per-token requantization" if inside
+                          else "gate/up GEMM + SiLU*up + per-token amax")
         roof["us_per_launch"] = round(gu_ms * 1e3, 3)
         roof["timing"] = gu_how
         ceil = stream_ceiling(torch, ocq, gbytes, dev)
@@ -462,7 +467,7 @@ def main():
         "data": "synthetic (seeded; shapes and distributions of the workload)",
         "config": {"workload": args.workload, "hidden": H, "inter": Iw, "M": M, "prec_mode": prec_name,
                    "weight_copies_rotated": R, "alg_bytes_per_block": ab,
-                   "requant": "inside gate/up" if args.fused_requant else "separate kernel"},
+                   "requant": "inside gate/up" if inside else "separate kernel"},
         "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
         "tokens_per_s": round(tok_s, 1),
         "us_per_block": round(ms_step * 1e3, 3),

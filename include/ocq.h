@@ -295,7 +295,8 @@ ocq_status ocq_diag_mfma_dot(int form, const void* a_dev, const void* b_dev, int
  * OCQ_ERR_DEVICE if the copy fails. */
 ocq_status ocq_diag_phase_stamps(int kernel, void* host_out, size_t bytes);
 
-/* Where the per-token requantization of h runs (process-wide; default 0).
+/* Where the per-token requantization of h runs (process-wide; mode 0, 1 or
+ * 2, default 2; another value: OCQ_ERR_INVALID_ARG).
  * 1: inside the gate/up kernel whenever its whole grid can be resident at
  * once (an occupancy check on the host before each launch): h stays in
  * registers, the row maxima meet through device-scope atomics and the
@@ -304,10 +305,17 @@ ocq_status ocq_diag_phase_stamps(int kernel, void* host_out, size_t bytes);
  * intermediate kept on chip).  Such a call must not share the GPU with
  * kernels that keep its workgroups from becoming resident for that long; if
  * the wait times out the call's y is NaN.  0: the two-pass form (fp32 h to
- * the workspace, then a requantization kernel), which is faster on MI355X:
- * each device-scope round trip the exchange needs costs more than a kernel
- * launch.  Both give bit-identical results. */
-ocq_status ocq_set_fused_requant(int enable);
+ * the workspace, then a requantization kernel).  2: mode 1 for calls of at
+ * most 64 rows, mode 0 above: on MI355X the in-launch form is faster by
+ * 0.3-1.2 us per block for 1 to 52 rows and no faster for 208.  All modes
+ * give bit-identical results. */
+ocq_status ocq_set_fused_requant(int mode);
+
+/* Where the last forward call on this thread (ocq_mlp_forward and its
+ * no-allocation form, or the last block of ocq_mlp_stack_forward) requantized
+ * h: 1 inside the gate/up kernel, 0 in a separate kernel (also the BF16-down
+ * mode, which has no requantization), -1 before the first call. */
+int ocq_last_requant_in_gateup(void);
 
 /* Message for the last failure on this thread ("" if none). */
 const char* ocq_last_error(void);

@@ -13,6 +13,7 @@ namespace ocq {
 static thread_local std::string g_err;
 static thread_local void* g_stage_events[5];
 static thread_local bool g_stage_on = false;
+static thread_local int g_last_requant = -1;
 
 ocq_status set_error(ocq_status st, const char* msg) {
   g_err = msg ? msg : "";
@@ -44,6 +45,8 @@ int ocq_version(void) { return 10000; }
 
 const char* ocq_last_error(void) { return g_err.c_str(); }
 
+int ocq_last_requant_in_gateup(void) { return g_last_requant; }
+
 ocq_status ocq_set_stage_events(void* const* events, int count) {
   g_err.clear();
   if (events == nullptr || count == 0) {
@@ -56,9 +59,10 @@ ocq_status ocq_set_stage_events(void* const* events, int count) {
   return OCQ_OK;
 }
 
-ocq_status ocq_set_fused_requant(int enable) {
+ocq_status ocq_set_fused_requant(int mode) {
   g_err.clear();
-  set_fused_requant(enable != 0);
+  if (mode < 0 || mode > 2) return set_error(OCQ_ERR_INVALID_ARG, "fused requantization mode must be 0, 1 or 2");
+  set_fused_requant(mode);
   return OCQ_OK;
 }
 
@@ -180,6 +184,7 @@ ocq_status ocq_mlp_forward(const void* packed_dev, size_t packed_bytes, const vo
   FwdArgs a{(const uint8_t*)packed_dev, (const uint16_t*)x_bf16_dev, (uint16_t*)y_bf16_dev, (uint8_t*)workspace_dev,
             stream, g_stage_on ? g_stage_events : nullptr, ocq_taps{}};
   if (taps) a.taps = *taps;
+  a.requant_in_gateup = &g_last_requant;
   int rc = launch_forward(p, a);
   if (rc != 0) return set_hip_error((hipError_t)rc, "kernel launch");
   return OCQ_OK;
@@ -291,7 +296,8 @@ ocq_status ocq_mlp_stack_forward(const void* const* packed_devs, const size_t* p
   for (int l = 0; l < L; ++l) {
     uint16_t* out = ((L - 1 - l) % 2 == 0) ? (uint16_t*)y_bf16_dev : act;
     const Plan p = make_plan(M, hidden, inter, prec_modes[l]);
-    FwdArgs a{(const uint8_t*)packed_devs[l], in, out, (uint8_t*)workspace_dev, stream, nullptr, ocq_taps{}};
+    FwdArgs a{(const uint8_t*)packed_devs[l], in, out, (uint8_t*)workspace_dev, stream, nullptr, ocq_taps{},
+              &g_last_requant};
     int rc = launch_forward(p, a);
     if (rc != 0) return set_hip_error((hipError_t)rc, "kernel launch");
     in = out;

@@ -377,10 +377,12 @@ __device__ __forceinline__ void gateup_tile_epilogue(const GateUpArgs& g, const 
 //
 // The row scale sh = max_n |h| / 448 spans the columns of every gate/up
 // workgroup.  When the whole grid is resident at once (checked on the host
-// before such a launch), each workgroup folds its row maxima into amax_g with
-// device-scope atomic maxima, arrives at a device-scope counter and waits for
-// every workgroup to arrive; it then reads the finished maxima and quantizes
-// the h values it has kept in registers, so h never goes to memory (the
+// before such a launch), each workgroup folds its row maxima into one of the
+// kAmaxSlots copies of amax_g with device-scope atomic maxima, arrives at a
+// device-scope counter and waits for every workgroup to arrive (the last to
+// arrive sets the kGoCopies release flags, each polled by a few workgroups);
+// it then combines the copies for its rows and quantizes the h values it has
+// kept in registers, so h never goes to memory (the
 // German page "Wie es funktioniert": SiLU and quantization fused, the
 // intermediate kept on chip).  Device-scope atomics and loads are coherent
 // across the XCDs' L2 caches, so no cache write-back or invalidation is
@@ -396,31 +398,71 @@ constexpr uint64_t kGridWaitTicks = 10000000;   // 0.1 s
 // whose result arrives only once the maximum has been performed.  Callers
 // OR the results together and hand them to grid_arrive_and_wait, which waits
 // for them before the workgroup arrives.
-__device__ __forceinline__ uint32_t amax_atomic(uint32_t* amax_g, int m, float a) {
+__device__ __forceinline__ uint32_t amax_atomic(const GateUpArgs& g, int m, float a) {
+  uint32_t* copy = g.amax_g + (size_t)(blockIdx.x % kAmaxSlots) * g.Mpad;
   // |h| >= +0: the float order is the unsigned order of the bits
-  return __hip_atomic_fetch_max(amax_g + m, __float_as_uint(a), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ float amax_load(const uint32_t* amax_g, int m) {
-  return __uint_as_float(__hip_atomic_load(amax_g + m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  return __hip_atomic_fetch_max(copy + m, __float_as_uint(a), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Every wave of the workgroup calls this (two workgroup barriers inside);
-// seen: the OR of the wave's amax_atomic results (0 if it made none).
-__device__ __forceinline__ void grid_arrive_and_wait(uint32_t* sync, uint32_t nwg, uint32_t seen) {
+// seen: the OR of the wave's amax_atomic results (0 if it made none).  Also
+// clears the workgroup's nrows row maxima rmax in LDS for grid_row_maxima.
+__device__ __forceinline__ void grid_arrive_and_wait(uint32_t* sync, uint32_t nwg, uint32_t seen, float* rmax,
+                                                     int nrows) {
   asm volatile("" ::"v"(seen));   // the results have arrived: this wave's maxima are performed
   wait_vm<0>();
+  for (int i = threadIdx.x; i < nrows; i += blockDim.x) rmax[i] = 0.0f;
   lds_barrier();                  // ... and those of every wave of the workgroup
-  if (threadIdx.x == 0) {
-    __hip_atomic_fetch_add(sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-    while (__hip_atomic_load(sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < nwg) {
-      __builtin_amdgcn_s_sleep(1);
-      if (__builtin_amdgcn_s_memrealtime() - t0 > kGridWaitTicks) {
-        __hip_atomic_store(sync + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        break;
+  if (threadIdx.x < 64) {          // wave 0
+    uint32_t last = 0u;
+    if (threadIdx.x == 0) {
+      const uint32_t G = kArriveGroups, grp = blockIdx.x % G;
+      const uint32_t members = nwg / G + (grp < nwg % G ? 1u : 0u);
+      uint32_t* gc = sync + kGoStride * (1 + kGoCopies + grp);
+      if (__hip_atomic_fetch_add(gc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == members - 1) {
+        const uint32_t groups = nwg < G ? nwg : G;   // the last of its group arrives for the group
+        last = __hip_atomic_fetch_add(sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == groups - 1 ? 1u : 0u;
       }
     }
+    last = __builtin_amdgcn_readfirstlane(last);
+    if (last) {                   // every other workgroup has arrived: release them
+      if (threadIdx.x < kGoCopies)
+        __hip_atomic_store(sync + kGoStride * (1 + threadIdx.x), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else if (threadIdx.x == 0) {
+      const uint32_t* go = sync + kGoStride * (1 + blockIdx.x % kGoCopies);
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      while (__hip_atomic_load(go, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+        __builtin_amdgcn_s_sleep(1);
+        if (__builtin_amdgcn_s_memrealtime() - t0 > kGridWaitTicks) {
+          __hip_atomic_store(sync + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+      }
+    }
+  }
+  lds_barrier();
+}
+
+// After grid_arrive_and_wait, by every thread of the workgroup (NT threads):
+// the maxima of its ROWS rows from row0 over the kAmaxSlots copies, into
+// rmax[0, ROWS) in LDS (cleared by grid_arrive_and_wait).  The threads share
+// the ROWS x kAmaxSlots loads, all requested before the first is used;
+// returns after a workgroup barrier.
+template <int NT, int ROWS>
+__device__ __forceinline__ void grid_row_maxima(const GateUpArgs& g, int row0, float* rmax) {
+  constexpr int PER = (ROWS * kAmaxSlots + NT - 1) / NT, nrows = ROWS, n = ROWS * kAmaxSlots;
+  uint32_t v[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = threadIdx.x + j * NT, rl = i % nrows, k = i / nrows;
+    v[j] = i < n ? __hip_atomic_load(g.amax_g + (size_t)k * g.Mpad + row0 + rl, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT)
+                 : 0u;
+  }
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = threadIdx.x + j * NT;
+    if (i < n) __hip_atomic_fetch_max((uint32_t*)rmax + i % nrows, v[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
   lds_barrier();
 }
@@ -442,13 +484,13 @@ __device__ __forceinline__ void stage_code(uint8_t* stage, int ncols, int rl, in
 // Write-out of a fused requantization, by every thread of the workgroup
 // (nthreads): the staged codes of rows [row0, row0 + nrows) x columns
 // [n0, n0 + ncols) as 8-byte pieces in the down projection's fragment order
-// and to the plain tap; the row scales of those rows (scales: one workgroup
-// per m-block); and zero codes and scales for the rows [rows_end, Mpad) that
+// and to the plain tap; the row scales of those rows from their maxima rmax
+// (scales: one workgroup per m-block); and zero codes and scales for the rows [rows_end, Mpad) that
 // lie past every gate/up m-block but inside the down projection's
 // (last_mb: the workgroups of the last m-block, each for its own columns).
-__device__ __forceinline__ void fused_write_out(const GateUpArgs& g, const uint8_t* stage, int row0, int nrows,
-                                                int n0, int ncols, bool scales, bool last_mb, int rows_end,
-                                                int nthreads) {
+__device__ __forceinline__ void fused_write_out(const GateUpArgs& g, const uint8_t* stage, const float* rmax,
+                                                int row0, int nrows, int n0, int ncols, bool scales, bool last_mb,
+                                                int rows_end, int nthreads) {
   const int C = g.I / kChunk, per_row = ncols / 8;
   for (int p = threadIdx.x; p < nrows * per_row; p += nthreads) {
     const int rl = p / per_row, t = p % per_row, m = row0 + rl, n = n0 + 8 * t;
@@ -459,7 +501,7 @@ __device__ __forceinline__ void fused_write_out(const GateUpArgs& g, const uint8
   if (scales) {
     for (int rl = threadIdx.x; rl < nrows; rl += nthreads) {
       const int m = row0 + rl;
-      const float s = amax_load(g.amax_g, m) / 448.0f;
+      const float s = rmax[rl] / 448.0f;
       g.sh[m] = s;
       if (g.tap_sh && m < g.M) g.tap_sh[m] = s;
     }

@@ -88,6 +88,7 @@ __global__ __launch_bounds__(64 * MS * KS) void ks_gateup(GateUpArgs g) {
   static_assert(!(FUSED && BF16H), "the BF16-down mode has no requantization");
   constexpr int MTW = (MT + MS - 1) / MS;
   extern __shared__ v4f red4[];
+  __shared__ float s_rmax[FUSED ? MT * 16 : 1];   // FUSED: the workgroup's grid-wide row maxima
   int mb, ng;
   gateup_block(g, (g.I / 8) / T, mb, ng);
   const int C = g.H / kChunk;
@@ -178,13 +179,14 @@ __global__ __launch_bounds__(64 * MS * KS) void ks_gateup(GateUpArgs g) {
         for (int t = 1; t < T; ++t) a = fmaxf(a, s_am[wave + t][lane]);
         const int m = row0 + sq * 16 + lane;
         if (m < g.M) {
-          if constexpr (FUSED) seen = amax_atomic(g.amax_g, m, a);
+          if constexpr (FUSED) seen = amax_atomic(g, m, a);
           else g.amax_part[(size_t)m * ((g.I / 8) / T) + ng] = a;
         }
       }
     }
     if constexpr (FUSED) {
-      grid_arrive_and_wait(g.sync, gridDim.x, seen);
+      grid_arrive_and_wait(g.sync, gridDim.x, seen, s_rmax, MT * 16);
+      grid_row_maxima<64 * NW, MT * 16>(g, row0, s_rmax);
       uint8_t* stage = (uint8_t*)red4;   // every partial tile was read before the barriers
       constexpr int NC = T * 8;
       if (wave < MT * T) {
@@ -192,12 +194,13 @@ __global__ __launch_bounds__(64 * MS * KS) void ks_gateup(GateUpArgs g) {
         for (int e = 0; e < 2; ++e) {
           const int rl = sq * 16 + gateup_value_row(e);
           float sc, rcp;
-          row_scale_of(amax_load(g.amax_g, row0 + rl), sc, rcp);
+          row_scale_of(s_rmax[rl], sc, rcp);
           stage_code(stage, NC, rl, st * 8 + (lane & 7), hv[e], sc, rcp);
         }
       }
       lds_barrier();
-      fused_write_out(g, stage, row0, MT * 16, ng * NC, NC, ng == 0, mb == g.n_mb - 1, g.n_mb * MT * 16, 64 * NW);
+      fused_write_out(g, stage, s_rmax, row0, MT * 16, ng * NC, NC, ng == 0, mb == g.n_mb - 1, g.n_mb * MT * 16,
+                      64 * NW);
     }
     return;
   }
@@ -252,7 +255,7 @@ __global__ __launch_bounds__(64 * MS * KS) void ks_gateup(GateUpArgs g) {
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
             if constexpr (FUSED) {
-              if (m + 2 * e < g.M) seen |= amax_atomic(g.amax_g, m + 2 * e, amax[jq][e]);
+              if (m + 2 * e < g.M) seen |= amax_atomic(g, m + 2 * e, amax[jq][e]);
             } else {
               g.amax_part[(size_t)(m + 2 * e) * ngroups + ng] = amax[jq][e];
             }
@@ -262,7 +265,8 @@ __global__ __launch_bounds__(64 * MS * KS) void ks_gateup(GateUpArgs g) {
     }
   }
   if constexpr (FUSED) {
-    grid_arrive_and_wait(g.sync, gridDim.x, seen);
+    grid_arrive_and_wait(g.sync, gridDim.x, seen, s_rmax, MT * 16);
+    grid_row_maxima<64 * NW, MT * 16>(g, row0, s_rmax);
     uint8_t* stage = (uint8_t*)red4;   // the last tile's partials were read before the barriers
     constexpr int NC = T * 8;
 #pragma unroll
@@ -273,14 +277,15 @@ __global__ __launch_bounds__(64 * MS * KS) void ks_gateup(GateUpArgs g) {
         for (int e = 0; e < 2; ++e) {
           const int rl = q * 16 + gateup_value_row(e);
           float sc, rcp;
-          row_scale_of(amax_load(g.amax_g, row0 + rl), sc, rcp);
+          row_scale_of(s_rmax[rl], sc, rcp);
 #pragma unroll
           for (int t = 0; t < T; ++t) stage_code(stage, NC, rl, t * 8 + (lane & 7), hvq[jq][t][e], sc, rcp);
         }
       }
     }
     lds_barrier();
-    fused_write_out(g, stage, row0, MT * 16, ng * NC, NC, ng == 0, mb == g.n_mb - 1, g.n_mb * MT * 16, 64 * NW);
+    fused_write_out(g, stage, s_rmax, row0, MT * 16, ng * NC, NC, ng == 0, mb == g.n_mb - 1, g.n_mb * MT * 16,
+                    64 * NW);
   }
 }
 
@@ -392,7 +397,8 @@ __device__ __forceinline__ void pc_producer(const GateUpArgs& g, uint8_t* lds, i
 }
 
 template <int BF, int NV, int T, int C, bool BF16H, bool FUSED>
-__device__ __forceinline__ void pc_consumer(const GateUpArgs& g, uint8_t* lds, int row0, int ng, int wave, int mt0) {
+__device__ __forceinline__ void pc_consumer(const GateUpArgs& g, uint8_t* lds, float* rmax, int row0, int ng, int wave,
+                                            int mt0) {
   using P = Pc<BF, T, C>;
   constexpr int MT = 13, Q = 2;
   const int lane = threadIdx.x & 63, kidx = wave & 1;
@@ -507,7 +513,7 @@ __device__ __forceinline__ void pc_consumer(const GateUpArgs& g, uint8_t* lds, i
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
             if constexpr (FUSED) {
-              if (m + 2 * e < g.M) seen |= amax_atomic(g.amax_g, m + 2 * e, amax[jq][e]);
+              if (m + 2 * e < g.M) seen |= amax_atomic(g, m + 2 * e, amax[jq][e]);
             } else {
               g.amax_part[(size_t)(m + 2 * e) * ngroups + ng] = amax[jq][e];
             }
@@ -519,7 +525,8 @@ __device__ __forceinline__ void pc_consumer(const GateUpArgs& g, uint8_t* lds, i
   if constexpr (FUSED) {
     // every wave of the workgroup (producers too) arrives here; afterwards
     // the codes go to an LDS stage [208 rows][T * 8 columns]
-    grid_arrive_and_wait(g.sync, gridDim.x, seen);
+    grid_arrive_and_wait(g.sync, gridDim.x, seen, rmax, MT * 16);
+    grid_row_maxima<64 * (kPcConsumers + kPcProducers), MT * 16>(g, row0, rmax);
     uint8_t* stage = lds;
     constexpr int NC = T * 8;
 #pragma unroll
@@ -530,7 +537,7 @@ __device__ __forceinline__ void pc_consumer(const GateUpArgs& g, uint8_t* lds, i
         for (int e = 0; e < 2; ++e) {
           const int rl = q * 16 + gateup_value_row(e);
           float sc, rcp;
-          row_scale_of(amax_load(g.amax_g, row0 + rl), sc, rcp);
+          row_scale_of(rmax[rl], sc, rcp);
 #pragma unroll
           for (int t = 0; t < T; ++t) stage_code(stage, NC, rl, t * 8 + (lane & 7), hvq[jq][t][e], sc, rcp);
         }
@@ -543,6 +550,7 @@ template <int BF, int T, int C, bool BF16H, bool FUSED>
 __global__ __launch_bounds__(64 * (kPcConsumers + kPcProducers)) void pc_gateup(GateUpArgs g) {
   static_assert(!(FUSED && BF16H), "the BF16-down mode has no requantization");
   extern __shared__ v4f pc_lds[];
+  __shared__ float s_rmax[FUSED ? 13 * 16 : 1];   // FUSED: the workgroup's grid-wide row maxima
   uint8_t* lds = (uint8_t*)pc_lds;
   int mb, ng;
   gateup_block(g, (g.I / 8) / T, mb, ng);
@@ -551,11 +559,14 @@ __global__ __launch_bounds__(64 * (kPcConsumers + kPcProducers)) void pc_gateup(
   OCQ_PC_STAMP(wave, 0);
   if (wave >= kPcConsumers) {
     pc_producer<BF, T, C>(g, lds, ng, wave - kPcConsumers);
-    if constexpr (FUSED) grid_arrive_and_wait(g.sync, gridDim.x, 0u);
+    if constexpr (FUSED) {
+      grid_arrive_and_wait(g.sync, gridDim.x, 0u, s_rmax, 13 * 16);
+      grid_row_maxima<64 * (kPcConsumers + kPcProducers), 13 * 16>(g, row0, s_rmax);
+    }
   } else if (wave < 2) {
-    pc_consumer<BF, 4, T, C, BF16H, FUSED>(g, lds, row0, ng, wave, 0);
+    pc_consumer<BF, 4, T, C, BF16H, FUSED>(g, lds, s_rmax, row0, ng, wave, 0);
   } else {
-    pc_consumer<BF, 3, T, C, BF16H, FUSED>(g, lds, row0, ng, wave, 1 + 3 * (wave >> 1));
+    pc_consumer<BF, 3, T, C, BF16H, FUSED>(g, lds, s_rmax, row0, ng, wave, 1 + 3 * (wave >> 1));
   }
 #ifdef OCQ_PHASE_STAMPS
   __builtin_amdgcn_s_waitcnt(0);
@@ -564,7 +575,7 @@ __global__ __launch_bounds__(64 * (kPcConsumers + kPcProducers)) void pc_gateup(
   if constexpr (FUSED) {
     lds_barrier();   // every code staged
     constexpr int NC = T * 8;
-    fused_write_out(g, lds, row0, 13 * 16, ng * NC, NC, ng == 0, mb == g.n_mb - 1, g.n_mb * 13 * 16,
+    fused_write_out(g, lds, s_rmax, row0, 13 * 16, ng * NC, NC, ng == 0, mb == g.n_mb - 1, g.n_mb * 13 * 16,
                     64 * (kPcConsumers + kPcProducers));
   }
 }

@@ -50,8 +50,10 @@ struct GateUpArgs {
   uint16_t* tap_hb;         // optional plain [M][I] copy of bf16(h) (BF16-down mode)
   float* amax_part;         // [Mpad][ngroups] max |h| of each row over each workgroup's columns
   // per-token requantization inside the gate/up kernel (fused launches only):
-  uint32_t* amax_g;         // [Mpad] max |h| of each row (float bits, atomic max), zeroed by the x quantization
-  uint32_t* sync;           // [0] arrival count, [1] wait time-out flag, zeroed by the x quantization
+  uint32_t* amax_g;         // [kAmaxSlots][Mpad] max |h| of each row (float bits, atomic max) over the
+                            // workgroups of each copy, zeroed by the x quantization
+  uint32_t* sync;           // [kSyncWords]: [0] arrival count, [1] wait time-out flag, release flags at
+                            // kGoStride (1 + k), zeroed by the x quantization
   uint8_t* hq;              // E4M3 codes of h, fragment order, Mpad rows
   float* sh;                // [Mpad] row scales
   uint8_t* tap_hq;          // optional plain [M][I] copy of the codes

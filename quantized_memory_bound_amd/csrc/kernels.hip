@@ -89,9 +89,10 @@ __global__ __launch_bounds__(kThreads) void k_xquant(const uint16_t* __restrict_
   int m, rest;
   if (!tile_row_of(blockIdx.x, Mpad / 16, m, rest)) return;
   const int C = H / 128;
-  // the next kernel's grid-wide row maxima and arrival count start at zero
-  if (threadIdx.x == 0) amax_g[m] = 0u;
+  // the next kernel's grid-wide row maxima (every copy), arrival counts and release flags start at zero
+  if (threadIdx.x < kAmaxSlots) amax_g[(size_t)threadIdx.x * Mpad + m] = 0u;
   if (m == 0 && threadIdx.x < 2) sync[threadIdx.x] = 0u;
+  if (m == 0 && threadIdx.x < kGoCopies + kArriveGroups) sync[kGoStride * (1 + threadIdx.x)] = 0u;
   if (m >= M) {                                     // padding row: zero codes, zero scale
     for (int k = threadIdx.x * 8; k < H; k += kThreads * 8) {
       if (f16) *(v4i*)((uint16_t*)xq + frag_off16(m, k, C)) = v4i{0, 0, 0, 0};
@@ -243,12 +244,16 @@ __global__ __launch_bounds__(kThreads) void k_requant(const float* __restrict__ 
 
 // ---------------------------------------------------------------- forward
 
-// Off by default: measured on MI355X, the grid-wide exchange of the row
-// maxima (device-scope atomics, arrival count, wait) costs more than the
-// separate requantization launch it replaces (spec-verify block 35 -> 50 us).
-static std::atomic<int> g_fused_requant{0};
+// Where h is requantized: 0 in a second kernel, 1 inside the gate/up kernel
+// (where its grid is resident at once), 2 (default) inside it for up to
+// kFusedMaxRows rows.  Measured on MI355X (graph replays, one box), the
+// in-launch form saves 0.3-1.2 us per block from 1 to 52 rows (decode 20.6 ->
+// 19.4 us, NVFP4 M=1 28.4 -> 27.5 us) and ties at 208 rows (36.8 us), where
+// its exchange costs as much as the launch it saves.
+static std::atomic<int> g_fused_requant{2};
+constexpr int kFusedMaxRows = 64;
 
-void set_fused_requant(bool on) { g_fused_requant.store(on ? 1 : 0, std::memory_order_relaxed); }
+void set_fused_requant(int mode) { g_fused_requant.store(mode, std::memory_order_relaxed); }
 
 static inline void stage(const FwdArgs& a, int i) {
   if (a.stage_events && a.stage_events[i]) (void)hipEventRecord((hipEvent_t)a.stage_events[i], (hipStream_t)a.stream);
@@ -303,9 +308,11 @@ int launch_forward(const Plan& p, const FwdArgs& a) {
     gev.start = (hipEvent_t)a.stage_events[1];
     gev.end = (hipEvent_t)a.stage_events[2];
   }
-  bool fused = !bf16_down && g_fused_requant.load(std::memory_order_relaxed) != 0;
+  const int fmode = g_fused_requant.load(std::memory_order_relaxed);
+  bool fused = !bf16_down && (fmode == 1 || (fmode == 2 && p.M <= kFusedMaxRows));
   e = launch_gateup(p, g, st, gev, fused);
   if (e != hipSuccess) return (int)e;
+  if (a.requant_in_gateup) *a.requant_in_gateup = fused ? 1 : 0;
 
   if (!bf16_down && !fused) {
     hipLaunchKernelGGL(k_requant, dim3(tile_row_grid(p.Mpad / 16, (p.inter + kRqCols - 1) / kRqCols)),

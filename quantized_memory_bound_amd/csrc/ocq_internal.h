@@ -34,12 +34,13 @@ struct FwdArgs {
   void* stream;
   void* const* stage_events;  // 5 hipEvent_t or NULL
   ocq_taps taps;              // each pointer nullable
+  int* requant_in_gateup;     // nullable: set to 1 if the gate/up launch requantized h itself, else 0
 };
 
 // enqueue the kernels of one forward call (kernels.hip); returns 0 or a hipError_t value
 int launch_forward(const Plan& p, const FwdArgs& a);
-// process-wide: may gate/up launches requantize h themselves (default off)
-void set_fused_requant(bool on);
+// process-wide: where gate/up launches requantize h (ocq_set_fused_requant)
+void set_fused_requant(int mode);   // 0, 1 or 2 (ocq_set_fused_requant)
 
 // measurement kernels (diag.hip); return 0 or a hipError_t value
 int diag_stream_read(const void* src, size_t bytes, void* out, int nblocks, void* stream);

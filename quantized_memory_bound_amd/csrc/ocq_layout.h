@@ -110,6 +110,17 @@ inline BlobLayout blob_layout(int hidden, int inter, int prec) {
 // m-tiles (16 rows each) per gate/up workgroup; instantiated template values
 constexpr int kMTChoices[] = {1, 2, 4, 7, 13};
 constexpr int kMTMax = 13;
+// In-launch requantization: the row maxima are folded with atomics into
+// kAmaxSlots copies (workgroup b into copy b % kAmaxSlots), so that no
+// address takes more than a few of them; workgroups arrive on kArriveGroups
+// group counters (b % kArriveGroups), the last of each group on the top
+// counter; the release of the grid-wide wait is broadcast through kGoCopies
+// flags, each polled by a few workgroups.  Counters and flags lie kGoStride
+// words apart (each on its own 128-byte line).
+constexpr int kAmaxSlots = 32;
+constexpr int kGoCopies = 32, kArriveGroups = 16, kGoStride = 32;
+// [0] top arrivals, [1] time-out, release flags, group arrivals
+constexpr int kSyncWords = kGoStride * (1 + kGoCopies + kArriveGroups);
 
 // LDS-tiled kernels for many rows; chosen from kLgMinRows rows on
 constexpr int kLgRM = 13;        // gate/up: m-tiles per workgroup
@@ -221,8 +232,8 @@ inline Plan make_plan(int M, int hidden, int inter, int prec) {
   p.off_hq = o;   o = align_up(o + (prec == kFP8DownBF16 ? 0 : Mp * inter));
   p.off_hb = o;   o = align_up(o + (prec == kFP8DownBF16 ? Mp * inter * 2 : 0));
   p.off_sh = o;   o = align_up(o + Mp * 4);
-  p.off_amaxg = o; o = align_up(o + Mp * 4);
-  p.off_sync = o; o = align_up(o + 2 * 4);
+  p.off_amaxg = o; o = align_up(o + (size_t)kAmaxSlots * Mp * 4);
+  p.off_sync = o; o = align_up(o + (size_t)kSyncWords * 4);
   p.total = o;
   return p;
 }

@@ -32,7 +32,7 @@ EXPORTS = ("ocq_version", "ocq_packed_bytes", "ocq_pack_weights_host", "ocq_pack
            "ocq_set_stage_events", "ocq_last_error", "ocq_stack_workspace_bytes", "ocq_mlp_stack_forward",
            "ocq_calibrate_smoothing_host", "ocq_pack_weights_smoothed_host", "ocq_pack_weights_smoothed",
            "ocq_diag_stream_read", "ocq_diag_window_read", "ocq_diag_mfma_rate", "ocq_diag_empty", "ocq_diag_mfma_dot", "ocq_diag_phase_stamps", "ocq_noalloc_scratch_bytes",
-           "ocq_mlp_forward_noalloc", "ocq_set_fused_requant")
+           "ocq_mlp_forward_noalloc", "ocq_set_fused_requant", "ocq_last_requant_in_gateup")
 
 
 class OcqError(RuntimeError):
@@ -83,6 +83,7 @@ def lib():
     L.ocq_mlp_stack_forward.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(sz), ip, i, vp, i, i, i, vp, vp, sz, vp]
     L.ocq_mlp_stack_forward.restype = i
     L.ocq_set_fused_requant.argtypes, L.ocq_set_fused_requant.restype = [i], i
+    L.ocq_last_requant_in_gateup.argtypes, L.ocq_last_requant_in_gateup.restype = [], i
     L.ocq_noalloc_scratch_bytes.argtypes, L.ocq_noalloc_scratch_bytes.restype = [], sz
     L.ocq_mlp_forward_noalloc.argtypes = [vp, sz, vp, i, i, i, i, vp, ctypes.POINTER(Taps), vp]
     L.ocq_mlp_forward_noalloc.restype = i
@@ -196,10 +197,21 @@ def pack_weights(w_gate, w_up, w_down, prec_mode, device="cuda", stream=None, sm
     return blob
 
 
-def set_fused_requant(enable):
+FUSED_REQUANT_DEFAULT = 2
+
+
+def set_fused_requant(mode):
     """Process-wide: requantize h inside the gate/up kernel where its grid
-    fits the GPU at once (True), or in a second kernel (False, the default)."""
-    _check(lib().ocq_set_fused_requant(1 if enable else 0))
+    fits the GPU at once (1 or True), in a second kernel (0 or False), or the
+    first for calls of at most 64 rows and the second above (2, the
+    default)."""
+    _check(lib().ocq_set_fused_requant(int(mode)))
+
+
+def last_requant_in_gateup():
+    """1 if the last forward call on this thread requantized h inside the
+    gate/up kernel, 0 if in a separate kernel, -1 before the first call."""
+    return lib().ocq_last_requant_in_gateup()
 
 
 def set_stage_events(events):

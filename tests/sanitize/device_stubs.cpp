@@ -15,7 +15,7 @@ namespace ocq {
 }
 
 int launch_forward(const Plan&, const FwdArgs&) { unreachable("launch_forward"); }
-void set_fused_requant(bool) {}
+void set_fused_requant(int) {}
 int diag_stream_read(const void*, size_t, void*, int, void*) { unreachable("diag_stream_read"); }
 int diag_window_read(const void*, size_t, int, void*, int, void*) { unreachable("diag_window_read"); }
 size_t diag_mfma_rate_flops(int, int) { unreachable("diag_mfma_rate_flops"); }

@@ -9,6 +9,7 @@
 import ctypes
 import os
 import re
+import threading
 
 import numpy as np
 import pytest
@@ -48,6 +49,24 @@ def test_phase_stamps_need_the_stamped_build():
         assert L.ocq_diag_phase_stamps(kernel, buf.ctypes.data, buf.nbytes) == ocq.ERR_UNSUPPORTED
         assert b"phase stamps" in ocq.lib().ocq_last_error()
     assert ocq.PHASE_SHAPES == {0: (2, 512, 8, 8), 1: (512, 12, 8), 2: (2, 1024, 2)}
+
+
+def test_requant_placement_mode_is_checked():
+    """The requantization mode takes 0, 1 or 2; the report of where the last
+    call requantized h reads -1 on a thread that made no forward call."""
+    L = ocq.lib()
+    assert ocq.FUSED_REQUANT_DEFAULT == 2
+    for bad in (-1, 3, 100):
+        assert L.ocq_set_fused_requant(bad) == ocq.ERR_INVALID_ARG
+        assert b"mode" in L.ocq_last_error()
+    for good in (0, 1, 2):
+        assert L.ocq_set_fused_requant(good) == ocq.OK
+    ocq.set_fused_requant(ocq.FUSED_REQUANT_DEFAULT)
+    res = []
+    t = threading.Thread(target=lambda: res.append(ocq.last_requant_in_gateup()))
+    t.start()
+    t.join()
+    assert res == [-1]
 
 
 def _packer_vs_oracle(hidden, inter, prec, seed=0, w_std=0.02):

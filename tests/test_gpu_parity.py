@@ -302,7 +302,8 @@ def test_binding_rejects_bad_tensors():
 # The per-token requantization inside the gate/up kernel (grid-wide row
 # maxima, h kept in registers) and the two-pass form (fp32 h to the
 # workspace, then k_requant) compute the same h, the same maxima and the
-# same codes: every output must be bit-identical.  Shapes: the skinny
+# same codes: every output must be bit-identical, in all three modes of
+# ocq_set_fused_requant (the default, 2, takes the first up to 64 rows).  Shapes: the skinny
 # kernels (one pair per wave, and several m-tiles per wave), the 13-m-tile
 # kernel with weight producers (E4M3 and NVFP4 weights), the decode and
 # spec-verify workloads' shapes, and NVFP4 with six tiles per workgroup.
@@ -314,13 +315,19 @@ def test_fused_requant_matches_two_pass(H, Iw, M, prec):
     d = I.make_inputs(H, Iw, M, x_outliers=True, w_std=0.02, seed=H + Iw + M + prec)
     blob = ocq.pack_weights(d["w_gate"], d["w_up"], d["w_down"], prec)
     try:
-        ocq.set_fused_requant(False)
+        ocq.set_fused_requant(0)
         g2, _ = run_gpu(d, prec, blob=blob)
-        ocq.set_fused_requant(True)
+        assert ocq.last_requant_in_gateup() == 0
+        ocq.set_fused_requant(1)
         g1, _ = run_gpu(d, prec, blob=blob)
+        assert ocq.last_requant_in_gateup() == 1   # every grid here fits the GPU at once
+        ocq.set_fused_requant(2)
+        g3, _ = run_gpu(d, prec, blob=blob)
+        assert ocq.last_requant_in_gateup() == (1 if M <= 64 else 0)
     finally:
-        ocq.set_fused_requant(False)
+        ocq.set_fused_requant(ocq.FUSED_REQUANT_DEFAULT)
     for k in ("y", "xq", "sx", "hq", "sh"):
         assert np.array_equal(g1[k], g2[k]), k
+        assert np.array_equal(g3[k], g2[k]), k
     r = O.block_reference(d["x_bits"], d["w_gate"], d["w_up"], d["w_down"], prec)
     compare(g1, r, prec, what="fused %dx%d M=%d prec=%d" % (H, Iw, M, prec))

@@ -311,9 +311,9 @@ def main():
     ap.add_argument("--no-stage-events", action="store_true", help="skip the gate/up kernel timing pass")
     ap.add_argument("--mode", choices=["graph", "eager"], default="graph",
                     help="graph: replay a captured HIP graph of R steps; eager: one call per step")
-    ap.add_argument("--fused-requant", type=int, choices=[0, 1, 2], default=2,
-                    help="where h is requantized: 0 a second kernel, 1 inside the gate/up kernel where its "
-                         "grid fits the GPU at once, 2 (the library's default) the latter up to 64 rows")
+    ap.add_argument("--fused-requant", type=int, choices=[0, 1], default=1,
+                    help="where h is requantized: 1 (the library's default) inside the gate/up kernel where "
+                         "its grid fits the GPU at once, 0 in a second kernel")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 256 MiB copy kernel (counter calibration for rocprofv3 --pmc)")
     ap.add_argument("--vendor-gemm", action="store_true",

@@ -295,8 +295,8 @@ ocq_status ocq_diag_mfma_dot(int form, const void* a_dev, const void* b_dev, int
  * OCQ_ERR_DEVICE if the copy fails. */
 ocq_status ocq_diag_phase_stamps(int kernel, void* host_out, size_t bytes);
 
-/* Where the per-token requantization of h runs (process-wide; mode 0, 1 or
- * 2, default 2; another value: OCQ_ERR_INVALID_ARG).
+/* Where the per-token requantization of h runs (process-wide; mode 0 or 1,
+ * default 1; another value: OCQ_ERR_INVALID_ARG).
  * 1: inside the gate/up kernel whenever its whole grid can be resident at
  * once (an occupancy check on the host before each launch): h stays in
  * registers, the row maxima meet through device-scope atomics and the
@@ -304,11 +304,12 @@ ocq_status ocq_diag_phase_stamps(int kernel, void* host_out, size_t bytes);
  * funktioniert" of the post: SiLU fused with the quantization, the
  * intermediate kept on chip).  Such a call must not share the GPU with
  * kernels that keep its workgroups from becoming resident for that long; if
- * the wait times out the call's y is NaN.  0: the two-pass form (fp32 h to
- * the workspace, then a requantization kernel).  2: mode 1 for calls of at
- * most 64 rows, mode 0 above: on MI355X the in-launch form is faster by
- * 0.3-1.2 us per block for 1 to 52 rows and no faster for 208.  All modes
- * give bit-identical results. */
+ * the wait times out the call's y is NaN.  Where the grid does not fit (the
+ * NVFP4 gate/up at 208 rows, the LDS-tiled kernels from 384 rows) or in the
+ * BF16-down mode the call takes the two-pass form.  0: always the two-pass
+ * form (fp32 h to the workspace, then a requantization kernel).  On MI355X
+ * mode 1 is faster by 0.3-1.2 us per block.  Both give bit-identical
+ * results. */
 ocq_status ocq_set_fused_requant(int mode);
 
 /* Where the last forward call on this thread (ocq_mlp_forward and its

@@ -61,7 +61,7 @@ ocq_status ocq_set_stage_events(void* const* events, int count) {
 
 ocq_status ocq_set_fused_requant(int mode) {
   g_err.clear();
-  if (mode < 0 || mode > 2) return set_error(OCQ_ERR_INVALID_ARG, "fused requantization mode must be 0, 1 or 2");
+  if (mode != 0 && mode != 1) return set_error(OCQ_ERR_INVALID_ARG, "fused requantization mode must be 0 or 1");
   set_fused_requant(mode);
   return OCQ_OK;
 }

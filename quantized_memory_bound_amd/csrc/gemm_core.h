@@ -443,18 +443,27 @@ __device__ __forceinline__ void grid_arrive_and_wait(uint32_t* sync, uint32_t nw
   lds_barrier();
 }
 
+// Row scale s = fl32(a / 448) of a row whose maximum |h| is a, and its
+// reciprocal (0 for a zero row)
+__device__ __forceinline__ void row_scale_of(float a, float& s, float& rcp) {
+  s = a / 448.0f;
+  rcp = s > 0.0f ? 1.0f / s : 0.0f;
+}
+
 // After grid_arrive_and_wait, by every thread of the workgroup (NT threads):
 // the maxima of its ROWS rows from row0 over the kAmaxSlots copies, into
-// rmax[0, ROWS) in LDS (cleared by grid_arrive_and_wait).  The threads share
-// the ROWS x kAmaxSlots loads, all requested before the first is used;
-// returns after a workgroup barrier.
+// rs[0, ROWS) in LDS (cleared by grid_arrive_and_wait), then each row's scale
+// s = fl32(max / 448) in rs[r] and its reciprocal in rs[ROWS + r] (computed
+// once per row here instead of by every lane that quantizes a value of the
+// row).  The threads share the ROWS x kAmaxSlots loads, all requested before
+// the first is used; returns after a workgroup barrier.
 template <int NT, int ROWS>
-__device__ __forceinline__ void grid_row_maxima(const GateUpArgs& g, int row0, float* rmax) {
-  constexpr int PER = (ROWS * kAmaxSlots + NT - 1) / NT, nrows = ROWS, n = ROWS * kAmaxSlots;
+__device__ __forceinline__ void grid_row_maxima(const GateUpArgs& g, int row0, float* rs) {
+  constexpr int PER = (ROWS * kAmaxSlots + NT - 1) / NT, n = ROWS * kAmaxSlots;
   uint32_t v[PER];
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
-    const int i = threadIdx.x + j * NT, rl = i % nrows, k = i / nrows;
+    const int i = threadIdx.x + j * NT, rl = i % ROWS, k = i / ROWS;
     v[j] = i < n ? __hip_atomic_load(g.amax_g + (size_t)k * g.Mpad + row0 + rl, __ATOMIC_RELAXED,
                                      __HIP_MEMORY_SCOPE_AGENT)
                  : 0u;
@@ -462,16 +471,11 @@ __device__ __forceinline__ void grid_row_maxima(const GateUpArgs& g, int row0, f
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
     const int i = threadIdx.x + j * NT;
-    if (i < n) __hip_atomic_fetch_max((uint32_t*)rmax + i % nrows, v[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (i < n) __hip_atomic_fetch_max((uint32_t*)rs + i % ROWS, v[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
   lds_barrier();
-}
-
-// Row scale s = fl32(a / 448) of a row whose maximum |h| is a, and its
-// reciprocal (0 for a zero row)
-__device__ __forceinline__ void row_scale_of(float a, float& s, float& rcp) {
-  s = a / 448.0f;
-  rcp = s > 0.0f ? 1.0f / s : 0.0f;
+  for (int rl = threadIdx.x; rl < ROWS; rl += NT) row_scale_of(rs[rl], rs[rl], rs[ROWS + rl]);
+  lds_barrier();
 }
 
 // E4M3 code of the lane's value hv into the LDS stage [row][ncols] bytes of
@@ -481,14 +485,24 @@ __device__ __forceinline__ void stage_code(uint8_t* stage, int ncols, int rl, in
   stage[rl * ncols + col] = (uint8_t)(s > 0.0f ? e4m3_quot1(hv, s, rcp) : 0u);
 }
 
+// The same for the lane's N values of row rl in columns col0 + 8 j
+template <int N>
+__device__ __forceinline__ void stage_codes(uint8_t* stage, int ncols, int rl, int col0, const float (&hv)[N], float s,
+                                            float rcp) {
+  uint32_t c[N];
+  e4m3_quotN<N>(hv, s, rcp, c);
+#pragma unroll
+  for (int j = 0; j < N; ++j) stage[rl * ncols + col0 + 8 * j] = (uint8_t)(s > 0.0f ? c[j] : 0u);
+}
+
 // Write-out of a fused requantization, by every thread of the workgroup
 // (nthreads): the staged codes of rows [row0, row0 + nrows) x columns
 // [n0, n0 + ncols) as 8-byte pieces in the down projection's fragment order
-// and to the plain tap; the row scales of those rows from their maxima rmax
-// (scales: one workgroup per m-block); and zero codes and scales for the rows [rows_end, Mpad) that
+// and to the plain tap; the row scales rs of those rows (scales: one
+// workgroup per m-block); and zero codes and scales for the rows [rows_end, Mpad) that
 // lie past every gate/up m-block but inside the down projection's
 // (last_mb: the workgroups of the last m-block, each for its own columns).
-__device__ __forceinline__ void fused_write_out(const GateUpArgs& g, const uint8_t* stage, const float* rmax,
+__device__ __forceinline__ void fused_write_out(const GateUpArgs& g, const uint8_t* stage, const float* rs,
                                                 int row0, int nrows, int n0, int ncols, bool scales, bool last_mb,
                                                 int rows_end, int nthreads) {
   const int C = g.I / kChunk, per_row = ncols / 8;
@@ -501,7 +515,7 @@ __device__ __forceinline__ void fused_write_out(const GateUpArgs& g, const uint8
   if (scales) {
     for (int rl = threadIdx.x; rl < nrows; rl += nthreads) {
       const int m = row0 + rl;
-      const float s = rmax[rl] / 448.0f;
+      const float s = rs[rl];
       g.sh[m] = s;
       if (g.tap_sh && m < g.M) g.tap_sh[m] = s;
     }

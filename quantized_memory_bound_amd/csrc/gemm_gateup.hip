@@ -88,7 +88,7 @@ __global__ __launch_bounds__(64 * MS * KS) void ks_gateup(GateUpArgs g) {
   static_assert(!(FUSED && BF16H), "the BF16-down mode has no requantization");
   constexpr int MTW = (MT + MS - 1) / MS;
   extern __shared__ v4f red4[];
-  __shared__ float s_rmax[FUSED ? MT * 16 : 1];   // FUSED: the workgroup's grid-wide row maxima
+  __shared__ float s_rmax[FUSED ? 2 * MT * 16 : 1];   // FUSED: the rows' scales and their reciprocals
   int mb, ng;
   gateup_block(g, (g.I / 8) / T, mb, ng);
   const int C = g.H / kChunk;
@@ -193,8 +193,7 @@ __global__ __launch_bounds__(64 * MS * KS) void ks_gateup(GateUpArgs g) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           const int rl = sq * 16 + gateup_value_row(e);
-          float sc, rcp;
-          row_scale_of(s_rmax[rl], sc, rcp);
+          const float sc = s_rmax[rl], rcp = s_rmax[MT * 16 + rl];
           stage_code(stage, NC, rl, st * 8 + (lane & 7), hv[e], sc, rcp);
         }
       }
@@ -276,10 +275,11 @@ __global__ __launch_bounds__(64 * MS * KS) void ks_gateup(GateUpArgs g) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           const int rl = q * 16 + gateup_value_row(e);
-          float sc, rcp;
-          row_scale_of(s_rmax[rl], sc, rcp);
+          const float sc = s_rmax[rl], rcp = s_rmax[MT * 16 + rl];
+          float hvt[T];
 #pragma unroll
-          for (int t = 0; t < T; ++t) stage_code(stage, NC, rl, t * 8 + (lane & 7), hvq[jq][t][e], sc, rcp);
+          for (int t = 0; t < T; ++t) hvt[t] = hvq[jq][t][e];
+          stage_codes<T>(stage, NC, rl, lane & 7, hvt, sc, rcp);
         }
       }
     }
@@ -536,10 +536,11 @@ __device__ __forceinline__ void pc_consumer(const GateUpArgs& g, uint8_t* lds, f
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           const int rl = q * 16 + gateup_value_row(e);
-          float sc, rcp;
-          row_scale_of(rmax[rl], sc, rcp);
+          const float sc = rmax[rl], rcp = rmax[MT * 16 + rl];
+          float hvt[T];
 #pragma unroll
-          for (int t = 0; t < T; ++t) stage_code(stage, NC, rl, t * 8 + (lane & 7), hvq[jq][t][e], sc, rcp);
+          for (int t = 0; t < T; ++t) hvt[t] = hvq[jq][t][e];
+          stage_codes<T>(stage, NC, rl, lane & 7, hvt, sc, rcp);
         }
       }
     }
@@ -550,7 +551,7 @@ template <int BF, int T, int C, bool BF16H, bool FUSED>
 __global__ __launch_bounds__(64 * (kPcConsumers + kPcProducers)) void pc_gateup(GateUpArgs g) {
   static_assert(!(FUSED && BF16H), "the BF16-down mode has no requantization");
   extern __shared__ v4f pc_lds[];
-  __shared__ float s_rmax[FUSED ? 13 * 16 : 1];   // FUSED: the workgroup's grid-wide row maxima
+  __shared__ float s_rmax[FUSED ? 2 * 13 * 16 : 1];   // FUSED: the rows' scales and their reciprocals
   uint8_t* lds = (uint8_t*)pc_lds;
   int mb, ng;
   gateup_block(g, (g.I / 8) / T, mb, ng);

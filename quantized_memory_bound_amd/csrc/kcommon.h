@@ -183,6 +183,34 @@ __device__ __forceinline__ v2u e4m3x8_quot(const float (&v)[8], float s, float r
   return v2u{(uint32_t)lo, (uint32_t)hi};
 }
 
+// N E4M3 codes (low bytes) of fl32(v[j] / s) for s > 0 with rcp = fl32(1 / s):
+// the rule of e4m3x8_quot (same window test, same fallback to the exact
+// quotients, same saturating hardware conversion) for the N values of one
+// row.  The exact quotients stay behind a branch that a wave skips unless
+// one of its lanes needs them (computed unconditionally, the divisions were
+// most of the in-launch requantization's vector work).
+template <int N>
+__device__ __forceinline__ void e4m3_quotN(const float (&v)[N], float s, float rcp, uint32_t (&c)[N]) {
+  float q[N];
+  bool near = false;
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    q[j] = v[j] * rcp;
+    const float t = fabsf(q[j]) * 512.0f;
+    near |= (t < 8.0f) & (fabsf(__builtin_amdgcn_fractf(t) - 0.5f) < 0x1p-19f);
+    near |= (__float_as_uint(q[j]) & 0xFFFFFu) - 0x7FFFDu <= 6u;
+  }
+  if (near) {
+    asm volatile("");   // not speculated: the block has a side effect
+#pragma unroll
+    for (int j = 0; j < N; ++j) q[j] = v[j] / s;
+  }
+#pragma unroll
+  for (int j = 0; j < N; ++j)
+    c[j] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(q[j], -448.0f, 448.0f), 0.0f, 0, false) &
+           0xFFu;
+}
+
 // One E4M3 code (low byte) of fl32(v / s) for s > 0 with rcp = fl32(1 / s):
 // the single-value form of e4m3x8_quot (same window test, same fallback to
 // the exact quotient, same saturating hardware conversion).

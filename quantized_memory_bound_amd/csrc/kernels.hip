@@ -244,14 +244,12 @@ __global__ __launch_bounds__(kThreads) void k_requant(const float* __restrict__ 
 
 // ---------------------------------------------------------------- forward
 
-// Where h is requantized: 0 in a second kernel, 1 inside the gate/up kernel
-// (where its grid is resident at once), 2 (default) inside it for up to
-// kFusedMaxRows rows.  Measured on MI355X (graph replays, one box), the
-// in-launch form saves 0.3-1.2 us per block from 1 to 52 rows (decode 20.6 ->
-// 19.4 us, NVFP4 M=1 28.4 -> 27.5 us) and ties at 208 rows (36.8 us), where
-// its exchange costs as much as the launch it saves.
-static std::atomic<int> g_fused_requant{2};
-constexpr int kFusedMaxRows = 64;
+// Where h is requantized: 1 (default) inside the gate/up kernel where its
+// grid is resident at once, 0 in a second kernel.  Measured on MI355X (graph
+// replays, one box at a time), the in-launch form saves 0.3-1.2 us per block:
+// spec-verify 35.2 -> 34.7 us, decode 20.6 -> 19.4 us, NVFP4 M=1 28.4 ->
+// 27.5 us.
+static std::atomic<int> g_fused_requant{1};
 
 void set_fused_requant(int mode) { g_fused_requant.store(mode, std::memory_order_relaxed); }
 
@@ -308,8 +306,7 @@ int launch_forward(const Plan& p, const FwdArgs& a) {
     gev.start = (hipEvent_t)a.stage_events[1];
     gev.end = (hipEvent_t)a.stage_events[2];
   }
-  const int fmode = g_fused_requant.load(std::memory_order_relaxed);
-  bool fused = !bf16_down && (fmode == 1 || (fmode == 2 && p.M <= kFusedMaxRows));
+  bool fused = !bf16_down && g_fused_requant.load(std::memory_order_relaxed) != 0;
   e = launch_gateup(p, g, st, gev, fused);
   if (e != hipSuccess) return (int)e;
   if (a.requant_in_gateup) *a.requant_in_gateup = fused ? 1 : 0;

@@ -40,7 +40,7 @@ struct FwdArgs {
 // enqueue the kernels of one forward call (kernels.hip); returns 0 or a hipError_t value
 int launch_forward(const Plan& p, const FwdArgs& a);
 // process-wide: where gate/up launches requantize h (ocq_set_fused_requant)
-void set_fused_requant(int mode);   // 0, 1 or 2 (ocq_set_fused_requant)
+void set_fused_requant(int mode);   // 0 or 1 (ocq_set_fused_requant)
 
 // measurement kernels (diag.hip); return 0 or a hipError_t value
 int diag_stream_read(const void* src, size_t bytes, void* out, int nblocks, void* stream);

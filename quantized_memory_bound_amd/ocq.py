@@ -197,14 +197,13 @@ def pack_weights(w_gate, w_up, w_down, prec_mode, device="cuda", stream=None, sm
     return blob
 
 
-FUSED_REQUANT_DEFAULT = 2
+FUSED_REQUANT_DEFAULT = 1
 
 
 def set_fused_requant(mode):
     """Process-wide: requantize h inside the gate/up kernel where its grid
-    fits the GPU at once (1 or True), in a second kernel (0 or False), or the
-    first for calls of at most 64 rows and the second above (2, the
-    default)."""
+    fits the GPU at once (1 or True, the default), or in a second kernel (0
+    or False)."""
     _check(lib().ocq_set_fused_requant(int(mode)))
 
 

@@ -141,8 +141,8 @@ int main() {
     EXPECT(ocq_diag_phase_stamps(1, stamps.data(), sb) == OCQ_ERR_UNSUPPORTED);
   }
   EXPECT(ocq_set_fused_requant(0) == OCQ_OK);
-  EXPECT(ocq_set_fused_requant(2) == OCQ_OK);
-  EXPECT(ocq_set_fused_requant(3) == OCQ_ERR_INVALID_ARG);
+  EXPECT(ocq_set_fused_requant(1) == OCQ_OK);
+  EXPECT(ocq_set_fused_requant(2) == OCQ_ERR_INVALID_ARG);
   EXPECT(ocq_set_fused_requant(-1) == OCQ_ERR_INVALID_ARG);
   EXPECT(ocq_last_requant_in_gateup() == -1);   // no forward call was made
   std::printf("%s (%d failed checks)\n", g_fail ? "FAIL" : "OK", g_fail);

@@ -52,14 +52,14 @@ def test_phase_stamps_need_the_stamped_build():
 
 
 def test_requant_placement_mode_is_checked():
-    """The requantization mode takes 0, 1 or 2; the report of where the last
+    """The requantization mode takes 0 or 1; the report of where the last
     call requantized h reads -1 on a thread that made no forward call."""
     L = ocq.lib()
-    assert ocq.FUSED_REQUANT_DEFAULT == 2
-    for bad in (-1, 3, 100):
+    assert ocq.FUSED_REQUANT_DEFAULT == 1
+    for bad in (-1, 2, 100):
         assert L.ocq_set_fused_requant(bad) == ocq.ERR_INVALID_ARG
         assert b"mode" in L.ocq_last_error()
-    for good in (0, 1, 2):
+    for good in (0, 1):
         assert L.ocq_set_fused_requant(good) == ocq.OK
     ocq.set_fused_requant(ocq.FUSED_REQUANT_DEFAULT)
     res = []

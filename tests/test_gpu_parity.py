@@ -79,14 +79,21 @@ SMALL = [(256, 512, 1), (256, 512, 4), (384, 640, 17), (512, 1024, 37), (256, 76
          (256, 512, 300), (640, 384, 65), (256, 768, 420), (384, 1152, 640)]
 
 
+# requant 1: h requantized inside the gate/up launch where its grid fits the
+# GPU at once (the library's default); 0: the two-pass form everywhere
+@pytest.mark.parametrize("requant", [1, 0])
 @pytest.mark.parametrize("prec", [0, 1, 2])
 @pytest.mark.parametrize("hidden,inter,M", SMALL)
-def test_small_shapes(hidden, inter, M, prec):
-    print("case hidden=%d inter=%d M=%d prec=%d" % (hidden, inter, M, prec), flush=True)
+def test_small_shapes(hidden, inter, M, prec, requant):
+    print("case hidden=%d inter=%d M=%d prec=%d requant=%d" % (hidden, inter, M, prec, requant), flush=True)
     d = I.make_inputs(hidden, inter, M, x_outliers=True, w_std=0.02, seed=hidden * 7 + inter + M)
-    g, _ = run_gpu(d, prec)
+    try:
+        ocq.set_fused_requant(requant)
+        g, _ = run_gpu(d, prec)
+    finally:
+        ocq.set_fused_requant(ocq.FUSED_REQUANT_DEFAULT)
     r = O.block_reference(d["x_bits"], d["w_gate"], d["w_up"], d["w_down"], prec)
-    compare(g, r, prec, what="%dx%d M=%d prec=%d" % (hidden, inter, M, prec))
+    compare(g, r, prec, what="%dx%d M=%d prec=%d requant=%d" % (hidden, inter, M, prec, requant))
 
 
 # blobs packed with activation-aware smoothing (factors calibrated on a
@@ -302,8 +309,7 @@ def test_binding_rejects_bad_tensors():
 # The per-token requantization inside the gate/up kernel (grid-wide row
 # maxima, h kept in registers) and the two-pass form (fp32 h to the
 # workspace, then k_requant) compute the same h, the same maxima and the
-# same codes: every output must be bit-identical, in all three modes of
-# ocq_set_fused_requant (the default, 2, takes the first up to 64 rows).  Shapes: the skinny
+# same codes: every output must be bit-identical.  Shapes: the skinny
 # kernels (one pair per wave, and several m-tiles per wave), the 13-m-tile
 # kernel with weight producers (E4M3 and NVFP4 weights), the decode and
 # spec-verify workloads' shapes, and NVFP4 with six tiles per workgroup.
@@ -321,13 +327,9 @@ def test_fused_requant_matches_two_pass(H, Iw, M, prec):
         ocq.set_fused_requant(1)
         g1, _ = run_gpu(d, prec, blob=blob)
         assert ocq.last_requant_in_gateup() == 1   # every grid here fits the GPU at once
-        ocq.set_fused_requant(2)
-        g3, _ = run_gpu(d, prec, blob=blob)
-        assert ocq.last_requant_in_gateup() == (1 if M <= 64 else 0)
     finally:
         ocq.set_fused_requant(ocq.FUSED_REQUANT_DEFAULT)
     for k in ("y", "xq", "sx", "hq", "sh"):
         assert np.array_equal(g1[k], g2[k]), k
-        assert np.array_equal(g3[k], g2[k]), k
     r = O.block_reference(d["x_bits"], d["w_gate"], d["w_up"], d["w_down"], prec)
     compare(g1, r, prec, what="fused %dx%d M=%d prec=%d" % (H, Iw, M, prec))

@@ -19,7 +19,10 @@ namespace ocq {
 // Time stamps (100 MHz clock, s_memrealtime) of the last launch of the
 // producer/consumer gate/up, built only with OCQ_PHASE_STAMPS:
 // [workgroup < 512][wave: 8 consumers, then 4 producers][entry, consumer loop
-// start, loop end, K halves' partial tiles stored, wave end, -, -, -].
+// start, loop end, K halves' partial tiles stored, wave end; with the
+// requantization inside the launch also: row maxima folded (arrival), grid
+// released, row scales ready].  Producer waves record entry, wave end and
+// the last three.
 __device__ uint64_t g_pc_phases[kPhaseWGs][12][8];
 static_assert(sizeof(g_pc_phases) == kPcPhaseBytes, "layout stated in ocq_internal.h");
 __device__ __forceinline__ void pc_stamp(int wave, int i) {
@@ -525,8 +528,11 @@ __device__ __forceinline__ void pc_consumer(const GateUpArgs& g, uint8_t* lds, f
   if constexpr (FUSED) {
     // every wave of the workgroup (producers too) arrives here; afterwards
     // the codes go to an LDS stage [208 rows][T * 8 columns]
+    OCQ_PC_STAMP(wave, 5);
     grid_arrive_and_wait(g.sync, gridDim.x, seen, rmax, MT * 16);
+    OCQ_PC_STAMP(wave, 6);
     grid_row_maxima<64 * (kPcConsumers + kPcProducers), MT * 16>(g, row0, rmax);
+    OCQ_PC_STAMP(wave, 7);
     uint8_t* stage = lds;
     constexpr int NC = T * 8;
 #pragma unroll
@@ -561,8 +567,11 @@ __global__ __launch_bounds__(64 * (kPcConsumers + kPcProducers)) void pc_gateup(
   if (wave >= kPcConsumers) {
     pc_producer<BF, T, C>(g, lds, ng, wave - kPcConsumers);
     if constexpr (FUSED) {
+      OCQ_PC_STAMP(wave, 5);
       grid_arrive_and_wait(g.sync, gridDim.x, 0u, s_rmax, 13 * 16);
+      OCQ_PC_STAMP(wave, 6);
       grid_row_maxima<64 * (kPcConsumers + kPcProducers), 13 * 16>(g, row0, s_rmax);
+      OCQ_PC_STAMP(wave, 7);
     }
   } else if (wave < 2) {
     pc_consumer<BF, 4, T, C, BF16H, FUSED>(g, lds, s_rmax, row0, ng, wave, 0);

@@ -70,12 +70,20 @@ def pc_summary(t):
     t0 = b[:, :, 0][b[:, :, 0] > 0].min()
     c = (b[:, :8] - t0) / 100.0              # consumers, microseconds from the first start
     med = np.median
-    return ["producer/consumer gate/up: %d workgroups; microseconds (medians over workgroups and consumer waves)" % n,
-            "  wave start: first 0.00, median %.2f, last %.2f" % (med(c[:, :, 0]), c[:, :, 0].max()),
-            "  start -> consumer loop %.2f, loop (with the wait for the first stage) %.2f, partial tiles %.2f, epilogue %.2f"
-            % (med(c[:, :, 1] - c[:, :, 0]), med(c[:, :, 2] - c[:, :, 1]), med(c[:, :, 3] - c[:, :, 2]),
-               med(c[:, :, 4] - c[:, :, 3])),
-            "  last wave end %.2f" % (((b[:, :, 4] - t0) / 100.0).max())]
+    lines = ["producer/consumer gate/up: %d workgroups; microseconds (medians over workgroups and consumer waves)" % n,
+             "  wave start: first 0.00, median %.2f, last %.2f" % (med(c[:, :, 0]), c[:, :, 0].max()),
+             "  start -> consumer loop %.2f, loop (with the wait for the first stage) %.2f, partial tiles %.2f, epilogue %.2f"
+             % (med(c[:, :, 1] - c[:, :, 0]), med(c[:, :, 2] - c[:, :, 1]), med(c[:, :, 3] - c[:, :, 2]),
+                med(c[:, :, 4] - c[:, :, 3]))]
+    if (b[:, :, 5:8] > 0).all():             # the launch requantized h itself
+        w = (b - t0) / 100.0
+        arrive = w[:, :, 5].max(axis=1)      # a workgroup arrives with its last wave
+        lines += ["  epilogue with the requantization inside the launch: SiLU and row maxima folded %.2f, wait %.2f,"
+                  " row scales %.2f, codes staged %.2f" % (med(c[:, :, 5] - c[:, :, 3]), med(c[:, :, 6] - c[:, :, 5]),
+                                                           med(c[:, :, 7] - c[:, :, 6]), med(c[:, :, 4] - c[:, :, 7])),
+                  "  workgroup arrival: first %.2f, median %.2f, last %.2f; released from %.2f to %.2f"
+                  % (arrive.min(), med(arrive), arrive.max(), c[:, :, 6].min(), c[:, :, 6].max())]
+    return lines + ["  last wave end %.2f" % (((b[:, :, 4] - t0) / 100.0).max())]
 
 
 def quant_summary(t):

@@ -5,9 +5,10 @@ The stamps only read clocks where the waves wait anyway, so a block run
 through either library must give identical x codes, h codes (or bf16 h),
 scales and y.  Shapes: the LDS-tiled kernels for many rows (420 rows, BF16
 down; the whole-chunk gate/up stages at hidden 256), the producer/consumer
-gate/up (208 rows, hidden 2048, FP8) with the quantization kernels.  The
-stamped library runs in a child process (one library per process in the
-binding), which writes its outputs and the stamp tables to a file.
+gate/up (208 rows, hidden 2048, FP8; h requantized inside the launch) with
+the x quantization.  The stamped library runs in a child process (one
+library per process in the binding), which writes its outputs and the stamp
+tables to a file.
 """
 
 import os
@@ -67,5 +68,8 @@ def test_phase_stamped_library_matches_plain(tmp_path, H, Iw, M, prec, family):
     else:
         t = s["stamps1"]
         assert np.all(t[0, :, 0] > 0) and np.all(t[0, :8, 2] >= t[0, :8, 1])
+        # h requantized inside the launch (the default): arrival, release and
+        # row scales in that order on every wave
+        assert np.all(t[0, :, 5] > 0) and np.all(t[0, :, 6] >= t[0, :, 5]) and np.all(t[0, :, 7] >= t[0, :, 6])
     q = s["stamps2"]
     assert np.all(q[0, :, 1] >= q[0, :, 0]) and (q[0, :, 0] > 0).sum() == M   # one x-quant workgroup per row
